@@ -1,0 +1,89 @@
+"""Seeded synthetic inputs for the M2RNN scan (shared by the oracle side and the
+HIP side of every test and of the benchmark).
+
+This module holds none of the method's arithmetic: it only draws random
+tensors.  The distributions stand in for the activations the paper's layer
+feeds the scan (slide "Most of the block can be computed before recurrence",
+paper Fig. 2: q, k, v come out of a SiLU; the forget gate lies in [0, 1]):
+
+    q, k = SiLU(N(0,1))            [B, T, K]   shared by the N value heads
+    v    = SiLU(N(0,1))            [B, T, N, V]
+    f    = sigmoid(N(mu, 1))       [B, T, N]   mu = 2 (mu = 3: long retention)
+    W    = N(0, 1/16)              [N, V, V]   (standard deviation 0.25)
+    w_r  = N(0, 1)                 [N, V]
+    dy   = N(0, 1)                 [B, T, N, V]  (float32, backward only)
+
+Draw order is fixed (q, k, v, f, W, w_r, dy) from one CPU torch.Generator
+seeded with `seed`; every tensor is drawn in float32 and, for bfloat16
+workloads, rounded to bfloat16 with round-to-nearest-even.  dy stays float32.
+"""
+from dataclasses import dataclass
+
+import torch
+
+K_DIM = 64
+V_DIM = 16
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int
+    N: int
+    dtype: str = "f32"      # dtype of q, k, v, f, W, w_r: "f32" or "bf16"
+    f_mu: float = 2.0       # mean of the pre-sigmoid forget-gate logits
+    backward: bool = False  # also draw dy
+    ckpt_every: int = 0     # state checkpoint interval for the backward
+    K: int = K_DIM
+    V: int = V_DIM
+
+    @property
+    def head_tokens(self):
+        return self.B * self.T * self.N
+
+
+WORKLOADS = {
+    "fwd_f32_B1_T256_N4": Workload("fwd_f32_B1_T256_N4", 1, 256, 4, "f32"),
+    "fwd_bf16_B8_T2048_N16": Workload("fwd_bf16_B8_T2048_N16", 8, 2048, 16, "bf16"),
+    "fwd_bf16_B2_T32768_N32": Workload("fwd_bf16_B2_T32768_N32", 2, 32768, 32, "bf16", f_mu=3.0),
+    "fwd_bf16_B32_T4096_N64": Workload("fwd_bf16_B32_T4096_N64", 32, 4096, 64, "bf16"),
+    "fwdbwd_bf16_B8_T2048_N16": Workload("fwdbwd_bf16_B8_T2048_N16", 8, 2048, 16, "bf16",
+                                         backward=True, ckpt_every=64),
+    # the headline shape, forward + backward
+    "fwdbwd_bf16_B32_T4096_N64": Workload("fwdbwd_bf16_B32_T4096_N64", 32, 4096, 64, "bf16",
+                                          backward=True, ckpt_every=64),
+}
+
+
+def torch_dtype(name):
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[name]
+
+
+def make_inputs(B, T, N, K=K_DIM, V=V_DIM, dtype="f32", f_mu=2.0, seed=0, with_dy=False):
+    """Draw one seeded input set.  Returns a dict of CPU tensors: q, k, v, f, W,
+    wr in `dtype` (float32 or bfloat16) and, if `with_dy`, dy in float32."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    td = torch_dtype(dtype)
+
+    def draw(*shape):
+        return torch.randn(*shape, generator=g, dtype=torch.float32)
+
+    out = {}
+    out["q"] = torch.nn.functional.silu(draw(B, T, K))
+    out["k"] = torch.nn.functional.silu(draw(B, T, K))
+    out["v"] = torch.nn.functional.silu(draw(B, T, N, V))
+    out["f"] = torch.sigmoid(draw(B, T, N) + f_mu)
+    out["W"] = draw(N, V, V) * 0.25
+    out["wr"] = draw(N, V)
+    for name in ("q", "k", "v", "f", "W", "wr"):
+        out[name] = out[name].to(td).contiguous()
+    if with_dy:
+        out["dy"] = draw(B, T, N, V).contiguous()
+    return out
+
+
+def make_workload(w: Workload, seed=0, with_dy=None):
+    return make_inputs(w.B, w.T, w.N, w.K, w.V, w.dtype, w.f_mu, seed,
+                       w.backward if with_dy is None else with_dy)

@@ -1,0 +1,111 @@
+"""Python handle on the fp64 CPU oracle of the M2RNN scan (oracle/m2rnn_ref.c).
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this module.  The HIP library
+(``non_linear_matrix_amd``) never imports it and shares no code with it.
+
+What the oracle computes follows the M2RNN paper-discussion slides (reading of
+arXiv:2603.14360v2): slide "Write, transform, retain, and read a matrix state"
+(paper Eqs. (10)-(12)) for the forward recurrence and slide "Backup: the
+recurrent gradient needs both paths" for the backward; q and k are shared by
+the value heads (slide "Shared queries and keys buy more recurrent capacity",
+paper Alg. 1).  Inputs are upcast exactly to float64; outputs are float64.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_dbl_p = ctypes.POINTER(ctypes.c_double)
+
+
+class Oracle:
+    """ctypes binding of one compiled copy of the oracle source."""
+
+    def __init__(self, lib_path):
+        self.path = lib_path
+        self.lib = ctypes.CDLL(lib_path)
+        fwd = self.lib.m2rnn_ref_forward
+        fwd.restype = ctypes.c_int
+        fwd.argtypes = [ctypes.c_int] * 5 + [_dbl_p] * 6 + [_dbl_p, _dbl_p, _dbl_p, ctypes.c_int, ctypes.c_int]
+        bwd = self.lib.m2rnn_ref_backward
+        bwd.restype = ctypes.c_int
+        bwd.argtypes = [ctypes.c_int] * 5 + [_dbl_p] * 6 + [_dbl_p, _dbl_p] + [_dbl_p] * 6 + [ctypes.c_int]
+
+    @staticmethod
+    def _arr(x, shape=None):
+        a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+        if shape is not None and a.shape != tuple(shape):
+            raise ValueError(f"expected shape {tuple(shape)}, got {a.shape}")
+        return a
+
+    @staticmethod
+    def _p(a):
+        return a.ctypes.data_as(_dbl_p) if a is not None else None
+
+    def _inputs(self, q, k, v, f, W, wr):
+        q = self._arr(q)
+        B, T, K = q.shape
+        v = self._arr(v)
+        N, V = v.shape[2], v.shape[3]
+        k = self._arr(k, (B, T, K))
+        v = self._arr(v, (B, T, N, V))
+        f = self._arr(f, (B, T, N))
+        W = self._arr(W, (N, V, V))
+        wr = self._arr(wr, (N, V))
+        return (B, T, N, K, V), (q, k, v, f, W, wr)
+
+    def forward(self, q, k, v, f, W, wr, ckpt_every=0, nthreads=0):
+        """Returns (y [B,T,N,V], H_T [B,N,K,V]) or, with ckpt_every > 0,
+        (y, H_T, H_ckpt [B,N,ceil(T/ckpt_every),K,V])."""
+        (B, T, N, K, V), ins = self._inputs(q, k, v, f, W, wr)
+        y = np.empty((B, T, N, V))
+        HT = np.empty((B, N, K, V))
+        ck = None
+        if ckpt_every > 0:
+            ck = np.empty((B, N, (T + ckpt_every - 1) // ckpt_every, K, V))
+        st = self.lib.m2rnn_ref_forward(B, T, N, K, V, *[self._p(a) for a in ins],
+                                        self._p(y), self._p(HT), self._p(ck), int(ckpt_every), int(nthreads))
+        if st != 0:
+            raise RuntimeError(f"m2rnn_ref_forward failed with status {st}")
+        return (y, HT) if ck is None else (y, HT, ck)
+
+    def backward(self, q, k, v, f, W, wr, dy, dH_T=None, nthreads=0):
+        """Gradients of sum(y*dy) + sum(H_T*dH_T): dict with dq, dk, dv, df, dW, dwr."""
+        (B, T, N, K, V), ins = self._inputs(q, k, v, f, W, wr)
+        dy = self._arr(dy, (B, T, N, V))
+        dHT = None if dH_T is None else self._arr(dH_T, (B, N, K, V))
+        out = dict(dq=np.empty((B, T, K)), dk=np.empty((B, T, K)), dv=np.empty((B, T, N, V)),
+                   df=np.empty((B, T, N)), dW=np.empty((N, V, V)), dwr=np.empty((N, V)))
+        st = self.lib.m2rnn_ref_backward(B, T, N, K, V, *[self._p(a) for a in ins],
+                                         self._p(dy), self._p(dHT),
+                                         *[self._p(out[n]) for n in ("dq", "dk", "dv", "df", "dW", "dwr")],
+                                         int(nthreads))
+        if st != 0:
+            raise RuntimeError(f"m2rnn_ref_backward failed with status {st}")
+        return out
+
+
+_default = None
+
+
+def get(rebuild=False):
+    """The oracle built from oracle/m2rnn_ref.c (compiled on first use)."""
+    global _default
+    if _default is None or rebuild:
+        if rebuild or not os.path.exists(_build.LIB) or \
+                os.path.getmtime(_build.LIB) < os.path.getmtime(_build.SRC):
+            _build.build()
+        _default = Oracle(_build.LIB)
+    return _default
+
+
+def forward(*args, **kw):
+    return get().forward(*args, **kw)
+
+
+def backward(*args, **kw):
+    return get().backward(*args, **kw)

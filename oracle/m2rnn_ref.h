@@ -1,0 +1,61 @@
+/*
+ * m2rnn_ref.h -- plain fp64 CPU oracle of the M2RNN matrix-state scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this library: only the test suite, the package smoke check and
+ * the benchmark's CPU-baseline leg use it.  It shares no code with the HIP
+ * library (non_linear_matrix_amd/csrc) and neither side includes the other.
+ *
+ * Source of the method: "M2RNN: Non-Linear RNNs with Matrix-Valued States for
+ * Scalable Language Modeling -- research paper discussion" (slides reading
+ * Mishra, Tan, Stoica, Gonzalez, Dao, arXiv:2603.14360v2):
+ *   - slide "Write, transform, retain, and read a matrix state"
+ *     (paper Eqs. (10)-(12)): the recurrence;
+ *   - slide "Shared queries and keys buy more recurrent capacity"
+ *     (paper Alg. 1, App. A): one q/k per token shared by N value heads,
+ *     one v, f, W, w_r per value head;
+ *   - slide "Backup: the recurrent gradient needs both paths": the
+ *     chain-rule backward for the state, f and W.
+ *
+ * Layouts (all dense, row-major, float64):
+ *   q, k  [B][T][K]        shared by the N value heads of a batch row
+ *   v     [B][T][N][V]
+ *   f     [B][T][N]        scalar forget gate per (token, head)
+ *   W     [N][V][V]        (H W)[i][j] = sum_l H[i][l] * W[n][l][j]
+ *   wr    [N][V]           value-residual weight
+ *   y     [B][T][N][V]     readout of the UPDATED state H_t
+ *   H_T   [B][N][K][V]     state after the last step
+ *   H_ckpt[B][N][ceil(T/ckpt_every)][K][V]  H at t = j*ckpt_every (H_0 = 0)
+ *
+ * Any K >= 1, V >= 1 is accepted.  Return 0 on success, -1 on a bad
+ * argument (null pointer, non-positive size).  nthreads <= 0 means "all
+ * online CPUs".
+ */
+#ifndef M2RNN_REF_H
+#define M2RNN_REF_H
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+int m2rnn_ref_forward(int B, int T, int N, int K, int V,
+                      const double* q, const double* k, const double* v,
+                      const double* f, const double* W, const double* wr,
+                      double* y, double* H_T,
+                      double* H_ckpt, int ckpt_every, /* H_ckpt may be NULL */
+                      int nthreads);
+
+/* Gradients of L = sum(y * dy) + sum(H_T * dH_T).  dH_T may be NULL (zero).
+ * dq, dk [B][T][K] are summed over the N heads (ascending n); dW [N][V][V]
+ * and dwr [N][V] over batch and time (ascending b, then descending t). */
+int m2rnn_ref_backward(int B, int T, int N, int K, int V,
+                       const double* q, const double* k, const double* v,
+                       const double* f, const double* W, const double* wr,
+                       const double* dy, const double* dH_T,
+                       double* dq, double* dk, double* dv, double* df,
+                       double* dW, double* dwr,
+                       int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,327 @@
+"""Pins of the fp64 oracle to facts fixed by the M2RNN slides and by mathematics.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees.  The pins are chosen so that a plausible slip anywhere in the oracle
+(a dropped term, a wrong sign or index, a transposed operand, a stale state)
+fails at least one of them; tests/test_oracle_mutants.py plants such slips in
+copies of the oracle source and checks exactly that.
+
+Sources (M2RNN paper-discussion slides, reading of arXiv:2603.14360v2):
+  [EQ]  slide "Write, transform, retain, and read a matrix state",
+        paper Eqs. (10)-(12): the recurrence, H_0 = 0, f in [0, 1].
+  [SH]  slide "Shared queries and keys buy more recurrent capacity",
+        paper Alg. 1 / App. A: q, k shared by the value heads.
+  [RNN] slide "Backup: embedding a vector RNN in one matrix row",
+        paper App. B, Eq. (25): f = 0, w_r = 0, q = k = e_1 turns row 1 of
+        the state into the Elman RNN h_t = tanh(W^T h_{t-1} + v_t), y_t = h_t.
+  [BW]  slide "Backup: the recurrent gradient needs both paths".
+"""
+import numpy as np
+import torch
+
+RNG_SEED = 1234
+
+
+def _rand_inputs(rng, B, T, N, K, V, f_lo=0.0, f_hi=1.0, scale=1.0):
+    q = rng.standard_normal((B, T, K)) * scale
+    k = rng.standard_normal((B, T, K)) * scale
+    v = rng.standard_normal((B, T, N, V)) * scale
+    f = rng.uniform(f_lo, f_hi, (B, T, N))
+    W = rng.standard_normal((N, V, V)) * 0.4
+    wr = rng.standard_normal((N, V))
+    return q, k, v, f, W, wr
+
+
+def _close(a, b, tol, what):
+    a = np.asarray(a)
+    b = np.asarray(b)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs diff {err:.3e} > {tol:.1e}"
+
+
+# ---------------------------------------------------------------- forward pins
+
+def pin_t1_closed_form(o):
+    """[EQ] with T = 1 and H_0 = 0: H_1 = (1 - f) tanh(k v^T) (the H W term
+    vanishes) and y_1 = H_1^T q + w_r * v."""
+    rng = np.random.default_rng(RNG_SEED)
+    B, T, N, K, V = 2, 1, 3, 5, 4
+    q, k, v, f, W, wr = _rand_inputs(rng, B, T, N, K, V)
+    y, HT = o.forward(q, k, v, f, W, wr)
+    for b in range(B):
+        for n in range(N):
+            H1 = (1 - f[b, 0, n]) * np.tanh(np.outer(k[b, 0], v[b, 0, n]))
+            _close(HT[b, n], H1, 1e-15, "T=1 H_1")
+            _close(y[b, 0, n], H1.T @ q[b, 0] + wr[n] * v[b, 0, n], 1e-14, "T=1 y_1")
+
+
+def pin_zero_w_zero_f_forward(o):
+    """[EQ] with W = 0 and f = 0: every step forgets, so H_t = tanh(k_t v_t^T)
+    exactly and y_t = tanh(k_t v_t^T)^T q_t + w_r * v_t."""
+    rng = np.random.default_rng(RNG_SEED + 1)
+    B, T, N, K, V = 2, 6, 2, 64, 16
+    q, k, v, _, _, wr = _rand_inputs(rng, B, T, N, K, V)
+    f = np.zeros((B, T, N))
+    W = np.zeros((N, V, V))
+    y, HT = o.forward(q, k, v, f, W, wr)
+    for b in range(B):
+        for n in range(N):
+            for t in range(T):
+                Z = np.tanh(np.outer(k[b, t], v[b, t, n]))
+                _close(y[b, t, n], Z.T @ q[b, t] + wr[n] * v[b, t, n], 1e-13, "W=0,f=0 y")
+            _close(HT[b, n], np.tanh(np.outer(k[b, T - 1], v[b, T - 1, n])), 1e-15, "W=0,f=0 H_T")
+
+
+def pin_f_one_forward(o):
+    """[EQ] with f = 1: H_t = H_{t-1} = H_0 = 0 for all t, so H_T = 0 and
+    y_t = w_r * v_t, bit-exact."""
+    rng = np.random.default_rng(RNG_SEED + 2)
+    B, T, N, K, V = 2, 7, 3, 64, 16
+    q, k, v, _, W, wr = _rand_inputs(rng, B, T, N, K, V)
+    f = np.ones((B, T, N))
+    y, HT = o.forward(q, k, v, f, W, wr)
+    assert np.array_equal(HT, np.zeros_like(HT)), "f=1 must keep H = 0"
+    assert np.array_equal(y, wr[None, None] * v), "f=1 must give y = w_r * v exactly"
+
+
+def pin_rnn_embedding_forward_backward(o):
+    """[RNN]: f = 0, w_r = 0, q = k = e_1 gives y_t = h_t of the textbook Elman
+    RNN h_t = tanh(W^T h_{t-1} + v_t), i.e. torch.nn.RNN with weight_ih = I and
+    weight_hh = W^T.  Its autograd gradient of sum(y * dy) pins the oracle's dv
+    (= dL/dx) and dW (= (dL/dweight_hh)^T) too."""
+    rng = np.random.default_rng(RNG_SEED + 3)
+    B, T, N, K, V = 2, 9, 2, 64, 16
+    _, _, v, _, W, _ = _rand_inputs(rng, B, T, N, K, V)
+    W = W * 2.0  # strong recurrence, so an orientation slip shows
+    q = np.zeros((B, T, K))
+    q[:, :, 0] = 1.0
+    k = q.copy()
+    f = np.zeros((B, T, N))
+    wr = np.zeros((N, V))
+    dy = rng.standard_normal((B, T, N, V))
+    y, _ = o.forward(q, k, v, f, W, wr)
+    g = o.backward(q, k, v, f, W, wr, dy)
+    for n in range(N):
+        rnn = torch.nn.RNN(V, V, nonlinearity="tanh", bias=False, batch_first=True).double()
+        with torch.no_grad():
+            rnn.weight_ih_l0.copy_(torch.eye(V, dtype=torch.float64))
+            rnn.weight_hh_l0.copy_(torch.from_numpy(W[n].T.copy()))
+        x = torch.from_numpy(v[:, :, n].copy()).requires_grad_(True)
+        h, _ = rnn(x)
+        _close(y[:, :, n], h.detach().numpy(), 1e-13, "RNN embedding y")
+        (h * torch.from_numpy(dy[:, :, n].copy())).sum().backward()
+        _close(g["dv"][:, :, n], x.grad.numpy(), 1e-12, "RNN embedding dv")
+        _close(g["dW"][n], rnn.weight_hh_l0.grad.numpy().T, 1e-11, "RNN embedding dW")
+
+
+def pin_convex_bound(o):
+    """[EQ]: H_t is a convex combination of H_{t-1} and tanh(.) in [-1, 1], so
+    |H_t| <= 1 elementwise for f in [0, 1], even for large inputs."""
+    rng = np.random.default_rng(RNG_SEED + 4)
+    B, T, N, K, V = 2, 40, 3, 64, 16
+    q, k, v, f, W, wr = _rand_inputs(rng, B, T, N, K, V, scale=4.0)
+    W = W * 5.0
+    f[:, ::3] = 0.0
+    f[:, 1::7] = 1.0
+    _, HT, ck = o.forward(q, k, v, f, W, wr, ckpt_every=1)
+    assert np.all(np.abs(ck) <= 1.0) and np.all(np.abs(HT) <= 1.0), "|H| must stay <= 1"
+    assert np.max(np.abs(HT)) > 0.5, "bound test must reach the saturated regime"
+
+
+def pin_checkpoints(o):
+    """H_ckpt[j] is the state after j*c steps (H_0 = 0 for j = 0): it must equal
+    H_T of the same recurrence run for j*c steps."""
+    rng = np.random.default_rng(RNG_SEED + 5)
+    B, T, N, K, V = 1, 11, 2, 8, 4
+    q, k, v, f, W, wr = _rand_inputs(rng, B, T, N, K, V)
+    c = 4
+    _, HT, ck = o.forward(q, k, v, f, W, wr, ckpt_every=c)
+    assert ck.shape == (B, N, 3, K, V)
+    assert np.array_equal(ck[:, :, 0], np.zeros((B, N, K, V))), "ckpt 0 must be H_0 = 0"
+    for j in (1, 2):
+        _, HTj = o.forward(q[:, :j * c], k[:, :j * c], v[:, :j * c], f[:, :j * c], W, wr)
+        assert np.array_equal(ck[:, :, j], HTj), f"ckpt {j} != H after {j * c} steps"
+
+
+def pin_permutations(o):
+    """Symmetries of [EQ] and [SH]:
+    - permuting the K index of q and k together permutes the rows of H_T and
+      leaves y unchanged (dq, dk permute the same way, the rest is unchanged);
+    - permuting the value channels of v, w_r and both indices of W permutes the
+      columns of H_T and the channels of y;
+    - permuting heads or batch rows permutes the outputs."""
+    rng = np.random.default_rng(RNG_SEED + 6)
+    B, T, N, K, V = 3, 6, 4, 8, 5
+    q, k, v, f, W, wr = _rand_inputs(rng, B, T, N, K, V)
+    dy = rng.standard_normal((B, T, N, V))
+    y, HT = o.forward(q, k, v, f, W, wr)
+    g = o.backward(q, k, v, f, W, wr, dy)
+    tol = 1e-13
+
+    p = rng.permutation(K)
+    y2, HT2 = o.forward(q[..., p], k[..., p], v, f, W, wr)
+    _close(y2, y, tol, "row perm y")
+    _close(HT2, HT[:, :, p, :], tol, "row perm H_T")
+    g2 = o.backward(q[..., p], k[..., p], v, f, W, wr, dy)
+    _close(g2["dq"], g["dq"][..., p], tol, "row perm dq")
+    _close(g2["dk"], g["dk"][..., p], tol, "row perm dk")
+    for name in ("dv", "df", "dW", "dwr"):
+        _close(g2[name], g[name], tol, f"row perm {name}")
+
+    s = rng.permutation(V)
+    y3, HT3 = o.forward(q, k, v[..., s], f, W[:, s][:, :, s], wr[:, s])
+    _close(y3, y[..., s], tol, "value perm y")
+    _close(HT3, HT[..., s], tol, "value perm H_T")
+
+    h = rng.permutation(N)
+    y4, HT4 = o.forward(q, k, v[:, :, h], f[:, :, h], W[h], wr[h])
+    _close(y4, y[:, :, h], tol, "head perm y")
+    _close(HT4, HT[:, h], tol, "head perm H_T")
+    g4 = o.backward(q, k, v[:, :, h], f[:, :, h], W[h], wr[h], dy[:, :, h])
+    _close(g4["dq"], g["dq"], tol, "head perm dq")
+    _close(g4["dk"], g["dk"], tol, "head perm dk")
+    _close(g4["dW"], g["dW"][h], tol, "head perm dW")
+
+    bp = rng.permutation(B)
+    y5, HT5 = o.forward(q[bp], k[bp], v[bp], f[bp], W, wr)
+    _close(y5, y[bp], tol, "batch perm y")
+    _close(HT5, HT[bp], tol, "batch perm H_T")
+
+
+def pin_readout_linear_in_q(o):
+    """[EQ]: q enters only through the readout, so y - w_r * v is linear in q."""
+    rng = np.random.default_rng(RNG_SEED + 7)
+    B, T, N, K, V = 2, 5, 2, 8, 4
+    q, k, v, f, W, wr = _rand_inputs(rng, B, T, N, K, V)
+    q2 = rng.standard_normal(q.shape)
+    base = wr[None, None] * v
+    ya, _ = o.forward(q, k, v, f, W, wr)
+    yb, _ = o.forward(q2, k, v, f, W, wr)
+    yc, _ = o.forward(q + 2.0 * q2, k, v, f, W, wr)
+    _close(yc - base, (ya - base) + 2.0 * (yb - base), 1e-13, "linearity in q")
+
+
+# --------------------------------------------------------------- backward pins
+
+def pin_f_one_backward(o):
+    """[BW] with f = 1: D_t = 0, so C_{t-1} = R_t and C_t = dH_T + sum_{s>t}
+    q_s u_s^T.  Hence dW = dk = dq = 0, dv = w_r * u, dw_r = sum_t u * v and
+    df_t = <dH_T + sum_{s>=t} q_s u_s^T, 0 - tanh(k_t v_t^T)>."""
+    rng = np.random.default_rng(RNG_SEED + 8)
+    B, T, N, K, V = 2, 6, 3, 8, 5
+    q, k, v, _, W, wr = _rand_inputs(rng, B, T, N, K, V)
+    f = np.ones((B, T, N))
+    dy = rng.standard_normal((B, T, N, V))
+    dHT = rng.standard_normal((B, N, K, V))
+    g = o.backward(q, k, v, f, W, wr, dy, dHT)
+    for name in ("dW", "dk", "dq"):
+        assert np.array_equal(g[name], np.zeros_like(g[name])), f"f=1: {name} must be 0"
+    _close(g["dv"], wr[None, None] * dy, 0.0, "f=1 dv")
+    _close(g["dwr"], np.einsum("btnj,btnj->nj", dy, v), 1e-12, "f=1 dwr")
+    for b in range(B):
+        for n in range(N):
+            acc = dHT[b, n].copy()
+            for t in range(T - 1, -1, -1):
+                acc = acc + np.outer(q[b, t], dy[b, t, n])
+                Z = np.tanh(np.outer(k[b, t], v[b, t, n]))
+                _close(g["df"][b, t, n], -np.sum(acc * Z), 1e-12, "f=1 df")
+
+
+def pin_zero_w_zero_f_backward(o):
+    """[BW] with W = 0, f = 0 and no dH_T: C_{t-1} = f R_t + D_t W^T = 0, so
+    R_t = q_t u_t^T, H_t = Z_t = tanh(k_t v_t^T), D_t = R_t * (1 - Z_t^2), and
+    df_t = <R_t, Z_{t-1} - Z_t>, dW = sum_t Z_{t-1}^T D_t, dk_t = sum_n D_t v_t,
+    dv_t = D_t^T k_t + w_r * u_t, dq_t = sum_n Z_t u_t."""
+    rng = np.random.default_rng(RNG_SEED + 9)
+    B, T, N, K, V = 2, 5, 3, 8, 4
+    q, k, v, _, _, wr = _rand_inputs(rng, B, T, N, K, V)
+    f = np.zeros((B, T, N))
+    W = np.zeros((N, V, V))
+    dy = rng.standard_normal((B, T, N, V))
+    g = o.backward(q, k, v, f, W, wr, dy)
+    dW = np.zeros((N, V, V))
+    for b in range(B):
+        dq = np.zeros((T, K))
+        dk = np.zeros((T, K))
+        for n in range(N):
+            Zprev = np.zeros((K, V))
+            for t in range(T):
+                Z = np.tanh(np.outer(k[b, t], v[b, t, n]))
+                R = np.outer(q[b, t], dy[b, t, n])
+                D = R * (1 - Z * Z)
+                _close(g["df"][b, t, n], np.sum(R * (Zprev - Z)), 1e-12, "W=0,f=0 df")
+                _close(g["dv"][b, t, n], D.T @ k[b, t] + wr[n] * dy[b, t, n], 1e-12, "W=0,f=0 dv")
+                dW[n] += Zprev.T @ D
+                dk[t] += D @ v[b, t, n]
+                dq[t] += Z @ dy[b, t, n]
+                Zprev = Z
+        _close(g["dq"][b], dq, 1e-12, "W=0,f=0 dq")
+        _close(g["dk"][b], dk, 1e-12, "W=0,f=0 dk")
+    _close(g["dW"], dW, 1e-12, "W=0,f=0 dW")
+
+
+def _loss(o, ins, dy, dHT):
+    y, HT = o.forward(*ins)
+    return float(np.sum(y * dy) + np.sum(HT * dHT))
+
+
+def _fd_check(o, B, T, N, K, V, seed, tol=1e-6, h=1e-6):
+    rng = np.random.default_rng(seed)
+    q, k, v, f, W, wr = _rand_inputs(rng, B, T, N, K, V, f_lo=0.05, f_hi=0.95)
+    dy = rng.standard_normal((B, T, N, V))
+    dHT = rng.standard_normal((B, N, K, V))
+    ins = [q, k, v, f, W, wr]
+    g = o.backward(*ins, dy, dHT)
+    names = ["dq", "dk", "dv", "df", "dW", "dwr"]
+    for idx, name in enumerate(names):
+        x = ins[idx]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            mi = it.multi_index
+            orig = x[mi]
+            x[mi] = orig + h
+            lp = _loss(o, ins, dy, dHT)
+            x[mi] = orig - h
+            lm = _loss(o, ins, dy, dHT)
+            x[mi] = orig
+            fd[mi] = (lp - lm) / (2 * h)
+        scale = max(1.0, float(np.max(np.abs(fd))))
+        err = float(np.max(np.abs(fd - g[name])))
+        assert err <= tol * scale, f"FD {name}: max abs diff {err:.3e} > {tol * scale:.1e}"
+
+
+def pin_finite_differences_small(o):
+    """[BW] against brute force: central differences of
+    L = sum(y * dy) + sum(H_T * dH_T) over every element of q, k, v, f, W, w_r,
+    at B=2, T=5, N=3, K=4, V=3."""
+    _fd_check(o, 2, 5, 3, 4, 3, RNG_SEED + 10)
+
+
+def pin_finite_differences_full_state(o):
+    """Same brute-force check at the real state shape K=64, V=16 (B=1, T=3, N=2)."""
+    _fd_check(o, 1, 3, 2, 64, 16, RNG_SEED + 11)
+
+
+def pin_thread_invariance(o):
+    """Outputs do not depend on the number of host threads (fixed summation
+    order over heads and batch rows)."""
+    rng = np.random.default_rng(RNG_SEED + 12)
+    B, T, N, K, V = 3, 7, 5, 8, 4
+    ins = _rand_inputs(rng, B, T, N, K, V)
+    dy = rng.standard_normal((B, T, N, V))
+    y1, H1 = o.forward(*ins, nthreads=1)
+    y4, H4 = o.forward(*ins, nthreads=4)
+    assert np.array_equal(y1, y4) and np.array_equal(H1, H4)
+    g1 = o.backward(*ins, dy, nthreads=1)
+    g4 = o.backward(*ins, dy, nthreads=4)
+    for name in g1:
+        assert np.array_equal(g1[name], g4[name]), name
+
+
+FORWARD_PINS = [pin_t1_closed_form, pin_f_one_forward, pin_zero_w_zero_f_forward, pin_readout_linear_in_q,
+                pin_checkpoints, pin_convex_bound, pin_permutations, pin_rnn_embedding_forward_backward]
+BACKWARD_PINS = [pin_f_one_backward, pin_zero_w_zero_f_backward, pin_finite_differences_small,
+                 pin_finite_differences_full_state]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + [pin_thread_invariance]

@@ -1,0 +1,76 @@
+"""Plant plausible slips in copies of the oracle source and check that the pins
+catch every one (CPU only; the real oracle is never modified).
+
+Each mutant is one textual edit of oracle/m2rnn_ref.c, compiled with gcc into a
+temporary library and run through the pin suite of tests/oracle_pins.py.  A
+mutant that passes every pin would mean the pins cannot tell that slip from the
+method, so the test fails.
+"""
+import os
+
+import pytest
+
+import oracle
+import oracle_pins
+from oracle import build as oracle_build
+
+SRC = oracle_build.SRC
+
+# (id, text in the oracle, replacement): one slip each
+MUTANTS = [
+    ("drop_rank1_write", "A[i * V + j] = s + kt[i] * vt[j];", "A[i * V + j] = s;"),
+    ("transposed_W_forward", "s += Hp[i * V + l] * Wn[l * V + j];", "s += Hp[i * V + l] * Wn[j * V + l];"),
+    ("gate_swapped", "Hn[e] = ft * Hp[e] + (1.0 - ft) * Z[e];", "Hn[e] = (1.0 - ft) * Hp[e] + ft * Z[e];"),
+    ("gate_drops_history", "Hn[e] = ft * Hp[e] + (1.0 - ft) * Z[e];", "Hn[e] = (1.0 - ft) * Z[e];"),
+    ("readout_of_old_state", "memcpy(H, Hn, sizeof(double) * S);\n      readout(J, b, n, t, H);",
+     "readout(J, b, n, t, H);\n      memcpy(H, Hn, sizeof(double) * S);"),
+    ("drop_value_residual", "yt[j] = s + wrn[j] * vt[j];", "yt[j] = s;"),
+    ("readout_uses_k", "const double* qt = J->q + ((size_t)b * T + t) * K;\n  const double* vt",
+     "const double* qt = J->k + ((size_t)b * T + t) * K;\n  const double* vt"),
+    ("ckpt_after_step", "memcpy(dst, H, sizeof(double) * S);", "memcpy(dst, H, sizeof(double) * S); dst[0] += 1e-3;"),
+    ("R_drops_future_gradient", "R[i * V + j] = C[i * V + j] + qt[i] * u[j];", "R[i * V + j] = qt[i] * u[j];"),
+    ("C_drops_DW", "C[i * V + l] = ft * R[i * V + l] + a;", "C[i * V + l] = ft * R[i * V + l];"),
+    ("C_drops_direct_path", "C[i * V + l] = ft * R[i * V + l] + a;", "C[i * V + l] = a;"),
+    ("C_transposed_W", "a += D[i * V + j] * Wn[l * V + j];", "a += D[i * V + j] * Wn[j * V + l];"),
+    ("D_drops_gate", "D[e] = ((1.0 - ft) * R[e]) * (1.0 - Z[e] * Z[e]);", "D[e] = R[e] * (1.0 - Z[e] * Z[e]);"),
+    ("D_wrong_tanh_derivative", "D[e] = ((1.0 - ft) * R[e]) * (1.0 - Z[e] * Z[e]);",
+     "D[e] = ((1.0 - ft) * R[e]) * (1.0 - Z[e]);"),
+    ("df_wrong_sign", "s += R[e] * (Hp[e] - Z[e]);", "s += R[e] * (Z[e] - Hp[e]);"),
+    ("df_uses_new_state", "s += R[e] * (Hp[e] - Z[e]);", "s += R[e] * (Hc[e] - Z[e]);"),
+    ("dW_uses_new_state", "a += Hp[i * V + l] * D[i * V + j];", "a += Hc[i * V + l] * D[i * V + j];"),
+    ("dW_transposed", "dWc[l * V + j] += a;", "dWc[j * V + l] += a;"),
+    ("dq_uses_old_state", "a += Hc[i * V + j] * u[j];", "a += Hp[i * V + j] * u[j];"),
+    ("dk_drops_v", "a += D[i * V + j] * vt[j];", "a += D[i * V + j];"),
+    ("dv_drops_residual", "dvt[j] = a + wrn[j] * u[j];", "dvt[j] = a;"),
+    ("dwr_drops_v", "dwrc[j] += u[j] * vt[j];", "dwrc[j] += u[j];"),
+    ("ignores_dH_T", "if (J->dH_T) memcpy(C,", "if (0) memcpy(C,"),
+    ("dq_keeps_last_head", "sq += J.dq_part", "sq = J.dq_part"),
+    ("dk_keeps_last_head", "sk += J.dk_part", "sk = J.dk_part"),
+    ("dW_keeps_last_batch", "s += J.dW_part", "s = J.dW_part"),
+]
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(SRC) as fh:
+        return fh.read()
+
+
+@pytest.mark.parametrize("mid,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, source, mid, old, new):
+    assert source.count(old) == 1, f"mutation anchor for {mid} must occur exactly once in the oracle"
+    mutated = source.replace(old, new)
+    src = tmp_path / "m2rnn_ref.c"
+    src.write_text(mutated)
+    # the header sits next to the real source
+    lib = oracle_build.build(str(src), str(tmp_path / f"lib_{mid}.so"),
+                             extra_flags=("-I" + os.path.dirname(SRC),))
+    mutant = oracle.Oracle(lib)
+    caught = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(mutant)
+        except AssertionError as exc:
+            caught.append(f"{pin.__name__}: {exc}")
+            break
+    assert caught, f"mutant {mid} passed every pin"
