@@ -1,0 +1,122 @@
+/*
+ * m2rnn.h -- C ABI of libm2rnn.so, the MI355X (gfx950) M2RNN scan.
+ *
+ * The operation, from the M2RNN paper-discussion slides (reading of
+ * Mishra, Tan, Stoica, Gonzalez, Dao, arXiv:2603.14360v2):
+ *
+ *   slide "Write, transform, retain, and read a matrix state" (paper
+ *   Eqs. (10)-(12)): for every batch row b and value head n, with H_0 = 0,
+ *       Z_t = tanh(H_{t-1} W + k_t v_t^T)
+ *       H_t = f_t H_{t-1} + (1 - f_t) Z_t
+ *       y_t = H_t^T q_t + w_r (.) v_t
+ *   H_t, Z_t are K x V (K = 64, V = 16), W is V x V, f_t a scalar per head.
+ *
+ *   slide "Shared queries and keys buy more recurrent capacity" (paper
+ *   Alg. 1 / App. A): one q_t and one k_t per token, shared by the N value
+ *   heads; v, f, W and w_r are per head.
+ *
+ *   slide "Backup: the recurrent gradient needs both paths": the backward
+ *   (R_t = C_t + q_t u_t^T, D_t = ((1-f_t) R_t) (.) (1 - Z_t (.) Z_t),
+ *   C_{t-1} = f_t R_t + D_t W^T, dL/df_t = <R_t, H_{t-1} - Z_t>,
+ *   dL/dW = sum_t H_{t-1}^T D_t), completed by the plain chain rule for
+ *   q, k, v and w_r.
+ *
+ * Conventions for every entry point:
+ *   - All tensors are dense, row-major (C-contiguous) DEVICE buffers owned by
+ *     the caller.  The library never allocates, frees or synchronises, and
+ *     keeps no state between calls except the thread-local error message.
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls are
+ *     asynchronous on that stream; results are ready when it is.
+ *   - Inputs q, k, v, f, W, w_r all have dtype `dtype` (M2RNN_F32 or
+ *     M2RNN_BF16, bfloat16 as raw 16-bit words).  The state, every
+ *     accumulation, y, H_T, checkpoints and all gradients are float32.
+ *   - q, k, v, y, H_T, H_ckpt, dy, dH_T and every gradient buffer must be
+ *     16-byte aligned; f, W, w_r need their element alignment.
+ *   - Outputs are fully overwritten; they need no zeroing.
+ *   - Sizes: B, T, N >= 0.  B == 0 or N == 0 is a no-op.  T == 0 leaves
+ *     y empty and sets H_T = H_0 = 0.  This build supports K == 64 and
+ *     V == 16 only (other values return M2RNN_ERR_UNSUPPORTED).
+ *   - f is used as given (not clamped); the method expects f in [0, 1].
+ *   - Errors are reported before anything is launched: a negative status is
+ *     returned and m2rnn_last_error() describes it.  A failed kernel launch
+ *     returns M2RNN_ERR_HIP.
+ */
+#ifndef M2RNN_H
+#define M2RNN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  M2RNN_OK = 0,
+  M2RNN_ERR_INVALID_ARG = -1, /* null/misaligned pointer, negative size, bad dtype */
+  M2RNN_ERR_UNSUPPORTED = -2, /* K != 64 or V != 16, or a size beyond the limits */
+  M2RNN_ERR_WORKSPACE = -3,   /* backward workspace missing or too small */
+  M2RNN_ERR_HIP = -4          /* the HIP runtime reported an error */
+} m2rnn_status;
+
+typedef enum { M2RNN_F32 = 0, M2RNN_BF16 = 1 } m2rnn_dtype;
+
+/*
+ * Forward scan (slide "Write, transform, retain, and read a matrix state",
+ * paper Eqs. (10)-(12)).
+ *   q, k    [B][T][K]     inputs, shared by the N heads of batch row b
+ *   v       [B][T][N][V]
+ *   f       [B][T][N]
+ *   W       [N][V][V]     (H W)[i][j] = sum_l H[i][l] * W[n][l][j]
+ *   w_r     [N][V]
+ *   y       [B][T][N][V]  float32 out, readout of the updated state H_t
+ *   H_T     [B][N][K][V]  float32 out, state after step T
+ *   H_ckpt  [B][N][ceil(T/ckpt_every)][K][V] float32 out, H at
+ *           t = j * ckpt_every (j = 0 gives H_0 = 0); NULL with
+ *           ckpt_every == 0 stores none.  These are what m2rnn_backward
+ *           restarts its recompute from.
+ */
+int m2rnn_forward(int B, int T, int N, int K, int V, int dtype,
+                  const void* q, const void* k, const void* v, const void* f,
+                  const void* W, const void* w_r,
+                  float* y, float* H_T, float* H_ckpt, int ckpt_every,
+                  void* stream);
+
+/*
+ * Bytes of device workspace m2rnn_backward needs for these sizes (0 if none).
+ */
+size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckpt_every);
+
+/*
+ * Backward scan: gradients of L = sum(y * dy) + sum(H_T * dH_T) (slide
+ * "Backup: the recurrent gradient needs both paths", plus the chain rule
+ * for q, k, v, w_r).
+ *   q, k, v, f, W, w_r   the forward's inputs (dtype `dtype`)
+ *   H_ckpt, ckpt_every   the forward's checkpoints (ckpt_every >= 1)
+ *   dy      [B][T][N][V] float32
+ *   dH_T    [B][N][K][V] float32, or NULL for zero
+ *   dq, dk  [B][T][K]    float32 out, summed over the N heads
+ *   dv      [B][T][N][V] float32 out
+ *   df      [B][T][N]    float32 out
+ *   dW      [N][V][V]    float32 out, summed over batch rows and time
+ *   dw_r    [N][V]       float32 out, summed over batch rows and time
+ *   workspace            device buffer of at least
+ *                        m2rnn_backward_workspace_bytes(...) bytes,
+ *                        16-byte aligned; contents on entry are ignored
+ */
+int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
+                   const void* q, const void* k, const void* v, const void* f,
+                   const void* W, const void* w_r,
+                   const float* H_ckpt, int ckpt_every,
+                   const float* dy, const float* dH_T,
+                   float* dq, float* dk, float* dv, float* df,
+                   float* dW, float* dw_r,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message for the last non-OK status on the calling thread ("" if none). */
+const char* m2rnn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* M2RNN_H */

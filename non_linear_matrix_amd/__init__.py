@@ -1,0 +1,141 @@
+"""Python binding of libm2rnn.so, the MI355X M2RNN scan (C ABI in include/m2rnn.h).
+
+Argument marshalling only: every step of the scan runs in the HIP kernels of
+libm2rnn.so.  PyTorch provides device memory and the current HIP stream.  If
+the library is missing or fails to load, importing this package raises: there
+is no CPU fallback.
+
+    import non_linear_matrix_amd as m2
+    y, H_T = m2.forward(q, k, v, f, W, w_r)                    # H_0 = 0
+    y, H_T, H_ckpt = m2.forward(q, k, v, f, W, w_r, ckpt_every=64)
+    grads = m2.backward(q, k, v, f, W, w_r, H_ckpt, 64, dy)     # dict
+
+Shapes (K = 64, V = 16): q, k [B,T,K]; v [B,T,N,V]; f [B,T,N]; W [N,V,V];
+w_r [N,V]; all six float32 or all six bfloat16, contiguous, on one GPU.
+Outputs and gradients are float32.
+"""
+import ctypes
+import os
+
+import torch
+
+K = 64
+V = 16
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libm2rnn.so")
+
+M2RNN_OK = 0
+M2RNN_ERR_INVALID_ARG = -1
+M2RNN_ERR_UNSUPPORTED = -2
+M2RNN_ERR_WORKSPACE = -3
+M2RNN_ERR_HIP = -4
+M2RNN_F32 = 0
+M2RNN_BF16 = 1
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m non_linear_matrix_amd.build`")
+lib = ctypes.CDLL(LIB_PATH)
+
+_i = ctypes.c_int
+_p = ctypes.c_void_p
+lib.m2rnn_forward.restype = _i
+lib.m2rnn_forward.argtypes = [_i] * 6 + [_p] * 6 + [_p, _p, _p, _i, _p]
+lib.m2rnn_backward_workspace_bytes.restype = ctypes.c_size_t
+lib.m2rnn_backward_workspace_bytes.argtypes = [_i] * 6
+lib.m2rnn_backward.restype = _i
+lib.m2rnn_backward.argtypes = [_i] * 6 + [_p] * 6 + [_p, _i] + [_p, _p] + [_p] * 6 + [_p, ctypes.c_size_t, _p]
+lib.m2rnn_last_error.restype = ctypes.c_char_p
+lib.m2rnn_last_error.argtypes = []
+
+
+class M2RNNError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"m2rnn status {status}: {msg}")
+        self.status = status
+
+
+def _check(status):
+    if status != M2RNN_OK:
+        raise M2RNNError(status, lib.m2rnn_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return M2RNN_F32
+    if t.dtype == torch.bfloat16:
+        return M2RNN_BF16
+    raise TypeError(f"inputs must be float32 or bfloat16, got {t.dtype}")
+
+
+def _sizes(q, v):
+    B, T, Kq = q.shape
+    N, Vv = v.shape[2], v.shape[3]
+    return B, T, N, Kq, Vv
+
+
+def m2rnn_forward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, y, H_T, H_ckpt, ckpt_every, stream):
+    """Raw C-ABI call with ctypes pointers; returns the status code."""
+    return lib.m2rnn_forward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, y, H_T, H_ckpt, ckpt_every, stream)
+
+
+def m2rnn_backward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_ckpt, ckpt_every, dy, dH_T,
+                   dq, dk, dv, df, dW, dw_r, workspace, workspace_bytes, stream):
+    """Raw C-ABI call with ctypes pointers; returns the status code."""
+    return lib.m2rnn_backward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_ckpt, ckpt_every, dy, dH_T,
+                              dq, dk, dv, df, dW, dw_r, workspace, workspace_bytes, stream)
+
+
+def m2rnn_backward_workspace_bytes(B, T, N, K_=K, V_=V, ckpt_every=64):
+    return int(lib.m2rnn_backward_workspace_bytes(B, T, N, K_, V_, ckpt_every))
+
+
+def m2rnn_last_error():
+    return lib.m2rnn_last_error().decode()
+
+
+def forward(q, k, v, f, W, w_r, ckpt_every=0, out=None):
+    """y [B,T,N,V], H_T [B,N,K,V] (float32) and, if ckpt_every > 0,
+    H_ckpt [B,N,ceil(T/ckpt_every),K,V].  `out` may pass preallocated
+    (y, H_T[, H_ckpt]) tensors."""
+    B, T, N, Kq, Vv = _sizes(q, v)
+    dev = q.device
+    if out is None:
+        y = torch.empty((B, T, N, Vv), device=dev, dtype=torch.float32)
+        H_T = torch.empty((B, N, Kq, Vv), device=dev, dtype=torch.float32)
+        H_ck = None
+        if ckpt_every > 0:
+            H_ck = torch.empty((B, N, (T + ckpt_every - 1) // ckpt_every, Kq, Vv), device=dev, dtype=torch.float32)
+    else:
+        y, H_T = out[0], out[1]
+        H_ck = out[2] if len(out) > 2 else None
+    _check(lib.m2rnn_forward(B, T, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W),
+                             _ptr(w_r), _ptr(y), _ptr(H_T), _ptr(H_ck), int(ckpt_every), _stream(dev)))
+    return (y, H_T) if H_ck is None else (y, H_T, H_ck)
+
+
+def backward(q, k, v, f, W, w_r, H_ckpt, ckpt_every, dy, dH_T=None, out=None, workspace=None):
+    """Gradients of sum(y*dy) + sum(H_T*dH_T): dict dq, dk [B,T,K]; dv [B,T,N,V];
+    df [B,T,N]; dW [N,V,V]; dw_r [N,V] (float32)."""
+    B, T, N, Kq, Vv = _sizes(q, v)
+    dev = q.device
+    if out is None:
+        out = dict(dq=torch.empty((B, T, Kq), device=dev), dk=torch.empty((B, T, Kq), device=dev),
+                   dv=torch.empty((B, T, N, Vv), device=dev), df=torch.empty((B, T, N), device=dev),
+                   dW=torch.empty((N, Vv, Vv), device=dev), dw_r=torch.empty((N, Vv), device=dev))
+    nbytes = int(lib.m2rnn_backward_workspace_bytes(B, T, N, Kq, Vv, int(ckpt_every)))
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty((nbytes,), device=dev, dtype=torch.uint8)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.m2rnn_backward(B, T, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W),
+                              _ptr(w_r), _ptr(H_ckpt), int(ckpt_every), _ptr(dy), _ptr(dH_T),
+                              _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["df"]),
+                              _ptr(out["dW"]), _ptr(out["dw_r"]), _ptr(workspace), wbytes, _stream(dev)))
+    return out

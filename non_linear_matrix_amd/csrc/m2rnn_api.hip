@@ -1,0 +1,107 @@
+// m2rnn_api.hip -- the C ABI of libm2rnn.so (declared in include/m2rnn.h):
+// argument validation, error reporting and kernel dispatch.  No allocation,
+// no synchronisation, no state beyond the thread-local error message.
+#include "m2rnn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "m2rnn_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Largest element count any single tensor may have (64-bit indexing is used in
+// the kernels; this only keeps products of int sizes from overflowing).
+constexpr long long kMaxElems = 1LL << 40;
+
+int check_sizes(int B, int T, int N, int K, int V, int dtype) {
+  if (B < 0 || T < 0 || N < 0) return fail(M2RNN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d T=%d N=%d)", B, T, N);
+  if (K != 64 || V != 16) return fail(M2RNN_ERR_UNSUPPORTED, "this build supports K=64, V=16 only (got K=%d V=%d)", K, V);
+  if (dtype != M2RNN_F32 && dtype != M2RNN_BF16) return fail(M2RNN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if ((long long)B * T * N * V > kMaxElems) return fail(M2RNN_ERR_UNSUPPORTED, "problem too large");
+  if ((long long)B * ((N + 3) / 4) > 0x7fffffffLL) return fail(M2RNN_ERR_UNSUPPORTED, "too many (batch, head) groups");
+  return M2RNN_OK;
+}
+
+// Check a required device pointer: non-null when the tensor is non-empty, and
+// aligned to `align` bytes.
+int need(const void* p, const char* name, long long elems, size_t align) {
+  if (elems <= 0) return M2RNN_OK;
+  if (!p) return fail(M2RNN_ERR_INVALID_ARG, "%s must not be NULL", name);
+  if (!aligned(p, align)) return fail(M2RNN_ERR_INVALID_ARG, "%s must be %zu-byte aligned", name, align);
+  return M2RNN_OK;
+}
+
+}  // namespace
+
+extern "C" const char* m2rnn_last_error(void) { return g_err; }
+
+extern "C" int m2rnn_forward(int B, int T, int N, int K, int V, int dtype,
+                             const void* q, const void* k, const void* v, const void* f,
+                             const void* W, const void* w_r,
+                             float* y, float* H_T, float* H_ckpt, int ckpt_every,
+                             void* stream) {
+  g_err[0] = 0;
+  int st = check_sizes(B, T, N, K, V, dtype);
+  if (st) return st;
+  const size_t es = dtype == M2RNN_F32 ? 4 : 2;
+  const long long BT = (long long)B * T, BTN = BT * N, BN = (long long)B * N;
+  if (ckpt_every < 0) return fail(M2RNN_ERR_INVALID_ARG, "ckpt_every must be >= 0");
+  if ((H_ckpt != nullptr) != (ckpt_every > 0))
+    return fail(M2RNN_ERR_INVALID_ARG, "H_ckpt and ckpt_every > 0 go together");
+  if ((st = need(q, "q", BT * K, 16)) || (st = need(k, "k", BT * K, 16)) || (st = need(v, "v", BTN * V, 16)) ||
+      (st = need(f, "f", BTN, es)) || (st = need(W, "W", (long long)N * V * V * (BN > 0), es)) ||
+      (st = need(w_r, "w_r", (long long)N * V * (BN > 0), es)) || (st = need(y, "y", BTN * V, 16)) ||
+      (st = need(H_T, "H_T", BN * K * V, 16)))
+    return st;
+  const int nck = ckpt_every > 0 ? (T + ckpt_every - 1) / ckpt_every : 0;
+  if (ckpt_every > 0 && (st = need(H_ckpt, "H_ckpt", BN * nck * K * V, 16))) return st;
+  if (BN == 0) return M2RNN_OK;
+
+  hipStream_t s = (hipStream_t)stream;
+  if (T == 0) {  // H_T = H_0 = 0; y is empty
+    hipError_t e = m2rnn::launch_fill_zero(H_T, (size_t)BN * K * V, s);
+    return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "zero fill: %s", hipGetErrorString(e));
+  }
+  m2rnn::FwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.wr = w_r;
+  a.y = y; a.H_T = H_T; a.H_ckpt = ckpt_every > 0 ? H_ckpt : nullptr;
+  a.B = B; a.T = T; a.N = N; a.ckpt_every = ckpt_every; a.nck = nck;
+  hipError_t e = m2rnn::launch_forward(a, dtype, s);
+  if (e != hipSuccess) return fail(M2RNN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  return M2RNN_OK;
+}
+
+extern "C" size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckpt_every) {
+  (void)B; (void)T; (void)N; (void)K; (void)V; (void)ckpt_every;
+  return 0;
+}
+
+extern "C" int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
+                              const void* q, const void* k, const void* v, const void* f,
+                              const void* W, const void* w_r, const float* H_ckpt, int ckpt_every,
+                              const float* dy, const float* dH_T, float* dq, float* dk, float* dv,
+                              float* df, float* dW, float* dw_r, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  (void)q; (void)k; (void)v; (void)f; (void)W; (void)w_r; (void)H_ckpt; (void)ckpt_every;
+  (void)dy; (void)dH_T; (void)dq; (void)dk; (void)dv; (void)df; (void)dW; (void)dw_r;
+  (void)workspace; (void)workspace_bytes; (void)stream;
+  g_err[0] = 0;
+  int st = check_sizes(B, T, N, K, V, dtype);
+  if (st) return st;
+  return fail(M2RNN_ERR_UNSUPPORTED, "backward not built yet");
+}

@@ -1,0 +1,140 @@
+// m2rnn_device.h -- gfx950 device helpers shared by the M2RNN scan kernels.
+//
+// State layout ("transposed frame").  A head's K x V = 64 x 16 state H is held
+// as four 16 x 16 row tiles j = 0..3 (rows kk = 16 j .. 16 j + 15).  Each tile
+// lives in one MFMA 16x16 accumulator (4 VGPRs per lane) holding the
+// TRANSPOSED tile: lane l = 16 g + m, register i holds
+//      P[j][i] = c * H[kk = 16 j + m][v = 4 g + i],        c = 2 / ln 2,
+// i.e. row (4g+i), column m of the 16x16 matrix H_tile^T.  In that layout the
+// step's contraction (H W)^T = W^T H^T is an MFMA whose B operand is the
+// accumulator itself, so the state never leaves registers between steps.
+// The scale c turns tanh(x) = 1 - 2 / (1 + e^{2x}) into one v_exp_f32 of the
+// scaled pre-activation (exp2(c x) = e^{2x}).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace m2rnn {
+
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kScale = 2.8853900817779268f;     // 2 / ln 2
+constexpr float kInvScale = 0.34657359027997264f; // ln 2 / 2
+
+struct bf16_t {
+  uint16_t bits;
+};
+
+// ---------------------------------------------------------------- input loads
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float((uint32_t)x.bits << 16); }
+
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+  typedef f4 raw;
+  __device__ static raw load(const float* p) { return *(const f4*)p; }
+  __device__ static f4 to_f4(raw r) { return r; }
+  __device__ static raw zero() { return f4{0.f, 0.f, 0.f, 0.f}; }
+};
+template <> struct Vec4<bf16_t> {
+  typedef uint2 raw;
+  __device__ static raw load(const bf16_t* p) { return *(const uint2*)p; }
+  __device__ static f4 to_f4(raw r) {
+    return f4{__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xffff0000u),
+              __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xffff0000u)};
+  }
+  __device__ static raw zero() { return uint2{0u, 0u}; }
+};
+
+// ------------------------------------------------------- bf16 hi/lo splitting
+// x = hi + lo + O(2^-17 |x|) with hi = bf16(x), lo = bf16(x - hi), both
+// round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  bf16x2 h = __builtin_convertvector((f2{x0, x1}), bf16x2);
+  hi = __builtin_bit_cast(uint32_t, h);
+  float l0 = x0 - __uint_as_float(hi << 16);
+  float l1 = x1 - __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{l0, l1}), bf16x2));
+}
+
+// B operand of v_mfma_f32_16x16x32_bf16 from an accumulator tile: k-slots
+// 0..3 of lane group g carry hi(x[0..3]), slots 4..7 carry lo(x[0..3]).
+__device__ __forceinline__ bf16x8 split_operand(f4 x) {
+  uint32_t h01, l01, h23, l23;
+  split2(x[0], x[1], h01, l01);
+  split2(x[2], x[3], h23, l23);
+  return __builtin_bit_cast(bf16x8, (u32x4{h01, h23, l01, l23}));
+}
+
+__device__ __forceinline__ f4 mfma_bf16(bf16x8 a, bf16x8 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Pack eight floats (already representable, or rounded RNE) into a bf16x8.
+__device__ __forceinline__ bf16x8 pack8(const float* w) {
+  u32x4 u;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    u[s] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{w[2 * s], w[2 * s + 1]}), bf16x2));
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// ------------------------------------------- the per-step contraction W^T P
+// Given a state tile in accumulator layout (lane 16g+m, register i holds
+// P^T[4g+i][m]), returns the accumulator-layout tile (W^T P^T)[v'][m] =
+// sum_v W[v][v'] P^T[v][m], i.e. the transposed tile of P W.
+template <typename TIn> struct WOperand;
+
+// bfloat16 inputs: W is exact in bf16; the fp32 state is split hi + lo and
+// both halves ride in one v_mfma_f32_16x16x32_bf16 (A = [W^T | W^T]).
+template <> struct WOperand<bf16_t> {
+  bf16x8 a;
+  __device__ void load(const bf16_t* Wn, int g, int m) {
+    float w[8];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float x = Wn ? to_f32(Wn[(4 * g + s) * 16 + m]) : 0.0f;
+      w[s] = w[s + 4] = x;
+    }
+    a = pack8(w);
+  }
+  __device__ f4 times_state(f4 p) const { return mfma_bf16(a, split_operand(p), f4{0.f, 0.f, 0.f, 0.f}); }
+};
+
+// float32 inputs: four exact v_mfma_f32_16x16x4_f32; accumulator register r
+// is the B operand of instruction r as is.
+template <> struct WOperand<float> {
+  float a[4];
+  __device__ void load(const float* Wn, int g, int m) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) a[r] = Wn ? Wn[(4 * g + r) * 16 + m] : 0.0f;
+  }
+  __device__ f4 times_state(f4 p) const {
+    f4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 4; ++r) d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], p[r], d, 0, 0, 0);
+    return d;
+  }
+};
+
+// ------------------------------------------------------ cross-lane reductions
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// Sum over the 16 lanes of each row (lanes 16g .. 16g+15); every lane of the
+// row ends with the row sum.
+__device__ __forceinline__ float row_sum16(float x) {
+  x += dpp<0xB1>(x);  // quad_perm [1,0,3,2]
+  x += dpp<0x4E>(x);  // quad_perm [2,3,0,1]
+  x += dpp<0x141>(x); // row_half_mirror
+  x += dpp<0x140>(x); // row_mirror
+  return x;
+}
+
+}  // namespace m2rnn
