@@ -1,0 +1,183 @@
+"""Benchmark of the MI355X M2RNN scan: head-tokens/s for forward + backward.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one pass of the whole scan path over one batch of seeded synthetic
+inputs already resident in HBM: the forward with state checkpoints every 64
+steps, then the backward (recompute from the checkpoints, reverse sweep, head
+and batch reductions).  `--pass fwd` times the forward alone.  Prints ONE JSON
+line.  The roofline object prices the dominant kernel's algorithmic work
+(2*K*V^2 MFMA flop per head-token per state contraction) against MI355X's
+published dense fp32 matrix peak; its duration is measured with HIP events
+recorded on the stream the kernel runs on.  The CPU baseline is the fp64
+oracle, timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix
+HBM_PEAK_GBS = 8000.0
+K_DIM, V_DIM = 64, 16
+FLOP_PER_CONTRACTION = 2 * K_DIM * V_DIM * V_DIM   # H W per head-token
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--pass", dest="which", choices=["fwdbwd", "fwd"], default="fwdbwd")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0)
+    return ap.parse_args()
+
+
+def algorithmic_bytes_fwd(w):
+    """HBM bytes the forward must move: inputs once, y and H_T (fp32) once,
+    checkpoints once."""
+    s = 2 if w.dtype == "bf16" else 4
+    B, T, N = w.B, w.T, w.N
+    ins = (2 * B * T * K_DIM + B * T * N * V_DIM + B * T * N + N * V_DIM * V_DIM + N * V_DIM) * s
+    outs = (B * T * N * V_DIM + B * N * K_DIM * V_DIM) * 4
+    ck = B * N * ((T + 63) // 64) * K_DIM * V_DIM * 4 if w.ckpt_every else 0
+    return ins + outs + ck
+
+
+def cpu_baseline(w, x, which, threads):
+    import numpy as np
+    import oracle
+    nthreads = threads or min(16, os.cpu_count() or 1)
+    # bounded sample: the first Bs batch rows and Ns heads at the full length
+    Bs, Ns = min(w.B, 2), min(w.N, max(1, nthreads // 2))
+    T = w.T
+    if which == "fwdbwd":
+        T = min(T, 2048)
+    sl = dict(q=x["q"][:Bs, :T], k=x["k"][:Bs, :T], v=x["v"][:Bs, :T, :Ns], f=x["f"][:Bs, :T, :Ns],
+              W=x["W"][:Ns], wr=x["wr"][:Ns])
+    ins = [sl[n].double().numpy() for n in ("q", "k", "v", "f", "W", "wr")]
+    t0 = time.perf_counter()
+    oracle.forward(*ins, nthreads=nthreads)
+    if which == "fwdbwd":
+        dy = x["dy"][:Bs, :T, :Ns].double().numpy()
+        oracle.backward(*ins, dy, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    htok = Bs * T * Ns
+    return {"value": htok / dt, "unit": "head-tokens/s", "cores": min(nthreads, Bs * Ns), "kind": "oracle",
+            "sample": f"{'fwd+bwd' if which == 'fwdbwd' else 'fwd'} fp64 oracle on B={Bs} T={T} N={Ns} "
+                      f"(first rows/heads of the same inputs), {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the scan shards over batch rows/heads with no communication, "
+                                   "but no multi-GPU path is built)"}))
+        return 2
+
+    import torch
+    import m2rnn_inputs
+    import non_linear_matrix_amd as m2
+
+    name = args.workload or ("fwdbwd_bf16_B32_T4096_N64" if args.which == "fwdbwd" else "fwd_bf16_B32_T4096_N64")
+    w = m2rnn_inputs.WORKLOADS[name]
+    ck = 64
+    x_cpu = m2rnn_inputs.make_workload(w, seed=args.seed, with_dy=(args.which == "fwdbwd"))
+    x = {k: v.cuda() for k, v in x_cpu.items()}
+    dev = x["q"].device
+    B, T, N = w.B, w.T, w.N
+    y = torch.empty((B, T, N, V_DIM), device=dev)
+    HT = torch.empty((B, N, K_DIM, V_DIM), device=dev)
+    Hck = torch.empty((B, N, (T + ck - 1) // ck, K_DIM, V_DIM), device=dev)
+    fwd_out = (y, HT, Hck) if args.which == "fwdbwd" else (y, HT)
+    grads = ws = None
+    if args.which == "fwdbwd":
+        grads = dict(dq=torch.empty((B, T, K_DIM), device=dev), dk=torch.empty((B, T, K_DIM), device=dev),
+                     dv=torch.empty((B, T, N, V_DIM), device=dev), df=torch.empty((B, T, N), device=dev),
+                     dW=torch.empty((N, V_DIM, V_DIM), device=dev), dw_r=torch.empty((N, V_DIM), device=dev))
+        nbytes = m2.m2rnn_backward_workspace_bytes(B, T, N, K_DIM, V_DIM, ck)
+        ws = torch.empty((max(nbytes, 1),), device=dev, dtype=torch.uint8)
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        m2.forward(x["q"], x["k"], x["v"], x["f"], x["W"], x["wr"],
+                   ckpt_every=ck if args.which == "fwdbwd" else 0, out=fwd_out)
+        if ev is not None:
+            ev[1].record(stream)
+        if args.which == "fwdbwd":
+            m2.backward(x["q"], x["k"], x["v"], x["f"], x["W"], x["wr"], Hck, ck, x["dy"],
+                        out=grads, workspace=ws)
+            if ev is not None:
+                ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps if args.which == "fwdbwd" else 0.0
+
+    htok = w.head_tokens
+    value = htok * args.steps / (total_ms * 1e-3)
+    # dominant kernel and its algorithmic MFMA work per launch
+    if args.which == "fwdbwd" and bwd_ms > fwd_ms:
+        dom, dom_ms, flops = "m2rnn_backward", bwd_ms, 3 * FLOP_PER_CONTRACTION * htok
+    else:
+        dom, dom_ms, flops = "m2rnn_fwd_kernel", fwd_ms, FLOP_PER_CONTRACTION * htok
+    achieved = flops / (dom_ms * 1e-3) / 1e12
+    res = {
+        "metric": "M2RNN scan head-tokens/s (K=64,V=16) fwd & bwd; % of HBM/MFMA roofline",
+        "value": value,
+        "unit": "head-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; SiLU(N(0,1)) q,k,v; sigmoid(N(2,1)) f; N(0,1/16) W; N(0,1) w_r, dy)",
+        "config": {"workload": name, "pass": "forward+backward" if args.which == "fwdbwd" else "forward",
+                   "B": B, "T": T, "N": N, "K": K_DIM, "V": V_DIM, "input_dtype": w.dtype,
+                   "ckpt_every": ck if args.which == "fwdbwd" else 0},
+        "fwd_ms": fwd_ms,
+        "bwd_ms": bwd_ms,
+        "fwd_head_tokens_per_s": htok / (fwd_ms * 1e-3),
+        "bwd_head_tokens_per_s": htok / (bwd_ms * 1e-3) if bwd_ms else None,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": None, "kernel": dom,
+                     "kernel_ms": dom_ms,
+                     "algorithmic": f"{flops / htok:.0f} flop/head-token x {htok} head-tokens per launch"},
+        "hbm": {"fwd_algorithmic_bytes": algorithmic_bytes_fwd(w),
+                "fwd_achieved_GBs": algorithmic_bytes_fwd(w) / (fwd_ms * 1e-3) / 1e9, "peak_GBs": HBM_PEAK_GBS},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, x_cpu, args.which, args.cpu_threads)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -25,24 +25,33 @@
 #include "m2rnn_device.h"
 #include "m2rnn_internal.h"
 
+#include <stdlib.h>
+
 namespace m2rnn {
 
-template <int NW, int TC>
-struct FwdSmem {
-  // per buffer: K_s[TC][64], Q_s[TC][64], V_s[TC][NW][16], F_s[TC][NW][4]
-  static constexpr int kPerStep = 64 + 64 + NW * 16 + NW * 4;
-  static constexpr int kBuf = TC * kPerStep;
-  static constexpr int kY = TC * NW * 16;
-  static constexpr int kFloats = 2 * kBuf + kY;
+// Launch shape: a workgroup serves HPW heads of one batch row; each head's four
+// row tiles are spread over WPH = 4 / TPW waves (TPW tiles per wave).  More
+// waves per head means more independent instruction streams per SIMD, which
+// is what the per-step VALU work needs; the readout of a head then combines
+// WPH per-wave partial sums through LDS.
+template <int HPW, int TPW, int TC>
+struct FwdCfg {
+  static constexpr int WPH = 4 / TPW;
+  static constexpr int NWAVES = HPW * WPH;
+  static constexpr int NT = 64 * NWAVES;
+  // one staging buffer: K_s[TC][64], Q_s[TC][64], V_s[TC][HPW][16], F_s[TC][HPW][4]
+  static constexpr int kBuf = TC * (128 + HPW * 20);
+  static constexpr int kY = TC * HPW * WPH * 16;  // per-wave readout partials
+  static constexpr int kWr = HPW * 16;
+  static constexpr int kFloats = 2 * kBuf + kY + kWr;
   static constexpr int kBytes = kFloats * 4;
 };
 
-template <typename TIn, int NW, int TC>
+template <typename TIn, int HPW, int NT, int TC>
 struct FwdStager {
   typedef typename Vec4<TIn>::raw raw;
-  static constexpr int kThreads = 64 * NW;
-  static constexpr int kQK = (2 * TC * 16 + kThreads - 1) / kThreads;  // 4-vectors of q and k
-  static constexpr int kV = (TC * NW * 4 + kThreads - 1) / kThreads;   // 4-vectors of v
+  static constexpr int kQK = (2 * TC * 16 + NT - 1) / NT;   // 4-vectors of q and k
+  static constexpr int kV = (TC * HPW * 4 + NT - 1) / NT;   // 4-vectors of v
   raw qk[kQK];
   raw vv[kV];
   float ff;
@@ -50,7 +59,7 @@ struct FwdStager {
   __device__ void load(const FwdArgs& a, int b, int n0, int t0, int tid) {
 #pragma unroll
     for (int r = 0; r < kQK; ++r) {
-      int u = tid + r * kThreads;           // [0, 2*TC*16)
+      int u = tid + r * NT;                 // [0, 2*TC*16)
       int which = u / (TC * 16);            // 0: q, 1: k
       int t = (u / 16) % TC, e0 = (u % 16) * 4;
       qk[r] = Vec4<TIn>::zero();
@@ -61,16 +70,16 @@ struct FwdStager {
     }
 #pragma unroll
     for (int r = 0; r < kV; ++r) {
-      int u = tid + r * kThreads;           // [0, TC*NW*4)
-      int t = u / (NW * 4), h = (u / 4) % NW, c4 = u % 4;
+      int u = tid + r * NT;                 // [0, TC*HPW*4)
+      int t = u / (HPW * 4), h = (u / 4) % HPW, c4 = u % 4;
       vv[r] = Vec4<TIn>::zero();
-      if (u < TC * NW * 4 && t0 + t < a.T && n0 + h < a.N)
+      if (u < TC * HPW * 4 && t0 + t < a.T && n0 + h < a.N)
         vv[r] = Vec4<TIn>::load((const TIn*)a.v + (((size_t)b * a.T + t0 + t) * a.N + n0 + h) * 16 + 4 * c4);
     }
     ff = 1.0f;
     {
-      int t = tid / NW, h = tid % NW;
-      if (tid < TC * NW && t0 + t < a.T && n0 + h < a.N)
+      int t = tid / HPW, h = tid % HPW;
+      if (tid < TC * HPW && t0 + t < a.T && n0 + h < a.N)
         ff = to_f32(((const TIn*)a.f)[((size_t)b * a.T + t0 + t) * a.N + n0 + h]);
     }
   }
@@ -79,68 +88,83 @@ struct FwdStager {
     float* K_s = buf;
     float* Q_s = buf + TC * 64;
     float* V_s = buf + 2 * TC * 64;
-    float* F_s = V_s + TC * NW * 16;
+    float* F_s = V_s + TC * HPW * 16;
 #pragma unroll
     for (int r = 0; r < kQK; ++r) {
-      int u = tid + r * kThreads;
+      int u = tid + r * NT;
       if (u < 2 * TC * 16) {
         int which = u / (TC * 16);
         int t = (u / 16) % TC, e0 = (u % 16) * 4;
         f4 x = Vec4<TIn>::to_f4(qk[r]);
         // element e = 16 j + m goes to [t][m][j]: a lane with column m reads
-        // its four tiles' values as one 16-byte word.
+        // its tiles' values as one contiguous word.
         float* dst = (which ? K_s : Q_s) + t * 64;
-        float s = which ? kScale : kInvScale;
+        float sc = which ? kScale : kInvScale;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           int e = e0 + i;
-          dst[(e % 16) * 4 + e / 16] = x[i] * s;
+          dst[(e % 16) * 4 + e / 16] = x[i] * sc;
         }
       }
     }
 #pragma unroll
     for (int r = 0; r < kV; ++r) {
-      int u = tid + r * kThreads;
-      if (u < TC * NW * 4) *(f4*)(V_s + u * 4) = Vec4<TIn>::to_f4(vv[r]);
+      int u = tid + r * NT;
+      if (u < TC * HPW * 4) *(f4*)(V_s + u * 4) = Vec4<TIn>::to_f4(vv[r]);
     }
-    if (tid < TC * NW) {
-      float g = 1.0f - ff;
-      *(f4*)(F_s + tid * 4) = f4{ff, kScale * g, -2.0f * kScale * g, 0.0f};
+    if (tid < TC * HPW) {
+      float gg = 1.0f - ff;
+      *(f4*)(F_s + tid * 4) = f4{ff, kScale * gg, -2.0f * kScale * gg, 0.0f};
     }
   }
 };
 
-template <typename TIn, int NW, int TC>
-__global__ __launch_bounds__(64 * NW) void m2rnn_fwd_kernel(FwdArgs a) {
-  typedef FwdSmem<NW, TC> Sm;
+// The TPW per-tile values a lane needs (k or q at rows 16 j + m of its tiles).
+template <int TPW> struct TileVals { float v[TPW]; };
+template <int TPW> __device__ __forceinline__ TileVals<TPW> load_tiles(const float* p) {
+  TileVals<TPW> r;
+  if constexpr (TPW == 4) {
+    f4 x = *(const f4*)p;
+    r.v[0] = x[0]; r.v[1] = x[1]; r.v[2] = x[2]; r.v[3] = x[3];
+  } else if constexpr (TPW == 2) {
+    f2 x = *(const f2*)p;
+    r.v[0] = x[0]; r.v[1] = x[1];
+  } else {
+    r.v[0] = *p;
+  }
+  return r;
+}
+
+template <typename TIn, int HPW, int TPW, int TC>
+__global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
+  typedef FwdCfg<HPW, TPW, TC> Cfg;
+  constexpr int WPH = Cfg::WPH;
   extern __shared__ float smem[];
-  float* ystage = smem + 2 * Sm::kBuf;
+  float* ystage = smem + 2 * Cfg::kBuf;
+  float* wr_s = ystage + Cfg::kY;
 
   const int tid = threadIdx.x;
   const int w = tid / 64, lane = tid % 64, g = lane / 16, m = lane % 16;
-  const int ngroups = (a.N + NW - 1) / NW;
+  const int hw = w / WPH, ts = w % WPH, j0 = ts * TPW;   // head in group, tile set, first tile
+  const int ngroups = (a.N + HPW - 1) / HPW;
   const int b = blockIdx.x / ngroups;
-  const int n0 = (blockIdx.x % ngroups) * NW;
-  const int n = n0 + w;
+  const int n0 = (blockIdx.x % ngroups) * HPW;
+  const int n = n0 + hw;
   const bool live = n < a.N;
 
-  // Resident W^T operand.  bf16 inputs: slot s of lane group g multiplies
-  // state row v = 4g + (s & 3) (hi half in slots 0..3, lo half in 4..7).
-  // fp32 inputs: instruction r of the four 16x16x4 MFMAs multiplies row 4g + r.
   WOperand<TIn> Aw;
   Aw.load(live ? (const TIn*)a.W + (size_t)n * 256 : nullptr, g, m);
-  f4 wr4 = {0.f, 0.f, 0.f, 0.f};
-  if (live) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) wr4[i] = to_f32(((const TIn*)a.wr)[(size_t)n * 16 + 4 * g + i]);
+  if (tid < HPW * 16) {
+    const int hh = tid / 16;
+    wr_s[tid] = n0 + hh < a.N ? to_f32(((const TIn*)a.wr)[(size_t)(n0 + hh) * 16 + tid % 16]) : 0.0f;
   }
 
-  f4 P[4];
+  f4 P[TPW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) P[j] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < TPW; ++j) P[j] = f4{0.f, 0.f, 0.f, 0.f};
 
   const int nchunks = (a.T + TC - 1) / TC;
-  FwdStager<TIn, NW, TC> st;
+  FwdStager<TIn, HPW, Cfg::NT, TC> st;
   st.load(a, b, n0, 0, tid);
   st.store(smem, tid);
   __syncthreads();
@@ -151,11 +175,11 @@ __global__ __launch_bounds__(64 * NW) void m2rnn_fwd_kernel(FwdArgs a) {
     const bool more = c + 1 < nchunks;
     if (more) st.load(a, b, n0, t0 + TC, tid);
 
-    const float* buf = smem + (c & 1) * Sm::kBuf;
+    const float* buf = smem + (c & 1) * Cfg::kBuf;
     const float* K_s = buf;
     const float* Q_s = buf + TC * 64;
     const float* V_s = buf + 2 * TC * 64;
-    const float* F_s = V_s + TC * NW * 16;
+    const float* F_s = V_s + TC * HPW * 16;
     const int steps = min(TC, a.T - t0);
     if (live) {
       for (int tt = 0; tt < steps; ++tt) {
@@ -164,67 +188,99 @@ __global__ __launch_bounds__(64 * NW) void m2rnn_fwd_kernel(FwdArgs a) {
           float* dst = a.H_ckpt + (((size_t)b * a.N + n) * a.nck + t / a.ckpt_every) * 1024;
           next_ck += a.ckpt_every;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) *(f4*)(dst + (16 * j + m) * 16 + 4 * g) = P[j] * kInvScale;
+          for (int j = 0; j < TPW; ++j) *(f4*)(dst + (16 * (j0 + j) + m) * 16 + 4 * g) = P[j] * kInvScale;
         }
-        const f4 kq = *(const f4*)(K_s + tt * 64 + m * 4);   // c k[16j+m]
-        const f4 qq = *(const f4*)(Q_s + tt * 64 + m * 4);   // q[16j+m] / c
-        const f4 vv = *(const f4*)(V_s + (tt * NW + w) * 16 + 4 * g);
-        const f4 fc = *(const f4*)(F_s + (tt * NW + w) * 4); // f, c(1-f), -2c(1-f)
-        f4 p = {0.f, 0.f, 0.f, 0.f};
+        const TileVals<TPW> kq = load_tiles<TPW>(K_s + tt * 64 + m * 4 + j0);   // c k[16j+m]
+        const TileVals<TPW> qq = load_tiles<TPW>(Q_s + tt * 64 + m * 4 + j0);   // q[16j+m] / c
+        const f4 vv = *(const f4*)(V_s + (tt * HPW + hw) * 16 + 4 * g);
+        const f4 fc = *(const f4*)(F_s + (tt * HPW + hw) * 4);                 // f, c(1-f), -2c(1-f)
+        // The tiles' elements are independent once the contractions are
+        // issued; the stages below are written element-wide so that the
+        // transcendental latencies overlap.
+        f4 x[TPW], hg[TPW];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const f4 D = Aw.times_state(P[j]);                     // c (H W)^T tile
+        for (int j = 0; j < TPW; ++j) x[j] = Aw.times_state(P[j]);   // c (H W)^T tile
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float x = fmaf(kq[j], vv[i], D[i]);             // c * (H W + k v^T)
-            const float r = __builtin_amdgcn_rcpf(__builtin_amdgcn_exp2f(x) + 1.0f);  // (1 - tanh)/2
-            const float h = fmaf(fc[0], P[j][i], fc[1]);          // f P + c (1 - f)
-            P[j][i] = fmaf(fc[2], r, h);                          // f P + c (1 - f) tanh
-            p[i] = fmaf(P[j][i], qq[j], p[i]);
+            x[j][i] = fmaf(kq.v[j], vv[i], x[j][i]);                // c (H W + k v^T)
+            hg[j][i] = fmaf(fc[0], P[j][i], fc[1]);                 // f P + c (1 - f)
           }
-        }
-        f4 y4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y4[i] = fmaf(wr4[i], vv[i], row_sum16(p[i]));
-        if (m == 0) *(f4*)(ystage + (tt * NW + w) * 16 + 4 * g) = y4;
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[j][i] = __builtin_amdgcn_exp2f(x[j][i]) + 1.0f;
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[j][i] = __builtin_amdgcn_rcpf(x[j][i]);  // (1 - tanh) / 2
+        f4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < TPW; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            P[j][i] = fmaf(fc[2], x[j][i], hg[j][i]);               // f P + c (1 - f) tanh
+            p[i] = fmaf(P[j][i], qq.v[j], p[i]);
+          }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[i] = row_sum16(p[i]);
+        if (m == 0) *(f4*)(ystage + ((tt * HPW + hw) * WPH + ts) * 16 + 4 * g) = p;
       }
     }
     __syncthreads();
-    // y rows of this chunk: [t][n0 .. n0+NW)[16], contiguous per t
+    // y = (sum of the per-wave partials) + w_r * v, rows [t][n0 .. n0+HPW)[16]
 #pragma unroll
-    for (int r = 0; r < (TC * NW * 4 + 64 * NW - 1) / (64 * NW); ++r) {
-      int u = tid + r * 64 * NW;
-      int tt = u / (NW * 4), h = (u / 4) % NW, c4 = u % 4;
-      if (u < TC * NW * 4 && tt < steps && n0 + h < a.N)
-        *(f4*)(a.y + (((size_t)b * a.T + t0 + tt) * a.N + n0 + h) * 16 + 4 * c4) = *(const f4*)(ystage + u * 4);
+    for (int r = 0; r < (TC * HPW * 4 + Cfg::NT - 1) / Cfg::NT; ++r) {
+      const int u = tid + r * Cfg::NT;
+      const int tt = u / (HPW * 4), hh = (u / 4) % HPW, c4 = u % 4;
+      if (u < TC * HPW * 4 && tt < steps && n0 + hh < a.N) {
+        f4 acc = *(const f4*)(ystage + ((tt * HPW + hh) * WPH) * 16 + 4 * c4);
+#pragma unroll
+        for (int ws = 1; ws < WPH; ++ws) acc += *(const f4*)(ystage + ((tt * HPW + hh) * WPH + ws) * 16 + 4 * c4);
+        const f4 vres = *(const f4*)(V_s + (tt * HPW + hh) * 16 + 4 * c4);
+        const f4 wres = *(const f4*)(wr_s + hh * 16 + 4 * c4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(wres[i], vres[i], acc[i]);
+        *(f4*)(a.y + (((size_t)b * a.T + t0 + tt) * a.N + n0 + hh) * 16 + 4 * c4) = acc;
+      }
     }
-    if (more) st.store(smem + ((c + 1) & 1) * Sm::kBuf, tid);
+    if (more) st.store(smem + ((c + 1) & 1) * Cfg::kBuf, tid);
     __syncthreads();
   }
 
   if (live) {
     float* dst = a.H_T + ((size_t)b * a.N + n) * 1024;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) *(f4*)(dst + (16 * j + m) * 16 + 4 * g) = P[j] * kInvScale;
+    for (int j = 0; j < TPW; ++j) *(f4*)(dst + (16 * (j0 + j) + m) * 16 + 4 * g) = P[j] * kInvScale;
   }
 }
 
-template <typename TIn, int NW>
+template <typename TIn, int HPW, int TPW, int TC>
 static hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  constexpr int TC = 32;
-  typedef FwdSmem<NW, TC> Sm;
-  static_assert(Sm::kBytes <= 64 * 1024, "forward LDS budget");
-  const int ngroups = (a.N + NW - 1) / NW;
-  dim3 grid((unsigned)(a.B * ngroups)), block(64 * NW);
-  hipLaunchKernelGGL((m2rnn_fwd_kernel<TIn, NW, TC>), grid, block, Sm::kBytes, stream, a);
+  typedef FwdCfg<HPW, TPW, TC> Cfg;
+  static_assert(Cfg::kBytes <= 64 * 1024, "forward LDS budget");
+  const int ngroups = (a.N + HPW - 1) / HPW;
+  dim3 grid((unsigned)(a.B * ngroups)), block(Cfg::NT);
+  hipLaunchKernelGGL((m2rnn_fwd_kernel<TIn, HPW, TPW, TC>), grid, block, Cfg::kBytes, stream, a);
   return hipGetLastError();
+}
+
+// Tiles per wave: four (one head per wave) by default; the M2RNN_FWD_TPW
+// environment variable (1, 2 or 4) overrides it for tuning.
+static int fwd_tiles_per_wave() {
+  const char* e = getenv("M2RNN_FWD_TPW");
+  int v = e ? atoi(e) : 4;
+  return (v == 1 || v == 2) ? v : 4;
 }
 
 template <typename TIn>
 static hipError_t dispatch_fwd(const FwdArgs& a, hipStream_t stream) {
-  if (a.N >= 4) return launch_fwd<TIn, 4>(a, stream);
-  if (a.N >= 2) return launch_fwd<TIn, 2>(a, stream);
-  return launch_fwd<TIn, 1>(a, stream);
+  switch (fwd_tiles_per_wave()) {
+    case 4: return launch_fwd<TIn, 4, 4, 32>(a, stream);
+    case 2: return launch_fwd<TIn, 4, 2, 16>(a, stream);
+    default: return launch_fwd<TIn, 4, 1, 16>(a, stream);
+  }
 }
 
 __global__ void fill_zero_kernel(float* p, size_t n) {
