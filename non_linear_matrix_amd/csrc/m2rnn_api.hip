@@ -87,8 +87,10 @@ extern "C" int m2rnn_forward(int B, int T, int N, int K, int V, int dtype,
 }
 
 extern "C" size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckpt_every) {
-  (void)B; (void)T; (void)N; (void)K; (void)V; (void)ckpt_every;
-  return 0;
+  if (B <= 0 || T <= 0 || N <= 0 || K != 64 || V != 16 || ckpt_every < 1) return 0;
+  size_t o1, o2, o3, o4;
+  int ng;
+  return sizeof(float) * m2rnn::backward_workspace_floats(B, T, N, ckpt_every, &o1, &o2, &o3, &o4, &ng);
 }
 
 extern "C" int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
@@ -97,11 +99,59 @@ extern "C" int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
                               const float* dy, const float* dH_T, float* dq, float* dk, float* dv,
                               float* df, float* dW, float* dw_r, void* workspace,
                               size_t workspace_bytes, void* stream) {
-  (void)q; (void)k; (void)v; (void)f; (void)W; (void)w_r; (void)H_ckpt; (void)ckpt_every;
-  (void)dy; (void)dH_T; (void)dq; (void)dk; (void)dv; (void)df; (void)dW; (void)dw_r;
-  (void)workspace; (void)workspace_bytes; (void)stream;
   g_err[0] = 0;
   int st = check_sizes(B, T, N, K, V, dtype);
   if (st) return st;
-  return fail(M2RNN_ERR_UNSUPPORTED, "backward not built yet");
+  if (ckpt_every < 1) return fail(M2RNN_ERR_INVALID_ARG, "ckpt_every must be >= 1 for the backward");
+  const size_t es = dtype == M2RNN_F32 ? 4 : 2;
+  const long long BT = (long long)B * T, BTN = BT * N, BN = (long long)B * N;
+  const int nck = T > 0 ? (T + ckpt_every - 1) / ckpt_every : 0;
+  if ((st = need(q, "q", BT * K * (N > 0), 16)) || (st = need(k, "k", BT * K * (N > 0), 16)) ||
+      (st = need(v, "v", BTN * V, 16)) || (st = need(f, "f", BTN, es)) || (st = need(W, "W", (long long)N * V * V, es)) ||
+      (st = need(w_r, "w_r", (long long)N * V, es)) || (st = need(H_ckpt, "H_ckpt", BN * nck * K * V, 16)) ||
+      (st = need(dy, "dy", BTN * V, 16)) || (st = need(dq, "dq", BT * K, 16)) || (st = need(dk, "dk", BT * K, 16)) ||
+      (st = need(dv, "dv", BTN * V, 16)) || (st = need(df, "df", BTN, 4)) || (st = need(dW, "dW", (long long)N * V * V, 16)) ||
+      (st = need(dw_r, "dw_r", (long long)N * V, 16)))
+    return st;
+  if (dH_T && !aligned(dH_T, 16)) return fail(M2RNN_ERR_INVALID_ARG, "dH_T must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (BTN == 0) {
+    // nothing flows back: dq, dk (if any) and the summed dW, dw_r are zero
+    hipError_t e = hipSuccess;
+    if (BT > 0) {
+      if (e == hipSuccess) e = m2rnn::launch_fill_zero(dq, (size_t)BT * K, s);
+      if (e == hipSuccess) e = m2rnn::launch_fill_zero(dk, (size_t)BT * K, s);
+    }
+    if (N > 0) {
+      if (e == hipSuccess) e = m2rnn::launch_fill_zero(dW, (size_t)N * V * V, s);
+      if (e == hipSuccess) e = m2rnn::launch_fill_zero(dw_r, (size_t)N * V, s);
+    }
+    return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "zero fill: %s", hipGetErrorString(e));
+  }
+  size_t o_dense, o_dqk, o_dW, o_dwr;
+  int ng;
+  const size_t need_bytes = sizeof(float) * m2rnn::backward_workspace_floats(B, T, N, ckpt_every, &o_dense, &o_dqk,
+                                                                              &o_dW, &o_dwr, &ng);
+  if (!workspace || workspace_bytes < need_bytes)
+    return fail(M2RNN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 256)) return fail(M2RNN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+  float* ws = (float*)workspace;
+  m2rnn::BwdArgs a;
+  a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.wr = w_r;
+  a.H_ckpt = H_ckpt; a.dy = dy; a.dH_T = dH_T;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.df = df; a.dW = dW; a.dw_r = dw_r;
+  a.ws_dqk = ws + o_dqk; a.ws_dW = ws + o_dW; a.ws_dwr = ws + o_dwr;
+  a.B = B; a.T = T; a.N = N;
+  a.ckpt_every = ckpt_every; a.nck = nck; a.ngroups = ng;
+  // replay of the caller's checkpoint chunks into states every sub-step count
+  const int L = m2rnn::backward_sub_steps();
+  m2rnn::FwdArgs rp;
+  rp.q = q; rp.k = k; rp.v = v; rp.f = f; rp.W = W; rp.wr = w_r;
+  rp.y = nullptr; rp.H_T = nullptr; rp.H_ckpt = ws + o_dense;
+  rp.B = B; rp.T = T; rp.N = N; rp.ckpt_every = L; rp.nck = (T + L - 1) / L;
+  rp.H_src = H_ckpt; rp.src_every = ckpt_every; rp.src_nck = nck;
+  hipError_t e = m2rnn::launch_backward(a, rp, dtype, s);
+  if (e != hipSuccess) return fail(M2RNN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+  return M2RNN_OK;
 }

@@ -56,14 +56,14 @@ struct FwdStager {
   raw vv[kV];
   float ff;
 
-  __device__ void load(const FwdArgs& a, int b, int n0, int t0, int tid) {
+  __device__ void load(const FwdArgs& a, int b, int n0, int t0, int t_end, int tid) {
 #pragma unroll
     for (int r = 0; r < kQK; ++r) {
       int u = tid + r * NT;                 // [0, 2*TC*16)
       int which = u / (TC * 16);            // 0: q, 1: k
       int t = (u / 16) % TC, e0 = (u % 16) * 4;
       qk[r] = Vec4<TIn>::zero();
-      if (u < 2 * TC * 16 && t0 + t < a.T) {
+      if (u < 2 * TC * 16 && t0 + t < t_end) {
         const TIn* src = (const TIn*)(which ? a.k : a.q);
         qk[r] = Vec4<TIn>::load(src + ((size_t)b * a.T + t0 + t) * 64 + e0);
       }
@@ -73,13 +73,13 @@ struct FwdStager {
       int u = tid + r * NT;                 // [0, TC*HPW*4)
       int t = u / (HPW * 4), h = (u / 4) % HPW, c4 = u % 4;
       vv[r] = Vec4<TIn>::zero();
-      if (u < TC * HPW * 4 && t0 + t < a.T && n0 + h < a.N)
+      if (u < TC * HPW * 4 && t0 + t < t_end && n0 + h < a.N)
         vv[r] = Vec4<TIn>::load((const TIn*)a.v + (((size_t)b * a.T + t0 + t) * a.N + n0 + h) * 16 + 4 * c4);
     }
     ff = 1.0f;
     {
       int t = tid / HPW, h = tid % HPW;
-      if (tid < TC * HPW && t0 + t < a.T && n0 + h < a.N)
+      if (tid < TC * HPW && t0 + t < t_end && n0 + h < a.N)
         ff = to_f32(((const TIn*)a.f)[((size_t)b * a.T + t0 + t) * a.N + n0 + h]);
     }
   }
@@ -135,7 +135,12 @@ template <int TPW> __device__ __forceinline__ TileVals<TPW> load_tiles(const flo
   return r;
 }
 
-template <typename TIn, int HPW, int TPW, int TC>
+// DENSE = false: the forward scan proper (y, H_T, optional checkpoints).
+// DENSE = true: the backward's replay.  Every workgroup takes one checkpoint
+// chunk [c * src_every, (c+1) * src_every) of HPW heads, restarts from the
+// stored H there and writes H every ckpt_every steps (no readout), so all
+// chunks of a sequence run in parallel.
+template <typename TIn, int HPW, int TPW, int TC, bool DENSE>
 __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
   typedef FwdCfg<HPW, TPW, TC> Cfg;
   constexpr int WPH = Cfg::WPH;
@@ -144,11 +149,21 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
   float* wr_s = ystage + Cfg::kY;
 
   const int tid = threadIdx.x;
-  const int w = tid / 64, lane = tid % 64, g = lane / 16, m = lane % 16;
+  const int w = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int lane = tid % 64, g = lane / 16, m = lane % 16;
   const int hw = w / WPH, ts = w % WPH, j0 = ts * TPW;   // head in group, tile set, first tile
   const int ngroups = (a.N + HPW - 1) / HPW;
-  const int b = blockIdx.x / ngroups;
-  const int n0 = (blockIdx.x % ngroups) * HPW;
+  int blk = blockIdx.x;
+  const int n0 = (blk % ngroups) * HPW;
+  blk /= ngroups;
+  int tb = 0, te = a.T;
+  if constexpr (DENSE) {
+    const int chunk = blk % a.src_nck;
+    blk /= a.src_nck;
+    tb = chunk * a.src_every;
+    te = min(a.T, tb + a.src_every);
+  }
+  const int b = blk;
   const int n = n0 + hw;
   const bool live = n < a.N;
 
@@ -162,25 +177,33 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
   f4 P[TPW];
 #pragma unroll
   for (int j = 0; j < TPW; ++j) P[j] = f4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (DENSE) {
+    if (live) {
+      const float* src = a.H_src + (((size_t)b * a.N + n) * a.src_nck + tb / a.src_every) * 1024;
+#pragma unroll
+      for (int j = 0; j < TPW; ++j) P[j] = *(const f4*)(src + (16 * (j0 + j) + m) * 16 + 4 * g) * kScale;
+    }
+  }
 
-  const int nchunks = (a.T + TC - 1) / TC;
+  const int nchunks = (te - tb + TC - 1) / TC;
   FwdStager<TIn, HPW, Cfg::NT, TC> st;
-  st.load(a, b, n0, 0, tid);
+  st.load(a, b, n0, tb, te, tid);
   st.store(smem, tid);
   __syncthreads();
 
-  int next_ck = a.H_ckpt ? 0 : a.T;  // next step whose incoming state is checkpointed
+  // next step whose incoming state is checkpointed
+  int next_ck = a.H_ckpt ? (tb + a.ckpt_every - 1) / a.ckpt_every * a.ckpt_every : a.T;
   for (int c = 0; c < nchunks; ++c) {
-    const int t0 = c * TC;
+    const int t0 = tb + c * TC;
     const bool more = c + 1 < nchunks;
-    if (more) st.load(a, b, n0, t0 + TC, tid);
+    if (more) st.load(a, b, n0, t0 + TC, te, tid);
 
     const float* buf = smem + (c & 1) * Cfg::kBuf;
     const float* K_s = buf;
     const float* Q_s = buf + TC * 64;
     const float* V_s = buf + 2 * TC * 64;
     const float* F_s = V_s + TC * HPW * 16;
-    const int steps = min(TC, a.T - t0);
+    const int steps = min(TC, te - t0);
     if (live) {
       for (int tt = 0; tt < steps; ++tt) {
         const int t = t0 + tt;
@@ -223,15 +246,17 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
             P[j][i] = fmaf(fc[2], x[j][i], hg[j][i]);               // f P + c (1 - f) tanh
             p[i] = fmaf(P[j][i], qq.v[j], p[i]);
           }
+        if constexpr (!DENSE) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p[i] = row_sum16(p[i]);
-        if (m == 0) *(f4*)(ystage + ((tt * HPW + hw) * WPH + ts) * 16 + 4 * g) = p;
+          for (int i = 0; i < 4; ++i) p[i] = row_sum16(p[i]);
+          if (m == 0) *(f4*)(ystage + ((tt * HPW + hw) * WPH + ts) * 16 + 4 * g) = p;
+        }
       }
     }
     __syncthreads();
     // y = (sum of the per-wave partials) + w_r * v, rows [t][n0 .. n0+HPW)[16]
 #pragma unroll
-    for (int r = 0; r < (TC * HPW * 4 + Cfg::NT - 1) / Cfg::NT; ++r) {
+    for (int r = 0; r < (DENSE ? 0 : (TC * HPW * 4 + Cfg::NT - 1) / Cfg::NT); ++r) {
       const int u = tid + r * Cfg::NT;
       const int tt = u / (HPW * 4), hh = (u / 4) % HPW, c4 = u % 4;
       if (u < TC * HPW * 4 && tt < steps && n0 + hh < a.N) {
@@ -249,20 +274,20 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
     __syncthreads();
   }
 
-  if (live) {
+  if (live && !DENSE) {
     float* dst = a.H_T + ((size_t)b * a.N + n) * 1024;
 #pragma unroll
     for (int j = 0; j < TPW; ++j) *(f4*)(dst + (16 * (j0 + j) + m) * 16 + 4 * g) = P[j] * kInvScale;
   }
 }
 
-template <typename TIn, int HPW, int TPW, int TC>
+template <typename TIn, int HPW, int TPW, int TC, bool DENSE = false>
 static hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   typedef FwdCfg<HPW, TPW, TC> Cfg;
   static_assert(Cfg::kBytes <= 64 * 1024, "forward LDS budget");
   const int ngroups = (a.N + HPW - 1) / HPW;
-  dim3 grid((unsigned)(a.B * ngroups)), block(Cfg::NT);
-  hipLaunchKernelGGL((m2rnn_fwd_kernel<TIn, HPW, TPW, TC>), grid, block, Cfg::kBytes, stream, a);
+  dim3 grid((unsigned)(a.B * ngroups * (DENSE ? a.src_nck : 1))), block(Cfg::NT);
+  hipLaunchKernelGGL((m2rnn_fwd_kernel<TIn, HPW, TPW, TC, DENSE>), grid, block, Cfg::kBytes, stream, a);
   return hipGetLastError();
 }
 
@@ -297,6 +322,10 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream) {
 
 hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t stream) {
   return dtype == 0 ? dispatch_fwd<float>(a, stream) : dispatch_fwd<bf16_t>(a, stream);
+}
+
+hipError_t launch_densify(const FwdArgs& a, int dtype, hipStream_t stream) {
+  return dtype == 0 ? launch_fwd<float, 4, 4, 32, true>(a, stream) : launch_fwd<bf16_t, 4, 4, 32, true>(a, stream);
 }
 
 }  // namespace m2rnn

@@ -12,9 +12,33 @@ struct FwdArgs {
   int B, T, N;
   int ckpt_every;  // > 0 when H_ckpt != nullptr
   int nck;         // ceil(T / ckpt_every)
+  // replay from stored states (backward): checkpoints H_src every src_every steps
+  const float* H_src = nullptr;
+  int src_every = 0, src_nck = 0;
 };
 
 hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t stream);
+// Replay every checkpoint chunk of H_src in parallel, writing H every
+// ckpt_every steps into H_ckpt (no y, no H_T).
+hipError_t launch_densify(const FwdArgs& a, int dtype, hipStream_t stream);
+
+struct BwdArgs {
+  const void *q, *k, *v, *f, *W, *wr;
+  const float *H_ckpt, *dy, *dH_T;  // H_ckpt: states every ckpt_every (<= sub-step count) steps
+  float *dq, *dk, *dv, *df, *dW, *dw_r;
+  float *ws_dqk, *ws_dW, *ws_dwr;   // workspace regions
+  int B, T, N;
+  int ckpt_every, nck, ngroups;
+};
+
+// Workspace layout (in floats) for the backward; returns the total.
+size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* off_dense, size_t* off_dqk,
+                                 size_t* off_dW, size_t* off_dwr, int* ngroups);
+// Steps between the states the reverse sweep restarts from.
+int backward_sub_steps();
+// When a.ckpt_every exceeds the sub-step count, `replay` (a densify launch
+// from the caller's checkpoints into the workspace) runs first.
+hipError_t launch_backward(const BwdArgs& a, const FwdArgs& replay, int dtype, hipStream_t stream);
 
 // Zero `n` floats with a plain fill kernel (graph-capture friendly).
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
