@@ -46,14 +46,18 @@ template <int HPW>
 struct BwdCfg {
   static constexpr int NWAVES = HPW * 4;
   static constexpr int NT = 64 * NWAVES;
-  // per staged step: K_s[64] (c k), Q_s[64] (q), V_s[HPW][16], F_s[HPW][4], U_s[HPW][16]
-  static constexpr int kStep = 128 + HPW * 36;
+  // per staged step: K_s[64] (c k), Q_s[64] (q), V_s[HPW][16], F_s[HPW][4],
+  // U_s[HPW][16], Kp_s[64] (c k permuted: [tile][g][r] = row 16 tile + 4 r + g)
+  static constexpr int kStep = 192 + HPW * 36;
   static constexpr int kBuf = kSub * kStep;
-  static constexpr int kXpose = NWAVES * 512;          // per wave: H_{t-1} tile, D tile
-  static constexpr int kDf = kSub * HPW * 4;           // [s][h][tile]
-  static constexpr int kDv = kSub * HPW * 4 * 16;      // [s][h][tile][16]
-  static constexpr int kDqk = kSub * HPW * 2 * 64;     // [s][h][dq|dk][64]
-  static constexpr int kFloats = 2 * kBuf + kXpose + kDf + kDv + kDqk;
+  // per wave, two slots of {H_{t-1} tile, D tile}; a tile is stored as
+  // [v / 4][kk][v % 4] with an 80-float stride between the v / 4 blocks so that
+  // both the 16-byte writes and the operand-layout reads are bank-conflict free
+  static constexpr int kTile = 4 * 80;
+  static constexpr int kXpose = NWAVES * 4 * kTile;
+  // per-lane partials of one sub-chunk, reduced in the pass: [s][h][tile][lane]
+  static constexpr int kPart = kSub * HPW * 4 * 64;
+  static constexpr int kFloats = 2 * kBuf + kXpose + 4 * kPart;
   static constexpr int kBytes = kFloats * 4;
 };
 
@@ -106,6 +110,7 @@ struct BwdStager {
     float* V_s = Q_s + kSub * 64;
     float* F_s = V_s + kSub * HPW * 16;
     float* U_s = F_s + kSub * HPW * 4;
+    float* Kp_s = U_s + kSub * HPW * 16;
 #pragma unroll
     for (int r = 0; r < kQK; ++r) {
       int u = tid + r * NT;
@@ -115,6 +120,14 @@ struct BwdStager {
         f4 x = Vec4<TIn>::to_f4(qk[r]);
         if (which) x *= kScale;
         *(f4*)((which ? K_s : Q_s) + t * 64 + e0) = x;
+        if (which) {
+          // row e = 16 tile + 4 r + g goes to [tile][g][r]
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = e0 + i;
+            Kp_s[t * 64 + (e / 16) * 16 + (e % 4) * 4 + (e % 16) / 4] = x[i];
+          }
+        }
       }
     }
 #pragma unroll
@@ -161,15 +174,41 @@ template <> struct WBackOperand<float> {
   }
 };
 
-__device__ __forceinline__ float sum_lane_groups(float x) {  // over lanes m, m+16, m+32, m+48
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+// Sum over the four lanes m, m+16, m+32, m+48 (every lane gets the sum).
+// v_permlane16_swap(x, x) returns x of the even and of the odd row of each
+// row pair; v_permlane32_swap(x, x) returns x of the lower and upper half.
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float s = __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
+  const uint32_t v = __builtin_bit_cast(uint32_t, s);
+  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return __builtin_bit_cast(float, (uint32_t)q[0]) + __builtin_bit_cast(float, (uint32_t)q[1]);
 }
 
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
+// dW[v][v'] += sum over 16 rows kk of A[kk][v] B[kk][v'], with lane (g, m)
+// holding A, B at rows 4r + g (r = 0..3) and column m.  fp32 inputs: four
+// exact v_mfma_f32_16x16x4_f32.  bf16 inputs: hi/lo bf16 halves,
+// A_hi B_hi + A_lo B_hi in one 16x16x32 and A_hi B_lo in one 16x16x16 MFMA.
+template <typename TIn>
+__device__ __forceinline__ f4 dw_update(f4 a, f4 b, f4 acc) {
+  if constexpr (sizeof(TIn) == 4) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], acc, 0, 0, 0);
+    return acc;
+  } else {
+    uint32_t ah01, al01, ah23, al23, bh01, bl01, bh23, bl23;
+    split2(a[0], a[1], ah01, al01);
+    split2(a[2], a[3], ah23, al23);
+    split2(b[0], b[1], bh01, bl01);
+    split2(b[2], b[3], bh23, bl23);
+    acc = mfma_bf16(__builtin_bit_cast(bf16x8, (u32x4{ah01, ah23, al01, al23})),
+                    __builtin_bit_cast(bf16x8, (u32x4{bh01, bh23, bh01, bh23})), acc);
+    typedef short s4 __attribute__((ext_vector_type(4)));
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, (u32x2{ah01, ah23})),
+                                                     __builtin_bit_cast(s4, (u32x2{bl01, bl23})), acc, 0, 0, 0);
+  }
 }
 
 // One forward step of one tile (no readout): returns r = (1 - tanh)/2 and
@@ -196,9 +235,10 @@ __global__ __launch_bounds__(256 * HPW) void m2rnn_bwd_kernel(BwdArgs a) {
   constexpr int NT = Cfg::NT;
   extern __shared__ float smem[];
   float* xpose = smem + 2 * Cfg::kBuf;
-  float* dfbuf = xpose + Cfg::kXpose;
-  float* dvbuf = dfbuf + Cfg::kDf;
-  float* dqkbuf = dvbuf + Cfg::kDv;
+  float* dfbuf = xpose + Cfg::kXpose;   // per-lane partials, [s][h][tile][lane]
+  float* dvbuf = dfbuf + Cfg::kPart;
+  float* dqbuf = dvbuf + Cfg::kPart;
+  float* dkbuf = dqbuf + Cfg::kPart;
 
   const int tid = threadIdx.x;
   // wave-uniform indices live in scalar registers
@@ -212,7 +252,7 @@ __global__ __launch_bounds__(256 * HPW) void m2rnn_bwd_kernel(BwdArgs a) {
   const int n = n0 + hw;
   const bool live = n < a.N;
   const int kk = 16 * j + m;                      // this lane's state row
-  float* xp = xpose + w * 512;
+  float* xp = xpose + w * 4 * Cfg::kTile;
   const size_t head = (size_t)b * a.N + n;
   // stored states H at t = s * L (s = 0 .. ns-1), L = a.ckpt_every <= kSub
   const int L = a.ckpt_every, ns = a.nck;
@@ -227,7 +267,7 @@ __global__ __launch_bounds__(256 * HPW) void m2rnn_bwd_kernel(BwdArgs a) {
   f4 C = {0.f, 0.f, 0.f, 0.f};
   if (live && a.dH_T) C = *(const f4*)(a.dH_T + head * 1024 + kk * 16 + 4 * g);
   f4 dW = {0.f, 0.f, 0.f, 0.f};   // lane (g, m), register i: c * dW[4g + i][m] partial
-  f4 dwr = {0.f, 0.f, 0.f, 0.f};
+  float dwr = 0.f;                 // thread tid < HPW * 16: dw_r[n0 + tid / 16][tid % 16] partial
 
   BwdStager<TIn, HPW, NT> st;
   {
@@ -253,13 +293,18 @@ __global__ __launch_bounds__(256 * HPW) void m2rnn_bwd_kernel(BwdArgs a) {
     const float* V_s = Q_s + kSub * 64;
     const float* F_s = V_s + kSub * HPW * 16;
     const float* U_s = F_s + kSub * HPW * 4;
+    const float* Kp_s = U_s + kSub * HPW * 16;     // c k permuted, [s][tile][g][r]
+    const int part = w * 64 + lane;                // this lane's slot in a partials row
 
     if (live) {
       // replay the sub-chunk keeping H_{t-1} and Z_t on chip
       f4 Pp[kSub], Z[kSub];
 #pragma unroll
+      // Steps s >= len of a short last sub-chunk are staged as f = 1 with
+      // q = k = v = u = 0: an exact identity for C and a zero contribution to
+      // every gradient, so all kSub steps run unguarded.
       for (int s = 0; s < kSub; ++s) {
-        if (s < len) {
+        {
           const f4 vv = *(const f4*)(V_s + (s * HPW + hw) * 16 + 4 * g);
           const f4 fc = *(const f4*)(F_s + (s * HPW + hw) * 4);
           const f4 uu = *(const f4*)(U_s + (s * HPW + hw) * 16 + 4 * g);
@@ -271,20 +316,37 @@ __global__ __launch_bounds__(256 * HPW) void m2rnn_bwd_kernel(BwdArgs a) {
           float dq = 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) dq = fmaf(P[i], uu[i], dq);
-          dq = sum_lane_groups(dq);
-          if (g == 0) dqkbuf[(s * HPW + hw) * 128 + kk] = dq * kInvScale;
+          dqbuf[s * Cfg::NWAVES * 64 + part] = dq;
         }
         __builtin_amdgcn_sched_barrier(0);   // keep each step's loads in its step
       }
-      // reverse sweep over the sub-chunk
+      // reverse sweep over the sub-chunk.  The dW / dv contractions over the
+      // tile's rows read H_{t-1} and D back from LDS in MFMA operand layout;
+      // they run one step behind the sweep so that the LDS round trip
+      // overlaps the next step's arithmetic (LDS requests of a wave complete
+      // in issue order, so no wait is needed between the write and the read).
+      auto drain = [&](int ps) {
+        const float* xs = xp + (ps & 1) * 2 * Cfg::kTile;
+        const f4 ckp = *(const f4*)(Kp_s + ps * 64 + j * 16 + g * 4);   // c k[16j+4r+g], r = 0..3
+        float dvp = 0.f;
+        f4 av, bv;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int at = (m / 4) * 80 + (4 * r + g) * 4 + m % 4;
+          av[r] = xs[at];                                   // c H_{t-1}[16j+4r+g][v = m]
+          bv[r] = xs[Cfg::kTile + at];                      // D[16j+4r+g][v' = m]
+          dvp = fmaf(bv[r], ckp[r], dvp);
+        }
+        dW = dw_update<TIn>(av, bv, dW);
+        dvbuf[ps * Cfg::NWAVES * 64 + part] = dvp;          // partial of dv[v' = m] over rows 4r+g
+      };
 #pragma unroll
       for (int s = kSub - 1; s >= 0; --s) {
-        if (s < len) {
+        {
           const f4 vv = *(const f4*)(V_s + (s * HPW + hw) * 16 + 4 * g);
           const f4 fc = *(const f4*)(F_s + (s * HPW + hw) * 4);   // f, c(1-f), -2c(1-f), 1-f
           const f4 uu = *(const f4*)(U_s + (s * HPW + hw) * 16 + 4 * g);
           const float qv = Q_s[s * 64 + kk];
-          const float ckv = K_s[s * 64 + kk];                      // c k[kk]
           f4 R, D, fR;
           float dfp = 0.f, dk = 0.f;
 #pragma unroll
@@ -295,65 +357,61 @@ __global__ __launch_bounds__(256 * HPW) void m2rnn_bwd_kernel(BwdArgs a) {
             dfp = fmaf(R[i], fmaf(Pp[s][i], kInvScale, -Z[s][i]), dfp);   // <R, H_{t-1} - Z>
             fR[i] = fc[0] * R[i];
             dk = fmaf(D[i], vv[i], dk);
-            dwr[i] = fmaf(uu[i], vv[i], dwr[i]);
           }
           C = Ab.apply(D, fR);                                       // C_{t-1} = f R + D W^T
-          // dk_t[kk] (this head) = sum_v' D[kk][v'] v[v']
-          dk = sum_lane_groups(dk);
-          if (g == 0) dqkbuf[(s * HPW + hw) * 128 + 64 + kk] = dk;
-          // dv_t[v'] partial over this tile's rows: sum_kk D[kk][v'] (c k[kk])
-          f4 dvp;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dvp[i] = row_sum16(D[i] * ckv);
-          if (m == 0) *(f4*)(dvbuf + ((s * HPW + hw) * 4 + j) * 16 + 4 * g) = dvp;
-          // df_t partial over this tile
-          dfp = sum_lane_groups(row_sum16(dfp));
-          if (lane == 0) dfbuf[(s * HPW + hw) * 4 + j] = dfp;
-          // dW += H_{t-1}^T D via LDS transpose + four exact fp32 MFMAs
-          *(f4*)(xp + m * 16 + 4 * g) = Pp[s];
-          *(f4*)(xp + 256 + m * 16 + 4 * g) = D;
-          wave_lds_fence();
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float av = xp[(4 * r + g) * 16 + m];        // c H_{t-1}[4r+g][v = m]
-            const float bv = xp[256 + (4 * r + g) * 16 + m];  // D[4r+g][v' = m]
-            dW = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, dW, 0, 0, 0);
-          }
-          wave_lds_fence();
+          // per-lane partials of dk_t[kk] (over v' = 4g..4g+3) and df_t
+          dkbuf[s * Cfg::NWAVES * 64 + part] = dk;
+          dfbuf[s * Cfg::NWAVES * 64 + part] = dfp;
+          // stage H_{t-1} and D of this step, finish the previous step
+          *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + g * 80 + m * 4) = Pp[s];
+          *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + Cfg::kTile + g * 80 + m * 4) = D;
+          if (s < kSub - 1) drain(s + 1);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      drain(0);
     }
     __syncthreads();
-    // df[b][t][n] = sum over the four tiles
-    if (tid < len * HPW) {
-      const int s = tid / HPW, hh = tid % HPW;
-      if (n0 + hh < a.N) {
-        const float* d4 = dfbuf + (s * HPW + hh) * 4;
-        a.df[((size_t)b * a.T + t0 + s) * a.N + n0 + hh] = (d4[0] + d4[1]) + (d4[2] + d4[3]);
-      }
+    // ---- pass: reduce this sub-chunk's per-lane partials.  Partials row
+    // [s] holds, per wave w = 4 h + tile and lane 16 g + m, the lane's share.
+    // df[b][t][n]: sum over the 4 tiles x 64 lanes of head h (one wave per (s, h))
+    for (int sh = w; sh < len * HPW; sh += Cfg::NWAVES) {
+      const int s = sh / HPW, hh = sh % HPW;
+      const float* d = dfbuf + s * Cfg::NWAVES * 64 + hh * 256 + lane;
+      float x = (d[0] + d[64]) + (d[128] + d[192]);
+      x = sum_lane_groups(row_sum16(x));
+      if (lane == 0 && n0 + hh < a.N) a.df[((size_t)b * a.T + t0 + s) * a.N + n0 + hh] = x;
     }
-    // dv[b][t][n][:] = (1/c) sum over tiles + w_r * u
-    for (int u = tid; u < len * HPW * 4; u += NT) {
-      const int s = u / (HPW * 4), hh = (u / 4) % HPW, c4 = u % 4;
+    // dv[b][t][n][v'] = (1/c) sum over tiles and g of the partial at lane 16 g + v', + w_r u
+    for (int u = tid; u < len * HPW * 16; u += NT) {
+      const int s = u / (HPW * 16), hh = (u / 16) % HPW, e = u % 16;
       if (n0 + hh < a.N) {
-        const float* d = dvbuf + ((s * HPW + hh) * 4) * 16 + 4 * c4;
-        f4 acc = (*(const f4*)d + *(const f4*)(d + 16)) + (*(const f4*)(d + 32) + *(const f4*)(d + 48));
-        const f4 uu = *(const f4*)(U_s + (s * HPW + hh) * 16 + 4 * c4);
-        const TIn* wrp = (const TIn*)a.wr + (size_t)(n0 + hh) * 16 + 4 * c4;
-        f4 out;
+        const float* d = dvbuf + s * Cfg::NWAVES * 64 + hh * 256 + e;
+        float acc = 0.f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) out[i] = fmaf(to_f32(wrp[i]), uu[i], acc[i] * kInvScale);
-        *(f4*)(a.dv + (((size_t)b * a.T + t0 + s) * a.N + n0 + hh) * 16 + 4 * c4) = out;
+        for (int q4 = 0; q4 < 16; ++q4) acc += d[q4 * 16];   // (tile, g) pairs
+        const float uu = U_s[(s * HPW + hh) * 16 + e];
+        const float wr = to_f32(((const TIn*)a.wr)[(size_t)(n0 + hh) * 16 + e]);
+        a.dv[(((size_t)b * a.T + t0 + s) * a.N + n0 + hh) * 16 + e] = fmaf(wr, uu, acc * kInvScale);
       }
     }
     // dq, dk partials of this workgroup's heads -> workspace [b][grp][t][dq|dk][64]
-    for (int u = tid; u < len * 32; u += NT) {
-      const int s = u / 32, e = (u % 32) * 4;
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int u = tid; u < len * 128; u += NT) {
+      const int s = u / 128, which = (u / 64) % 2, r = u % 64;   // row r = 16 tile + m
+      const float* src = (which ? dkbuf : dqbuf) + s * Cfg::NWAVES * 64 + (r / 16) * 64 + r % 16;
+      float acc = 0.f;
       for (int hh = 0; hh < HPW; ++hh)
-        if (n0 + hh < a.N) acc += *(const f4*)(dqkbuf + (s * HPW + hh) * 128 + e);
-      *(f4*)(a.ws_dqk + (((size_t)b * ngroups + grp) * a.T + t0 + s) * 128 + e) = acc;
+        if (n0 + hh < a.N) {
+          const float* d = src + hh * 256;
+          acc += (d[0] + d[16]) + (d[32] + d[48]);           // the four lane groups
+        }
+      a.ws_dqk[(((size_t)b * ngroups + grp) * a.T + t0 + s) * 128 + u % 128] = which ? acc : acc * kInvScale;
+    }
+    // dw_r partial: sum over the sub-chunk of u (.) v (padded steps stage u = 0)
+    if (tid < HPW * 16) {
+      const int hh = tid / 16, e = tid % 16;
+#pragma unroll
+      for (int s = 0; s < kSub; ++s) dwr = fmaf(U_s[(s * HPW + hh) * 16 + e], V_s[(s * HPW + hh) * 16 + e], dwr);
     }
     if (more) st.store(smem + ((it + 1) & 1) * Cfg::kBuf, tid);
     __syncthreads();
@@ -363,8 +421,8 @@ __global__ __launch_bounds__(256 * HPW) void m2rnn_bwd_kernel(BwdArgs a) {
     float* dst = a.ws_dW + (head * 4 + j) * 256;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[(4 * g + i) * 16 + m] = dW[i] * kInvScale;
-    if (j == 0 && m == 0) *(f4*)(a.ws_dwr + head * 16 + 4 * g) = dwr;
   }
+  if (tid < HPW * 16 && n0 + tid / 16 < a.N) a.ws_dwr[((size_t)b * a.N + n0 + tid / 16) * 16 + tid % 16] = dwr;
 }
 
 // Fixed-order sums over workgroups (dq, dk), batch rows and row tiles (dW),
@@ -421,7 +479,14 @@ size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* of
 template <typename TIn>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   typedef BwdCfg<kBwdHPW> Cfg;
-  static_assert(Cfg::kBytes <= 64 * 1024, "backward LDS budget");
+  static_assert(Cfg::kBytes <= 160 * 1024, "backward LDS budget");
+  static bool attr_set = false;   // per process; the attribute is per kernel
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)m2rnn_bwd_kernel<TIn, kBwdHPW>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
   dim3 grid((unsigned)(a.B * a.ngroups)), block(Cfg::NT);
   hipLaunchKernelGGL((m2rnn_bwd_kernel<TIn, kBwdHPW>), grid, block, Cfg::kBytes, stream, a);
   hipError_t e = hipGetLastError();
