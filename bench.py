@@ -37,6 +37,11 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target length of the oracle CPU-baseline sample")
+    ap.add_argument("--copy-calibration-bytes", type=int, default=0,
+                    help="also run one plain device-to-device copy of this many bytes (for scaling the "
+                         "HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -51,28 +56,68 @@ def algorithmic_bytes_fwd(w):
     return ins + outs + ck
 
 
-def cpu_baseline(w, x, which, threads):
-    import numpy as np
+def kernel_source_sha256():
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "non_linear_matrix_amd", "csrc", "*"))):
+        with open(p, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload, which):
+    """HBM bytes per launch from the committed profiler summary for this
+    workload (two rocprofv3 --pmc passes, FETCH_SIZE and WRITE_SIZE, scaled by
+    a plain copy of known size), or None when there is none or the kernel
+    sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"m2rnn_{workload}_hbm_bytes.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch_backward",
+                                                       "traffic_bytes_per_launch_forward", "source_sha256"):
+                k, v = line.split(":", 1)
+                vals[k] = v.strip()
+    if vals.get("source_sha256") != kernel_source_sha256():
+        return None
+    key = "traffic_bytes_per_launch_backward" if which == "bwd" else "traffic_bytes_per_launch_forward"
+    return float(vals[key]) if key in vals else None
+
+
+def cpu_baseline(w, x, which, threads, seconds):
+    """The fp64 oracle timed on a bounded sample of the same inputs: the first
+    batch rows and heads at the full length, sized from a short calibration
+    run to take about `seconds`."""
     import oracle
     nthreads = threads or min(16, os.cpu_count() or 1)
-    # bounded sample: the first Bs batch rows and Ns heads at the full length
-    Bs, Ns = min(w.B, 2), min(w.N, max(1, nthreads // 2))
     T = w.T
-    if which == "fwdbwd":
-        T = min(T, 2048)
-    sl = dict(q=x["q"][:Bs, :T], k=x["k"][:Bs, :T], v=x["v"][:Bs, :T, :Ns], f=x["f"][:Bs, :T, :Ns],
-              W=x["W"][:Ns], wr=x["wr"][:Ns])
-    ins = [sl[n].double().numpy() for n in ("q", "k", "v", "f", "W", "wr")]
-    t0 = time.perf_counter()
-    oracle.forward(*ins, nthreads=nthreads)
-    if which == "fwdbwd":
-        dy = x["dy"][:Bs, :T, :Ns].double().numpy()
-        oracle.backward(*ins, dy, nthreads=nthreads)
-    dt = time.perf_counter() - t0
+
+    def run(Bs, Ns):
+        sl = dict(q=x["q"][:Bs], k=x["k"][:Bs], v=x["v"][:Bs, :, :Ns], f=x["f"][:Bs, :, :Ns],
+                  W=x["W"][:Ns], wr=x["wr"][:Ns])
+        ins = [sl[n].double().numpy() for n in ("q", "k", "v", "f", "W", "wr")]
+        dy = x["dy"][:Bs, :, :Ns].double().numpy() if which == "fwdbwd" else None
+        t0 = time.perf_counter()
+        oracle.forward(*ins, nthreads=nthreads)
+        if which == "fwdbwd":
+            oracle.backward(*ins, dy, nthreads=nthreads)
+        return time.perf_counter() - t0
+
+    # calibration: one batch row, as many heads as threads
+    Ns0 = min(w.N, nthreads)
+    rate = 1 * T * Ns0 / max(run(1, Ns0), 1e-6)
+    chains = max(1, int(seconds * rate / T))
+    Ns = min(w.N, max(1, chains))
+    Bs = min(w.B, max(1, chains // Ns))
+    dt = run(Bs, Ns)
     htok = Bs * T * Ns
     return {"value": htok / dt, "unit": "head-tokens/s", "cores": min(nthreads, Bs * Ns), "kind": "oracle",
-            "sample": f"{'fwd+bwd' if which == 'fwdbwd' else 'fwd'} fp64 oracle on B={Bs} T={T} N={Ns} "
-                      f"(first rows/heads of the same inputs), {dt:.1f} s"}
+            "sample": f"{'forward+backward' if which == 'fwdbwd' else 'forward'} of the fp64 oracle on the first "
+                      f"B={Bs} batch rows x N={Ns} heads at T={T} of the same inputs ({htok} head-tokens), "
+                      f"{dt:.1f} s on {min(nthreads, Bs * Ns)} threads"}
 
 
 def main():
@@ -121,6 +166,14 @@ def main():
             if ev is not None:
                 ev[2].record(stream)
 
+    if args.copy_calibration_bytes > 0:
+        # a plain copy of known size: its profiler byte counters give the scale
+        # factor for the kernels' FETCH_SIZE / WRITE_SIZE readings
+        src = torch.empty(args.copy_calibration_bytes // 4, device=dev, dtype=torch.float32).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -142,9 +195,13 @@ def main():
     value = htok * args.steps / (total_ms * 1e-3)
     # dominant kernel and its algorithmic MFMA work per launch
     if args.which == "fwdbwd" and bwd_ms > fwd_ms:
-        dom, dom_ms, flops = "m2rnn_backward", bwd_ms, 3 * FLOP_PER_CONTRACTION * htok
+        # the backward call: replay, reverse-sweep and reduction launches on one stream
+        dom, dom_ms, flops = ("m2rnn_backward (m2rnn_fwd_kernel<...,true> replay + m2rnn_bwd_kernel + "
+                              "m2rnn_bwd_reduce_kernel)"), bwd_ms, 3 * FLOP_PER_CONTRACTION * htok
+        traffic = profiled_traffic(name, "bwd")
     else:
         dom, dom_ms, flops = "m2rnn_fwd_kernel", fwd_ms, FLOP_PER_CONTRACTION * htok
+        traffic = profiled_traffic(name, "fwd")
     achieved = flops / (dom_ms * 1e-3) / 1e12
     res = {
         "metric": "M2RNN scan head-tokens/s (K=64,V=16) fwd & bwd; % of HBM/MFMA roofline",
@@ -162,19 +219,20 @@ def main():
         "config": {"workload": name, "pass": "forward+backward" if args.which == "fwdbwd" else "forward",
                    "B": B, "T": T, "N": N, "K": K_DIM, "V": V_DIM, "input_dtype": w.dtype,
                    "ckpt_every": ck if args.which == "fwdbwd" else 0},
+        "copy_calibration_bytes": args.copy_calibration_bytes,
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
         "fwd_head_tokens_per_s": htok / (fwd_ms * 1e-3),
         "bwd_head_tokens_per_s": htok / (bwd_ms * 1e-3) if bwd_ms else None,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": None, "kernel": dom,
+                     "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": traffic, "kernel": dom,
                      "kernel_ms": dom_ms,
                      "algorithmic": f"{flops / htok:.0f} flop/head-token x {htok} head-tokens per launch"},
         "hbm": {"fwd_algorithmic_bytes": algorithmic_bytes_fwd(w),
                 "fwd_achieved_GBs": algorithmic_bytes_fwd(w) / (fwd_ms * 1e-3) / 1e9, "peak_GBs": HBM_PEAK_GBS},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, x_cpu, args.which, args.cpu_threads)
+        res["cpu_baseline"] = cpu_baseline(w, x_cpu, args.which, args.cpu_threads, args.cpu_seconds)
     print(json.dumps(res), flush=True)
     return 0
 
