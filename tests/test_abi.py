@@ -1,0 +1,68 @@
+"""The C-ABI library on the CPU: it loads, exports every entry point that
+include/m2rnn.h declares, and rejects bad arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "m2rnn.h")
+
+
+def declared():
+    with open(HEADER) as fh:
+        src = fh.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(m2rnn_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def m2():
+    import non_linear_matrix_amd
+    return non_linear_matrix_amd
+
+
+def test_header_declares_the_entry_points():
+    assert declared() == ["m2rnn_backward", "m2rnn_backward_workspace_bytes", "m2rnn_forward",
+                          "m2rnn_last_error"]
+
+
+def test_library_exports_every_declared_symbol(m2):
+    lib = ctypes.CDLL(m2.LIB_PATH)
+    for name in declared():
+        assert hasattr(lib, name), name
+
+
+def test_workspace_query(m2):
+    ws = m2.m2rnn_backward_workspace_bytes
+    assert ws(2, 100, 5, 64, 16, 64) > 0
+    assert ws(2, 100, 5, 64, 16, 64) % 256 == 0
+    # the 8-step replay states are only needed when checkpoints are sparser
+    assert ws(2, 100, 5, 64, 16, 8) < ws(2, 100, 5, 64, 16, 64)
+    assert ws(2, 100, 5, 32, 16, 64) == 0 and ws(2, 100, 5, 64, 16, 0) == 0 and ws(0, 100, 5, 64, 16, 64) == 0
+
+
+def test_argument_errors_without_launch(m2):
+    dummy = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    args6 = [dummy] * 6
+    f = m2.lib.m2rnn_forward
+    assert f(1, 4, 2, 32, 16, 0, *args6, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert "K=64" in m2.m2rnn_last_error()
+    assert f(1, 4, 2, 64, 8, 0, *args6, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert f(1, 4, 2, 64, 16, 5, *args6, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(-1, 4, 2, 64, 16, 0, *args6, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 16, 0, None, *args6[1:], dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert "q" in m2.m2rnn_last_error()
+    odd = ctypes.c_void_p(256 + 4)   # y must be 16-byte aligned
+    assert f(1, 4, 2, 64, 16, 0, *args6, odd, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 16, 0, *args6, dummy, dummy, dummy, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 16, 0, *args6, dummy, dummy, None, -3, None) == m2.M2RNN_ERR_INVALID_ARG
+    b = m2.lib.m2rnn_backward
+    grads = [dummy] * 6
+    assert b(1, 4, 2, 64, 16, 0, *args6, dummy, 0, dummy, None, *grads, dummy, 1 << 30, None) == \
+        m2.M2RNN_ERR_INVALID_ARG          # ckpt_every must be >= 1
+    assert b(1, 4, 2, 64, 16, 0, *args6, dummy, 64, dummy, None, *grads, dummy, 16, None) == \
+        m2.M2RNN_ERR_WORKSPACE            # too small
+    assert "workspace" in m2.m2rnn_last_error()
+    assert b(1, 4, 2, 64, 16, 0, *args6, dummy, 64, dummy, None, *grads, None, 0, None) == m2.M2RNN_ERR_WORKSPACE
