@@ -15,32 +15,32 @@
 // tiles do not remove the sequential dependency"); this one keeps the caches
 // on chip instead:
 //
+//  * the states the sweep restarts from: when the caller's checkpoints are
+//    sparser than kSub steps, a replay launch (the forward kernel in DENSE
+//    mode, m2rnn_fwd.hip) restarts every checkpoint chunk in parallel and
+//    writes H every kSub steps into the workspace;
 //  * one wave64 owns one 16-row tile of one (b, n) head (rows of H never mix
 //    in the recurrence; only the reductions couple them), so a head is four
 //    waves of one workgroup and a workgroup holds HPW heads of a batch row;
-//  * the forward stored H every `ckpt_every` steps.  Per checkpoint chunk,
-//    level 1 replays the chunk and writes a sub-checkpoint every kSub steps
-//    to the workspace; level 2 replays each sub-chunk (latest first) keeping
-//    H_{t-1} and Z_t of its kSub steps in registers, then the reverse sweep
-//    walks those steps back;
+//    per kSub-step sub-chunk, latest first, the wave replays the steps keeping
+//    H_{t-1} and Z_t in registers, then walks them back;
 //  * C_{t-1}^T = f R^T + W D^T is one v_mfma_f32_16x16x32_bf16 per step (W in
 //    the A operand, hi/lo split of D^T in B, f R^T as the accumulator input;
 //    four exact fp32 MFMAs for fp32 inputs), in the same transposed frame as
 //    the forward, so C stays in registers;
 //  * dW needs a contraction over the rows, which live on lanes: each step the
 //    wave writes its H_{t-1} and D tiles to LDS and reads them back in MFMA
-//    operand layout for four exact v_mfma_f32_16x16x4_f32, accumulated in
-//    registers over the whole sequence;
-//  * per-step sums over a head's rows (df, dv) and over the heads of the
-//    workgroup (dq, dk) go through LDS after every sub-chunk; the sums over
-//    workgroups (dq, dk) and batch rows (dW, dw_r) are a second, fixed-order
-//    reduction kernel.
+//    operand layout one step later (bf16 hi/lo MFMAs, or exact fp32 MFMAs for
+//    fp32 inputs), accumulated in registers over the whole sequence;
+//  * per-lane partials of df, dv, dq and dk go to LDS and are reduced once per
+//    sub-chunk; the sums over workgroups (dq, dk) and batch rows (dW, dw_r)
+//    are a second, fixed-order reduction kernel.
 #include "m2rnn_device.h"
 #include "m2rnn_internal.h"
 
 namespace m2rnn {
 
-constexpr int kSub = 8;  // steps kept in registers by the level-2 replay
+constexpr int kSub = 4;  // steps between restart states; their H_{t-1}, Z_t stay in registers
 
 template <int HPW>
 struct BwdCfg {
@@ -53,7 +53,7 @@ struct BwdCfg {
   // per wave, two slots of {H_{t-1} tile, D tile}; a tile is stored as
   // [v / 4][kk][v % 4] with an 80-float stride between the v / 4 blocks so that
   // both the 16-byte writes and the operand-layout reads are bank-conflict free
-  static constexpr int kTile = 4 * 80;
+  static constexpr int kTile = 3 * 80 + 64;
   static constexpr int kXpose = NWAVES * 4 * kTile;
   // per-lane partials of one sub-chunk, reduced in the pass: [s][h][tile][lane]
   static constexpr int kPart = kSub * HPW * 4 * 64;
@@ -230,7 +230,7 @@ __device__ __forceinline__ f4 fwd_tile_step(const WOperand<TIn>& Aw, f4& P, floa
 }
 
 template <typename TIn, int HPW>
-__global__ __launch_bounds__(256 * HPW) void m2rnn_bwd_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) void m2rnn_bwd_kernel(BwdArgs a) {
   typedef BwdCfg<HPW> Cfg;
   constexpr int NT = Cfg::NT;
   extern __shared__ float smem[];
@@ -282,9 +282,10 @@ __global__ __launch_bounds__(256 * HPW) void m2rnn_bwd_kernel(BwdArgs a) {
   for (int sb = ns - 1, it = 0; sb >= 0; --sb, ++it) {
     const int t0 = sb * L, len = min(L, a.T - t0);
     const bool more = sb > 0;
+    const int tidv = tid;
     f4 P = Pnext;
     if (more) {
-      st.load(a, b, n0, t0 - L, L, tid);
+      st.load(a, b, n0, t0 - L, L, tidv);
       if (live) Pnext = *(const f4*)(Hs + (size_t)(sb - 1) * 1024) * kScale;
     }
     const float* buf = smem + (it & 1) * Cfg::kBuf;
@@ -383,7 +384,7 @@ __global__ __launch_bounds__(256 * HPW) void m2rnn_bwd_kernel(BwdArgs a) {
       if (lane == 0 && n0 + hh < a.N) a.df[((size_t)b * a.T + t0 + s) * a.N + n0 + hh] = x;
     }
     // dv[b][t][n][v'] = (1/c) sum over tiles and g of the partial at lane 16 g + v', + w_r u
-    for (int u = tid; u < len * HPW * 16; u += NT) {
+    for (int u = tidv; u < len * HPW * 16; u += NT) {
       const int s = u / (HPW * 16), hh = (u / 16) % HPW, e = u % 16;
       if (n0 + hh < a.N) {
         const float* d = dvbuf + s * Cfg::NWAVES * 64 + hh * 256 + e;
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(256 * HPW) void m2rnn_bwd_kernel(BwdArgs a) {
       }
     }
     // dq, dk partials of this workgroup's heads -> workspace [b][grp][t][dq|dk][64]
-    for (int u = tid; u < len * 128; u += NT) {
+    for (int u = tidv; u < len * 128; u += NT) {
       const int s = u / 128, which = (u / 64) % 2, r = u % 64;   // row r = 16 tile + m
       const float* src = (which ? dkbuf : dqbuf) + s * Cfg::NWAVES * 64 + (r / 16) * 64 + r % 16;
       float acc = 0.f;
@@ -408,12 +409,12 @@ __global__ __launch_bounds__(256 * HPW) void m2rnn_bwd_kernel(BwdArgs a) {
       a.ws_dqk[(((size_t)b * ngroups + grp) * a.T + t0 + s) * 128 + u % 128] = which ? acc : acc * kInvScale;
     }
     // dw_r partial: sum over the sub-chunk of u (.) v (padded steps stage u = 0)
-    if (tid < HPW * 16) {
-      const int hh = tid / 16, e = tid % 16;
+    if (tidv < HPW * 16) {
+      const int hh = tidv / 16, e = tidv % 16;
 #pragma unroll
       for (int s = 0; s < kSub; ++s) dwr = fmaf(U_s[(s * HPW + hh) * 16 + e], V_s[(s * HPW + hh) * 16 + e], dwr);
     }
-    if (more) st.store(smem + ((it + 1) & 1) * Cfg::kBuf, tid);
+    if (more) st.store(smem + ((it + 1) & 1) * Cfg::kBuf, tidv);
     __syncthreads();
   }
 
