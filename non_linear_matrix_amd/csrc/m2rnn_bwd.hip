@@ -30,8 +30,9 @@
 //    the forward, so C stays in registers;
 //  * dW needs a contraction over the rows, which live on lanes: each step the
 //    wave writes its H_{t-1} and D tiles to LDS and reads them back in MFMA
-//    operand layout one step later (bf16 hi/lo MFMAs, or exact fp32 MFMAs for
-//    fp32 inputs), accumulated in registers over the whole sequence;
+//    operand layout one step later (one bf16 MFMA on rounded factors for
+//    bf16 inputs, four exact fp32 MFMAs for fp32 inputs), accumulated in
+//    registers over the whole sequence;
 //  * per-lane partials of df, dv, dq and dk go to LDS and are reduced once per
 //    sub-chunk; the sums over workgroups (dq, dk) and batch rows (dW, dw_r)
 //    are a second, fixed-order reduction kernel.
@@ -188,8 +189,11 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 
 // dW[v][v'] += sum over 16 rows kk of A[kk][v] B[kk][v'], with lane (g, m)
 // holding A, B at rows 4r + g (r = 0..3) and column m.  fp32 inputs: four
-// exact v_mfma_f32_16x16x4_f32.  bf16 inputs: hi/lo bf16 halves,
-// A_hi B_hi + A_lo B_hi in one 16x16x32 and A_hi B_lo in one 16x16x16 MFMA.
+// exact v_mfma_f32_16x16x4_f32.  bf16 inputs: one v_mfma_f32_16x16x16_bf16 on
+// the RNE bf16 roundings of both factors.  Each product is off by at most
+// ~2^-8 relative; over a whole sequence the errors are independent and the
+// sum over time and rows stays within ~6e-4 of max|dW| (bf16 inputs carry a
+// 5e-3 bar), for a quarter of the VALU work of the hi/lo products.
 template <typename TIn>
 __device__ __forceinline__ f4 dw_update(f4 a, f4 b, f4 acc) {
   if constexpr (sizeof(TIn) == 4) {
@@ -197,17 +201,15 @@ __device__ __forceinline__ f4 dw_update(f4 a, f4 b, f4 acc) {
     for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], acc, 0, 0, 0);
     return acc;
   } else {
-    uint32_t ah01, al01, ah23, al23, bh01, bl01, bh23, bl23;
-    split2(a[0], a[1], ah01, al01);
-    split2(a[2], a[3], ah23, al23);
-    split2(b[0], b[1], bh01, bl01);
-    split2(b[2], b[3], bh23, bl23);
-    acc = mfma_bf16(__builtin_bit_cast(bf16x8, (u32x4{ah01, ah23, al01, al23})),
-                    __builtin_bit_cast(bf16x8, (u32x4{bh01, bh23, bh01, bh23})), acc);
     typedef short s4 __attribute__((ext_vector_type(4)));
+    const bf16x2 a01 = __builtin_convertvector((f2{a[0], a[1]}), bf16x2);
+    const bf16x2 a23 = __builtin_convertvector((f2{a[2], a[3]}), bf16x2);
+    const bf16x2 b01 = __builtin_convertvector((f2{b[0], b[1]}), bf16x2);
+    const bf16x2 b23 = __builtin_convertvector((f2{b[2], b[3]}), bf16x2);
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, (u32x2{ah01, ah23})),
-                                                     __builtin_bit_cast(s4, (u32x2{bl01, bl23})), acc, 0, 0, 0);
+    const u32x2 au = {__builtin_bit_cast(uint32_t, a01), __builtin_bit_cast(uint32_t, a23)};
+    const u32x2 bu = {__builtin_bit_cast(uint32_t, b01), __builtin_bit_cast(uint32_t, b23)};
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, au), __builtin_bit_cast(s4, bu), acc, 0, 0, 0);
   }
 }
 
