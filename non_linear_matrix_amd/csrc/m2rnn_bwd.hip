@@ -45,6 +45,8 @@ constexpr int kSub = 4;  // steps between restart states; their H_{t-1}, Z_t sta
 
 template <int HPW>
 struct BwdCfg {
+  // the reduction pass gives each of the 8 waves of two heads a fixed role
+  static_assert(HPW == 2 && kSub == 4, "backward workgroup shape: lane = (step, 16 values)");
   static constexpr int NWAVES = HPW * 4;
   static constexpr int NT = 64 * NWAVES;
   // per staged step: K_s[64] (c k), Q_s[64] (q), V_s[HPW][16], F_s[HPW][4],
@@ -56,92 +58,78 @@ struct BwdCfg {
   // both the 16-byte writes and the operand-layout reads are bank-conflict free
   static constexpr int kTile = 3 * 80 + 64;
   static constexpr int kXpose = NWAVES * 4 * kTile;
-  // per-lane partials of one sub-chunk, reduced in the pass: [s][h][tile][lane]
-  static constexpr int kPart = kSub * HPW * 4 * 64;
-  static constexpr int kFloats = 2 * kBuf + kXpose + 4 * kPart;
+  // per-lane partials of one sub-chunk, each a 256-float block per (step, head):
+  //   qk: [s][dq | dk][h] x [g][64 rows], the 4-row quads of lane group g
+  //       rotated by 4 g quads (conflict-free writes, 16-byte reads);
+  //   dv: [s][h] x [v'][16 (tile, g)], quads rotated by v' / 4;
+  //   df: [s][h] x [tile][lane].
+  static constexpr int kQK = kSub * 2 * HPW * 256;
+  static constexpr int kDV = kSub * HPW * 256;
+  static constexpr int kDF = kSub * HPW * 256;
+  static constexpr int kFloats = 2 * kBuf + kXpose + kQK + kDV + kDF;
   static constexpr int kBytes = kFloats * 4;
 };
 
-// Staging of one sub-chunk (up to kSub steps starting at t0) for HPW heads.
-template <typename TIn, int HPW, int NT>
-struct BwdStager {
+// Staging of one sub-chunk (kSub steps from t0, the first len of them real)
+// through registers into an LDS buffer.  Wave 7 carries k, wave 6 q (lane =
+// 4 consecutive elements of one step), wave 5 v and u (lanes 0..31) and f
+// (lanes 32..39).  Steps past len are staged as f = 1, q = k = v = u = 0.
+template <typename TIn, int HPW>
+struct BwdStage {
   typedef typename Vec4<TIn>::raw raw;
-  static constexpr int kQK = (2 * kSub * 16 + NT - 1) / NT;
-  static constexpr int kV = (kSub * HPW * 4 + NT - 1) / NT;
-  raw qk[kQK];
-  raw vv[kV];
-  f4 uu[kV];
+  static constexpr int kVU = kSub * HPW * 4;   // lanes carrying v, u
+  static constexpr int kF = kSub * HPW;        // lanes carrying f
+  raw x;
+  f4 uu;
   float ff;
 
-  __device__ void load(const BwdArgs& a, int b, int n0, int t0, int len, int tid) {
-#pragma unroll
-    for (int r = 0; r < kQK; ++r) {
-      int u = tid + r * NT;
-      int which = u / (kSub * 16);
-      int t = (u / 16) % kSub, e0 = (u % 16) * 4;
-      qk[r] = Vec4<TIn>::zero();
-      if (u < 2 * kSub * 16 && t < len) {
-        const TIn* src = (const TIn*)(which ? a.k : a.q);
-        qk[r] = Vec4<TIn>::load(src + ((size_t)b * a.T + t0 + t) * 64 + e0);
+  __device__ void load(const BwdArgs& a, int w, int lane, int b, int n0, int t0, int len) {
+    x = Vec4<TIn>::zero();
+    if (w >= 6) {
+      const TIn* src = (const TIn*)(w == 7 ? a.k : a.q) + ((size_t)b * a.T + t0) * 64;
+      if (lane < len * 16) x = Vec4<TIn>::load(src + lane * 4);
+    } else if (w == 5) {
+      uu = f4{0.f, 0.f, 0.f, 0.f};
+      ff = 1.0f;
+      if (lane < kVU) {
+        const int t = lane / (HPW * 4), h = (lane / 4) % HPW, c4 = lane % 4;
+        if (t < len && n0 + h < a.N) {
+          const size_t off = (((size_t)b * a.T + t0 + t) * a.N + n0 + h) * 16 + 4 * c4;
+          x = Vec4<TIn>::load((const TIn*)a.v + off);
+          uu = *(const f4*)(a.dy + off);
+        }
+      } else if (lane < kVU + kF) {
+        const int t = (lane - kVU) / HPW, h = (lane - kVU) % HPW;
+        if (t < len && n0 + h < a.N) ff = to_f32(((const TIn*)a.f)[((size_t)b * a.T + t0 + t) * a.N + n0 + h]);
       }
-    }
-#pragma unroll
-    for (int r = 0; r < kV; ++r) {
-      int u = tid + r * NT;
-      int t = u / (HPW * 4), h = (u / 4) % HPW, c4 = u % 4;
-      vv[r] = Vec4<TIn>::zero();
-      uu[r] = f4{0.f, 0.f, 0.f, 0.f};
-      if (u < kSub * HPW * 4 && t < len && n0 + h < a.N) {
-        const size_t off = (((size_t)b * a.T + t0 + t) * a.N + n0 + h) * 16 + 4 * c4;
-        vv[r] = Vec4<TIn>::load((const TIn*)a.v + off);
-        uu[r] = *(const f4*)(a.dy + off);
-      }
-    }
-    ff = 1.0f;
-    {
-      int t = tid / HPW, h = tid % HPW;
-      if (tid < kSub * HPW && t < len && n0 + h < a.N)
-        ff = to_f32(((const TIn*)a.f)[((size_t)b * a.T + t0 + t) * a.N + n0 + h]);
     }
   }
 
-  __device__ void store(float* buf, int tid) const {
+  __device__ void store(float* buf, int w, int lane) const {
     float* K_s = buf;
     float* Q_s = K_s + kSub * 64;
     float* V_s = Q_s + kSub * 64;
     float* F_s = V_s + kSub * HPW * 16;
     float* U_s = F_s + kSub * HPW * 4;
     float* Kp_s = U_s + kSub * HPW * 16;
+    if (w == 7) {
+      const f4 xv = Vec4<TIn>::to_f4(x) * kScale;
+      *(f4*)(K_s + lane * 4) = xv;
+      // element e = 4 (lane % 16) + i of step lane / 16 goes to [tile][g][r]
+      // with row e = 16 tile + 4 r + g
+      float* kp = Kp_s + (lane / 16) * 64 + ((lane % 16) / 4) * 16 + lane % 4;
 #pragma unroll
-    for (int r = 0; r < kQK; ++r) {
-      int u = tid + r * NT;
-      if (u < 2 * kSub * 16) {
-        int which = u / (kSub * 16);
-        int t = (u / 16) % kSub, e0 = (u % 16) * 4;
-        f4 x = Vec4<TIn>::to_f4(qk[r]);
-        if (which) x *= kScale;
-        *(f4*)((which ? K_s : Q_s) + t * 64 + e0) = x;
-        if (which) {
-          // row e = 16 tile + 4 r + g goes to [tile][g][r]
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int e = e0 + i;
-            Kp_s[t * 64 + (e / 16) * 16 + (e % 4) * 4 + (e % 16) / 4] = x[i];
-          }
-        }
+      for (int i = 0; i < 4; ++i) kp[i * 4] = xv[i];
+    } else if (w == 6) {
+      *(f4*)(Q_s + lane * 4) = Vec4<TIn>::to_f4(x);
+    } else if (w == 5) {
+      if (lane < kVU) {
+        *(f4*)(V_s + lane * 4) = Vec4<TIn>::to_f4(x);
+        *(f4*)(U_s + lane * 4) = uu;
+      } else if (lane < kVU + kF) {
+        const float gg = 1.0f - ff;
+        *(f4*)(F_s + (lane - kVU) * 4) = f4{ff, kScale * gg, -2.0f * kScale * gg, gg};
       }
-    }
-#pragma unroll
-    for (int r = 0; r < kV; ++r) {
-      int u = tid + r * NT;
-      if (u < kSub * HPW * 4) {
-        *(f4*)(V_s + u * 4) = Vec4<TIn>::to_f4(vv[r]);
-        *(f4*)(U_s + u * 4) = uu[r];
-      }
-    }
-    if (tid < kSub * HPW) {
-      float gg = 1.0f - ff;
-      *(f4*)(F_s + tid * 4) = f4{ff, kScale * gg, -2.0f * kScale * gg, gg};
     }
   }
 };
@@ -174,18 +162,6 @@ template <> struct WBackOperand<float> {
     return cin;
   }
 };
-
-// Sum over the four lanes m, m+16, m+32, m+48 (every lane gets the sum).
-// v_permlane16_swap(x, x) returns x of the even and of the odd row of each
-// row pair; v_permlane32_swap(x, x) returns x of the lower and upper half.
-__device__ __forceinline__ float sum_lane_groups(float x) {
-  const uint32_t u = __builtin_bit_cast(uint32_t, x);
-  const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-  const float s = __builtin_bit_cast(float, (uint32_t)p[0]) + __builtin_bit_cast(float, (uint32_t)p[1]);
-  const uint32_t v = __builtin_bit_cast(uint32_t, s);
-  const auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  return __builtin_bit_cast(float, (uint32_t)q[0]) + __builtin_bit_cast(float, (uint32_t)q[1]);
-}
 
 // dW[v][v'] += sum over 16 rows kk of A[kk][v] B[kk][v'], with lane (g, m)
 // holding A, B at rows 4r + g (r = 0..3) and column m.  fp32 inputs: four
@@ -231,16 +207,33 @@ __device__ __forceinline__ f4 fwd_tile_step(const WOperand<TIn>& Aw, f4& P, floa
   return r;
 }
 
+// Sum over lanes of four values at once: returns, in every lane of 16-lane
+// row r, the sum over all 64 lanes of x[o] with o = 2 (r & 1) + (r >> 1).
+// v_permlane32_swap(a, b) yields {[a_lo, b_lo], [a_hi, b_hi]} by 32-lane
+// halves and v_permlane16_swap(a, b) yields {[a0, b0, a2, b2], [a1, b1, a3, b3]}
+// by 16-lane rows (checked on the GPU).
+__device__ __forceinline__ float sum4_over_lanes(float x0, float x1, float x2, float x3) {
+  auto s32 = [](float p, float q) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, p), __builtin_bit_cast(uint32_t, q),
+                                                    false, false);
+    return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+  };
+  const float y01 = s32(x0, x1);   // lanes 0..31: x0 partial, 32..63: x1 partial
+  const float y23 = s32(x2, x3);
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, y01), __builtin_bit_cast(uint32_t, y23),
+                                                  false, false);
+  // rows: x0, x2, x1, x3, each summed over its four lane groups so far
+  return row_sum16(__builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
 template <typename TIn, int HPW>
 __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) void m2rnn_bwd_kernel(BwdArgs a) {
   typedef BwdCfg<HPW> Cfg;
-  constexpr int NT = Cfg::NT;
   extern __shared__ float smem[];
   float* xpose = smem + 2 * Cfg::kBuf;
-  float* dfbuf = xpose + Cfg::kXpose;   // per-lane partials, [s][h][tile][lane]
-  float* dvbuf = dfbuf + Cfg::kPart;
-  float* dqbuf = dvbuf + Cfg::kPart;
-  float* dkbuf = dqbuf + Cfg::kPart;
+  float* qkbuf = xpose + Cfg::kXpose;
+  float* dvbuf = qkbuf + Cfg::kQK;
+  float* dfbuf = dvbuf + Cfg::kDV;
 
   const int tid = threadIdx.x;
   // wave-uniform indices live in scalar registers
@@ -259,6 +252,10 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   // stored states H at t = s * L (s = 0 .. ns-1), L = a.ckpt_every <= kSub
   const int L = a.ckpt_every, ns = a.nck;
   const float* Hs = a.H_ckpt + head * (size_t)ns * 1024 + kk * 16 + 4 * g;
+  // this lane's slots in the partials blocks (see BwdCfg)
+  const int qk_slot = hw * 256 + g * 64 + (((4 * j + m / 4 + 4 * g) & 15) << 2) + (m & 3);
+  const int dv_slot = hw * 256 + m * 16 + (((j + m / 4) & 3) << 2) + g;
+  const int df_slot = w * 64 + lane;
 
   WOperand<TIn> Af;
   Af.load(live ? (const TIn*)a.W + (size_t)n * 256 : nullptr, g, m);
@@ -269,13 +266,23 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   f4 C = {0.f, 0.f, 0.f, 0.f};
   if (live && a.dH_T) C = *(const f4*)(a.dH_T + head * 1024 + kk * 16 + 4 * g);
   f4 dW = {0.f, 0.f, 0.f, 0.f};   // lane (g, m), register i: c * dW[4g + i][m] partial
-  float dwr = 0.f;                 // thread tid < HPW * 16: dw_r[n0 + tid / 16][tid % 16] partial
+  // dv waves (2, 3): w_r of their (head, v') and the dw_r partial of their step slot
+  float wr_e = 0.f, dwr = 0.f;
+  if (w == 2 || w == 3) {
+    const int hh = w - 2;
+    if (n0 + hh < a.N) wr_e = to_f32(((const TIn*)a.wr)[(size_t)(n0 + hh) * 16 + m]);
+  }
+  if (!live) {
+    // a missing head adds zero to the dq, dk sums of the pass
+#pragma unroll
+    for (int s = 0; s < 2 * kSub; ++s) qkbuf[s * HPW * 256 + qk_slot] = 0.f;
+  }
 
-  BwdStager<TIn, HPW, NT> st;
+  BwdStage<TIn, HPW> st;
   {
     const int t0 = (ns - 1) * L;
-    st.load(a, b, n0, t0, min(L, a.T - t0), tid);
-    st.store(smem, tid);
+    st.load(a, w, lane, b, n0, t0, min(L, a.T - t0));
+    st.store(smem, w, lane);
   }
   f4 Pnext = {0.f, 0.f, 0.f, 0.f};
   if (live) Pnext = *(const f4*)(Hs + (size_t)(ns - 1) * 1024) * kScale;
@@ -284,10 +291,9 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   for (int sb = ns - 1, it = 0; sb >= 0; --sb, ++it) {
     const int t0 = sb * L, len = min(L, a.T - t0);
     const bool more = sb > 0;
-    const int tidv = tid;
     f4 P = Pnext;
     if (more) {
-      st.load(a, b, n0, t0 - L, L, tidv);
+      st.load(a, w, lane, b, n0, t0 - L, L);
       if (live) Pnext = *(const f4*)(Hs + (size_t)(sb - 1) * 1024) * kScale;
     }
     const float* buf = smem + (it & 1) * Cfg::kBuf;
@@ -297,7 +303,6 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     const float* F_s = V_s + kSub * HPW * 16;
     const float* U_s = F_s + kSub * HPW * 4;
     const float* Kp_s = U_s + kSub * HPW * 16;     // c k permuted, [s][tile][g][r]
-    const int part = w * 64 + lane;                // this lane's slot in a partials row
 
     if (live) {
       // replay the sub-chunk keeping H_{t-1} and Z_t on chip
@@ -305,7 +310,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
 #pragma unroll
       // Steps s >= len of a short last sub-chunk are staged as f = 1 with
       // q = k = v = u = 0: an exact identity for C and a zero contribution to
-      // every gradient, so all kSub steps run unguarded.
+      // dq, dk, dv, dW and dw_r (df of such steps is not stored), so all kSub
+      // steps run unguarded.
       for (int s = 0; s < kSub; ++s) {
         {
           const f4 vv = *(const f4*)(V_s + (s * HPW + hw) * 16 + 4 * g);
@@ -319,7 +325,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
           float dq = 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) dq = fmaf(P[i], uu[i], dq);
-          dqbuf[s * Cfg::NWAVES * 64 + part] = dq;
+          qkbuf[(2 * s) * HPW * 256 + qk_slot] = dq;
         }
         __builtin_amdgcn_sched_barrier(0);   // keep each step's loads in its step
       }
@@ -341,7 +347,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
           dvp = fmaf(bv[r], ckp[r], dvp);
         }
         dW = dw_update<TIn>(av, bv, dW);
-        dvbuf[ps * Cfg::NWAVES * 64 + part] = dvp;          // partial of dv[v' = m] over rows 4r+g
+        dvbuf[ps * HPW * 256 + dv_slot] = dvp;              // partial of dv[v' = m] over rows 4r+g
       };
 #pragma unroll
       for (int s = kSub - 1; s >= 0; --s) {
@@ -363,8 +369,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
           }
           C = Ab.apply(D, fR);                                       // C_{t-1} = f R + D W^T
           // per-lane partials of dk_t[kk] (over v' = 4g..4g+3) and df_t
-          dkbuf[s * Cfg::NWAVES * 64 + part] = dk;
-          dfbuf[s * Cfg::NWAVES * 64 + part] = dfp;
+          qkbuf[(2 * s + 1) * HPW * 256 + qk_slot] = dk;
+          dfbuf[s * HPW * 256 + df_slot] = dfp;
           // stage H_{t-1} and D of this step, finish the previous step
           *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + g * 80 + m * 4) = Pp[s];
           *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + Cfg::kTile + g * 80 + m * 4) = D;
@@ -375,48 +381,42 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       drain(0);
     }
     __syncthreads();
-    // ---- pass: reduce this sub-chunk's per-lane partials.  Partials row
-    // [s] holds, per wave w = 4 h + tile and lane 16 g + m, the lane's share.
-    // df[b][t][n]: sum over the 4 tiles x 64 lanes of head h (one wave per (s, h))
-    for (int sh = w; sh < len * HPW; sh += Cfg::NWAVES) {
-      const int s = sh / HPW, hh = sh % HPW;
-      const float* d = dfbuf + s * Cfg::NWAVES * 64 + hh * 256 + lane;
-      float x = (d[0] + d[64]) + (d[128] + d[192]);
-      x = sum_lane_groups(row_sum16(x));
-      if (lane == 0 && n0 + hh < a.N) a.df[((size_t)b * a.T + t0 + s) * a.N + n0 + hh] = x;
-    }
-    // dv[b][t][n][v'] = (1/c) sum over tiles and g of the partial at lane 16 g + v', + w_r u
-    for (int u = tidv; u < len * HPW * 16; u += NT) {
-      const int s = u / (HPW * 16), hh = (u / 16) % HPW, e = u % 16;
-      if (n0 + hh < a.N) {
-        const float* d = dvbuf + s * Cfg::NWAVES * 64 + hh * 256 + e;
-        float acc = 0.f;
+    // ---- pass: reduce this sub-chunk's partials; each wave has one role.
+    if (w < 2) {
+      // dq (wave 0), dk (wave 1): lane (s, 4-row quad r4) sums the HPW heads
+      // and four lane groups -> workspace [b][grp][t][dq | dk][64]
+      const int s = lane / 16, r4 = lane % 16;
+      const float* src = qkbuf + (2 * s + w) * HPW * 256;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int q4 = 0; q4 < 16; ++q4) acc += d[q4 * 16];   // (tile, g) pairs
-        const float uu = U_s[(s * HPW + hh) * 16 + e];
-        const float wr = to_f32(((const TIn*)a.wr)[(size_t)(n0 + hh) * 16 + e]);
-        a.dv[(((size_t)b * a.T + t0 + s) * a.N + n0 + hh) * 16 + e] = fmaf(wr, uu, acc * kInvScale);
-      }
-    }
-    // dq, dk partials of this workgroup's heads -> workspace [b][grp][t][dq|dk][64]
-    for (int u = tidv; u < len * 128; u += NT) {
-      const int s = u / 128, which = (u / 64) % 2, r = u % 64;   // row r = 16 tile + m
-      const float* src = (which ? dkbuf : dqbuf) + s * Cfg::NWAVES * 64 + (r / 16) * 64 + r % 16;
-      float acc = 0.f;
       for (int hh = 0; hh < HPW; ++hh)
-        if (n0 + hh < a.N) {
-          const float* d = src + hh * 256;
-          acc += (d[0] + d[16]) + (d[32] + d[48]);           // the four lane groups
-        }
-      a.ws_dqk[(((size_t)b * ngroups + grp) * a.T + t0 + s) * 128 + u % 128] = which ? acc : acc * kInvScale;
-    }
-    // dw_r partial: sum over the sub-chunk of u (.) v (padded steps stage u = 0)
-    if (tidv < HPW * 16) {
-      const int hh = tidv / 16, e = tidv % 16;
 #pragma unroll
-      for (int s = 0; s < kSub; ++s) dwr = fmaf(U_s[(s * HPW + hh) * 16 + e], V_s[(s * HPW + hh) * 16 + e], dwr);
+        for (int gg = 0; gg < 4; ++gg) acc += *(const f4*)(src + hh * 256 + gg * 64 + (((r4 + 4 * gg) & 15) << 2));
+      if (w == 0) acc *= kInvScale;
+      if (s < len) *(f4*)(a.ws_dqk + (((size_t)b * ngroups + grp) * a.T + t0 + s) * 128 + w * 64 + 4 * r4) = acc;
+    } else if (w < 4) {
+      // dv[b][t][n][v'] = (1/c) (sum of the 16 (tile, g) partials) + w_r u; dw_r
+      const int hh = w - 2, s = lane / 16, e = lane % 16;
+      const float* d = dvbuf + (s * HPW + hh) * 256 + e * 16;
+      const f4 p = (*(const f4*)d + *(const f4*)(d + 4)) + (*(const f4*)(d + 8) + *(const f4*)(d + 12));
+      const float uu = U_s[(s * HPW + hh) * 16 + e];
+      dwr = fmaf(uu, V_s[(s * HPW + hh) * 16 + e], dwr);
+      if (s < len && n0 + hh < a.N)
+        a.dv[(((size_t)b * a.T + t0 + s) * a.N + n0 + hh) * 16 + e] = fmaf(wr_e, uu, ((p[0] + p[1]) + (p[2] + p[3])) * kInvScale);
+    } else if (w < 6) {
+      // df[b][t][n]: wave 4 steps 0, 1, wave 5 steps 2, 3; both heads
+      const int s0 = 2 * (w - 4);
+      float x[4];
+#pragma unroll
+      for (int o = 0; o < 4; ++o) {
+        const f4 p = *(const f4*)(dfbuf + ((s0 + o / 2) * HPW + o % 2) * 256 + lane * 4);
+        x[o] = (p[0] + p[1]) + (p[2] + p[3]);
+      }
+      const float tot = sum4_over_lanes(x[0], x[1], x[2], x[3]);
+      const int s = s0 + (g & 1), hh = g >> 1;
+      if (m == 0 && s < len && n0 + hh < a.N) a.df[((size_t)b * a.T + t0 + s) * a.N + n0 + hh] = tot;
     }
-    if (more) st.store(smem + ((it + 1) & 1) * Cfg::kBuf, tidv);
+    if (more) st.store(smem + ((it + 1) & 1) * Cfg::kBuf, w, lane);
     __syncthreads();
   }
 
@@ -425,7 +425,17 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[(4 * g + i) * 16 + m] = dW[i] * kInvScale;
   }
-  if (tid < HPW * 16 && n0 + tid / 16 < a.N) a.ws_dwr[((size_t)b * a.N + n0 + tid / 16) * 16 + tid % 16] = dwr;
+  // dw_r: the dv waves hold one partial per (step slot, head, v'); sum the
+  // step slots in a fixed order
+  if (w == 2 || w == 3) dfbuf[(w - 2) * 64 + lane] = dwr;
+  __syncthreads();
+  if (w == 0 && lane < HPW * 16) {
+    const int hh = lane / 16, e = lane % 16;
+    float acc = 0.f;
+#pragma unroll
+    for (int s = 0; s < kSub; ++s) acc += dfbuf[hh * 64 + s * 16 + e];
+    if (n0 + hh < a.N) a.ws_dwr[((size_t)b * a.N + n0 + hh) * 16 + e] = acc;
+  }
 }
 
 // Fixed-order sums over workgroups (dq, dk), batch rows and row tiles (dW),
