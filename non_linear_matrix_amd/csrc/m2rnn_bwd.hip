@@ -54,17 +54,21 @@ struct BwdCfg {
   static constexpr int kStep = 192 + HPW * 36;
   static constexpr int kBuf = kSub * kStep;
   // per wave, two slots of {H_{t-1} tile, D tile}; a tile is stored as
-  // [v / 4][kk][v % 4] with an 80-float stride between the v / 4 blocks so that
-  // both the 16-byte writes and the operand-layout reads are bank-conflict free
-  static constexpr int kTile = 3 * 80 + 64;
+  // [v / 4][kk][v % 4] with a 72-float stride between the v / 4 blocks, which
+  // keeps both the 16-byte writes and the operand-layout reads free of bank
+  // conflicts (LDS: 32 four-byte banks, a 4-byte access served per 32 lanes,
+  // a 16-byte access per 8 lanes)
+  static constexpr int kXs = 72;
+  static constexpr int kTile = 3 * kXs + 64;
   static constexpr int kXpose = NWAVES * 4 * kTile;
   // per-lane partials of one sub-chunk, each a 256-float block per (step, head):
   //   qk: [s][dq | dk][h] x [g][64 rows], the 4-row quads of lane group g
   //       rotated by 4 g quads (conflict-free writes, 16-byte reads);
-  //   dv: [s][h] x [v'][16 (tile, g)], quads rotated by v' / 4;
+  //   dv: [s][h] x [v'][20], the 16 (tile, g) partials of row v' at column
+  //       (tile + 4 g + v') mod 16;
   //   df: [s][h] x [tile][lane].
   static constexpr int kQK = kSub * 2 * HPW * 256;
-  static constexpr int kDV = kSub * HPW * 256;
+  static constexpr int kDV = kSub * HPW * 320;
   static constexpr int kDF = kSub * HPW * 256;
   static constexpr int kFloats = 2 * kBuf + kXpose + kQK + kDV + kDF;
   static constexpr int kBytes = kFloats * 4;
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   const float* Hs = a.H_ckpt + head * (size_t)ns * 1024 + kk * 16 + 4 * g;
   // this lane's slots in the partials blocks (see BwdCfg)
   const int qk_slot = hw * 256 + g * 64 + (((4 * j + m / 4 + 4 * g) & 15) << 2) + (m & 3);
-  const int dv_slot = hw * 256 + m * 16 + (((j + m / 4) & 3) << 2) + g;
+  const int dv_slot = hw * 320 + m * 20 + ((j + 4 * g + m) & 15);
   const int df_slot = w * 64 + lane;
 
   WOperand<TIn> Af;
@@ -341,13 +345,13 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
         f4 av, bv;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int at = (m / 4) * 80 + (4 * r + g) * 4 + m % 4;
+          const int at = (m / 4) * Cfg::kXs + (4 * r + g) * 4 + m % 4;
           av[r] = xs[at];                                   // c H_{t-1}[16j+4r+g][v = m]
           bv[r] = xs[Cfg::kTile + at];                      // D[16j+4r+g][v' = m]
           dvp = fmaf(bv[r], ckp[r], dvp);
         }
         dW = dw_update<TIn>(av, bv, dW);
-        dvbuf[ps * HPW * 256 + dv_slot] = dvp;              // partial of dv[v' = m] over rows 4r+g
+        dvbuf[ps * HPW * 320 + dv_slot] = dvp;              // partial of dv[v' = m] over rows 4r+g
       };
 #pragma unroll
       for (int s = kSub - 1; s >= 0; --s) {
@@ -372,8 +376,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
           qkbuf[(2 * s + 1) * HPW * 256 + qk_slot] = dk;
           dfbuf[s * HPW * 256 + df_slot] = dfp;
           // stage H_{t-1} and D of this step, finish the previous step
-          *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + g * 80 + m * 4) = Pp[s];
-          *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + Cfg::kTile + g * 80 + m * 4) = D;
+          *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + g * Cfg::kXs + m * 4) = Pp[s];
+          *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + Cfg::kTile + g * Cfg::kXs + m * 4) = D;
           if (s < kSub - 1) drain(s + 1);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -397,7 +401,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     } else if (w < 4) {
       // dv[b][t][n][v'] = (1/c) (sum of the 16 (tile, g) partials) + w_r u; dw_r
       const int hh = w - 2, s = lane / 16, e = lane % 16;
-      const float* d = dvbuf + (s * HPW + hh) * 256 + e * 16;
+      const float* d = dvbuf + (s * HPW + hh) * 320 + e * 20;
       const f4 p = (*(const f4*)d + *(const f4*)(d + 4)) + (*(const f4*)(d + 8) + *(const f4*)(d + 12));
       const float uu = U_s[(s * HPW + hh) * 16 + e];
       dwr = fmaf(uu, V_s[(s * HPW + hh) * 16 + e], dwr);
