@@ -38,8 +38,9 @@ def test_workspace_query(m2):
     ws = m2.m2rnn_backward_workspace_bytes
     assert ws(2, 100, 5, 64, 16, 64) > 0
     assert ws(2, 100, 5, 64, 16, 64) % 256 == 0
-    # the 8-step replay states are only needed when checkpoints are sparser
-    assert ws(2, 100, 5, 64, 16, 8) < ws(2, 100, 5, 64, 16, 64)
+    # the 4-step replay states are only needed when checkpoints are sparser
+    assert ws(2, 100, 5, 64, 16, 4) < ws(2, 100, 5, 64, 16, 8) == ws(2, 100, 5, 64, 16, 64)
+    assert ws(2, 100, 5, 64, 16, 1) == ws(2, 100, 5, 64, 16, 4)
     assert ws(2, 100, 5, 32, 16, 64) == 0 and ws(2, 100, 5, 64, 16, 0) == 0 and ws(0, 100, 5, 64, 16, 64) == 0
 
 

@@ -49,7 +49,7 @@ def check(gg, gr, tol, label):
                                       (1, 9, 1, 100), (3, 1, 2, 64)])
 def test_backward_parity_small(dtype, B, T, N, ck):
     """Ragged lengths, head counts that do not fill a workgroup, and checkpoint
-    intervals below, at and above the 8-step replay window (with dH_T)."""
+    intervals below, at and above the 4-step replay window (with dH_T)."""
     x = make(B, T, N, dtype, seed=100 + B * 7 + T + N + ck, with_dy=True)
     dHT = torch.randn(B, N, 64, 16, generator=torch.Generator().manual_seed(ck))
     check(gpu_grads(x, ck, dHT), ref_grads(x, dHT), TOL[dtype], f"{dtype} B{B} T{T} N{N} ck{ck}")
