@@ -30,10 +30,10 @@ class Oracle:
         self.lib = ctypes.CDLL(lib_path)
         fwd = self.lib.m2rnn_ref_forward
         fwd.restype = ctypes.c_int
-        fwd.argtypes = [ctypes.c_int] * 5 + [_dbl_p] * 6 + [_dbl_p, _dbl_p, _dbl_p, ctypes.c_int, ctypes.c_int]
+        fwd.argtypes = [ctypes.c_int] * 5 + [_dbl_p] * 7 + [_dbl_p, _dbl_p, _dbl_p, ctypes.c_int, ctypes.c_int]
         bwd = self.lib.m2rnn_ref_backward
         bwd.restype = ctypes.c_int
-        bwd.argtypes = [ctypes.c_int] * 5 + [_dbl_p] * 6 + [_dbl_p, _dbl_p] + [_dbl_p] * 6 + [ctypes.c_int]
+        bwd.argtypes = [ctypes.c_int] * 5 + [_dbl_p] * 7 + [_dbl_p, _dbl_p] + [_dbl_p] * 7 + [ctypes.c_int]
 
     @staticmethod
     def _arr(x, shape=None):
@@ -58,31 +58,36 @@ class Oracle:
         wr = self._arr(wr, (N, V))
         return (B, T, N, K, V), (q, k, v, f, W, wr)
 
-    def forward(self, q, k, v, f, W, wr, ckpt_every=0, nthreads=0):
+    def forward(self, q, k, v, f, W, wr, ckpt_every=0, nthreads=0, H_0=None):
         """Returns (y [B,T,N,V], H_T [B,N,K,V]) or, with ckpt_every > 0,
-        (y, H_T, H_ckpt [B,N,ceil(T/ckpt_every),K,V])."""
+        (y, H_T, H_ckpt [B,N,ceil(T/ckpt_every),K,V]).  H_0 [B,N,K,V] is the
+        initial state (None: zero)."""
         (B, T, N, K, V), ins = self._inputs(q, k, v, f, W, wr)
+        h0 = None if H_0 is None else self._arr(H_0, (B, N, K, V))
         y = np.empty((B, T, N, V))
         HT = np.empty((B, N, K, V))
         ck = None
         if ckpt_every > 0:
             ck = np.empty((B, N, (T + ckpt_every - 1) // ckpt_every, K, V))
-        st = self.lib.m2rnn_ref_forward(B, T, N, K, V, *[self._p(a) for a in ins],
+        st = self.lib.m2rnn_ref_forward(B, T, N, K, V, *[self._p(a) for a in ins], self._p(h0),
                                         self._p(y), self._p(HT), self._p(ck), int(ckpt_every), int(nthreads))
         if st != 0:
             raise RuntimeError(f"m2rnn_ref_forward failed with status {st}")
         return (y, HT) if ck is None else (y, HT, ck)
 
-    def backward(self, q, k, v, f, W, wr, dy, dH_T=None, nthreads=0):
-        """Gradients of sum(y*dy) + sum(H_T*dH_T): dict with dq, dk, dv, df, dW, dwr."""
+    def backward(self, q, k, v, f, W, wr, dy, dH_T=None, nthreads=0, H_0=None):
+        """Gradients of sum(y*dy) + sum(H_T*dH_T) for the run from H_0 (None:
+        zero): dict with dq, dk, dv, df, dW, dwr and dH_0."""
         (B, T, N, K, V), ins = self._inputs(q, k, v, f, W, wr)
+        h0 = None if H_0 is None else self._arr(H_0, (B, N, K, V))
         dy = self._arr(dy, (B, T, N, V))
         dHT = None if dH_T is None else self._arr(dH_T, (B, N, K, V))
         out = dict(dq=np.empty((B, T, K)), dk=np.empty((B, T, K)), dv=np.empty((B, T, N, V)),
-                   df=np.empty((B, T, N)), dW=np.empty((N, V, V)), dwr=np.empty((N, V)))
-        st = self.lib.m2rnn_ref_backward(B, T, N, K, V, *[self._p(a) for a in ins],
+                   df=np.empty((B, T, N)), dW=np.empty((N, V, V)), dwr=np.empty((N, V)),
+                   dH_0=np.empty((B, N, K, V)))
+        st = self.lib.m2rnn_ref_backward(B, T, N, K, V, *[self._p(a) for a in ins], self._p(h0),
                                          self._p(dy), self._p(dHT),
-                                         *[self._p(out[n]) for n in ("dq", "dk", "dv", "df", "dW", "dwr")],
+                                         *[self._p(out[n]) for n in ("dq", "dk", "dv", "df", "dW", "dwr", "dH_0")],
                                          int(nthreads))
         if st != 0:
             raise RuntimeError(f"m2rnn_ref_backward failed with status {st}")

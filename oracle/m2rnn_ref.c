@@ -6,7 +6,9 @@
  * which the equations are written on the slides.
  *
  * Forward, per (batch b, value head n), slide "Write, transform, retain, and
- * read a matrix state" (paper Eqs. (10)-(12)), with H_0 = 0:
+ * read a matrix state" (paper Eqs. (10)-(12)), with H_0 = 0 as the slides fix
+ * it, or a caller-given H_0 (the same recurrence resumed from a stored state,
+ * so that a sequence can be split across calls):
  *     Z_t = tanh(H_{t-1} W + k_t v_t^T)
  *     H_t = f_t H_{t-1} + (1 - f_t) Z_t
  *     y_t = H_t^T q_t + w_r (.) v_t
@@ -24,7 +26,8 @@
  * plain chain rule on the forward equations gives
  *     dL/dk_t = D_t v_t,            dL/dv_t = D_t^T k_t + w_r (.) u_t,
  *     dL/dq_t = H_t u_t,            dL/dw_r = sum_t u_t (.) v_t,
- * with dq, dk summed over the heads that share q_t, k_t.
+ * with dq, dk summed over the heads that share q_t, k_t.  The recursion for C
+ * ends at C_0 = dL/dH_0, the gradient of a caller-given initial state.
  */
 #include "m2rnn_ref.h"
 
@@ -37,12 +40,14 @@
 typedef struct {
   int B, T, N, K, V;
   const double *q, *k, *v, *f, *W, *wr;
+  const double* H_0; /* NULL: zero initial state */
   /* forward outputs */
   double *y, *H_T, *H_ckpt;
   int ckpt_every;
   /* backward inputs / outputs */
   const double *dy, *dH_T;
   double *dv, *df;
+  double* dH_0;             /* NULL: not wanted */
   double *dq_part, *dk_part; /* [B][N][T][K] per-chain contributions */
   double *dW_part, *dwr_part; /* [B][N][V][V], [B][N][V] */
   int nthreads, tid;
@@ -108,7 +113,8 @@ static void* forward_worker(void* arg) {
   const int nck = J->ckpt_every > 0 ? (T + J->ckpt_every - 1) / J->ckpt_every : 0;
   for (int c = J->tid; c < J->B * N; c += J->nthreads) {
     const int b = c / N, n = c % N;
-    memset(H, 0, sizeof(double) * S); /* H_0 = 0 */
+    if (J->H_0) memcpy(H, J->H_0 + ((size_t)b * N + n) * S, sizeof(double) * S);
+    else memset(H, 0, sizeof(double) * S); /* H_0 = 0 */
     for (int t = 0; t < T; ++t) {
       if (J->H_ckpt && J->ckpt_every > 0 && t % J->ckpt_every == 0) {
         double* dst = J->H_ckpt + (((size_t)b * N + n) * nck + t / J->ckpt_every) * S;
@@ -148,7 +154,8 @@ static void* backward_worker(void* arg) {
     memset(dwrc, 0, sizeof(double) * V);
 
     /* recompute and keep the whole trajectory */
-    memset(Hs, 0, sizeof(double) * S);
+    if (J->H_0) memcpy(Hs, J->H_0 + ((size_t)b * N + n) * S, sizeof(double) * S);
+    else memset(Hs, 0, sizeof(double) * S);
     for (int t = 0; t < T; ++t) step(J, b, n, t, Hs + (size_t)t * S, A, Zs + (size_t)t * S, Hs + (size_t)(t + 1) * S);
 
     /* C_T = dL/dH_T (only the final-state term) */
@@ -215,6 +222,8 @@ static void* backward_worker(void* arg) {
           C[i * V + l] = ft * R[i * V + l] + a;
         }
     }
+    /* C_0 = dL/dH_0 */
+    if (J->dH_0) memcpy(J->dH_0 + ((size_t)b * N + n) * S, C, sizeof(double) * S);
   }
   free(Hs); free(Zs); free(work);
   return NULL;
@@ -252,6 +261,7 @@ static int bad_dims(int B, int T, int N, int K, int V) {
 int m2rnn_ref_forward(int B, int T, int N, int K, int V,
                       const double* q, const double* k, const double* v,
                       const double* f, const double* W, const double* wr,
+                      const double* H_0,
                       double* y, double* H_T, double* H_ckpt, int ckpt_every,
                       int nthreads) {
   if (bad_dims(B, T, N, K, V) || !q || !k || !v || !f || !W || !wr || !y || !H_T) return -1;
@@ -259,7 +269,7 @@ int m2rnn_ref_forward(int B, int T, int N, int K, int V,
   job_t J;
   memset(&J, 0, sizeof J);
   J.B = B; J.T = T; J.N = N; J.K = K; J.V = V;
-  J.q = q; J.k = k; J.v = v; J.f = f; J.W = W; J.wr = wr;
+  J.q = q; J.k = k; J.v = v; J.f = f; J.W = W; J.wr = wr; J.H_0 = H_0;
   J.y = y; J.H_T = H_T; J.H_ckpt = H_ckpt; J.ckpt_every = ckpt_every;
   return run_pool(&J, resolve_threads(nthreads, B * N), forward_worker);
 }
@@ -267,17 +277,18 @@ int m2rnn_ref_forward(int B, int T, int N, int K, int V,
 int m2rnn_ref_backward(int B, int T, int N, int K, int V,
                        const double* q, const double* k, const double* v,
                        const double* f, const double* W, const double* wr,
+                       const double* H_0,
                        const double* dy, const double* dH_T,
                        double* dq, double* dk, double* dv, double* df,
-                       double* dW, double* dwr, int nthreads) {
+                       double* dW, double* dwr, double* dH_0, int nthreads) {
   if (bad_dims(B, T, N, K, V) || !q || !k || !v || !f || !W || !wr || !dy ||
       !dq || !dk || !dv || !df || !dW || !dwr) return -1;
   const size_t part = (size_t)B * N * T * K;
   job_t J;
   memset(&J, 0, sizeof J);
   J.B = B; J.T = T; J.N = N; J.K = K; J.V = V;
-  J.q = q; J.k = k; J.v = v; J.f = f; J.W = W; J.wr = wr;
-  J.dy = dy; J.dH_T = dH_T; J.dv = dv; J.df = df;
+  J.q = q; J.k = k; J.v = v; J.f = f; J.W = W; J.wr = wr; J.H_0 = H_0;
+  J.dy = dy; J.dH_T = dH_T; J.dv = dv; J.df = df; J.dH_0 = dH_0;
   J.dq_part = (double*)malloc(sizeof(double) * part);
   J.dk_part = (double*)malloc(sizeof(double) * part);
   J.dW_part = (double*)malloc(sizeof(double) * (size_t)B * N * V * V);

@@ -25,7 +25,10 @@
  *   wr    [N][V]           value-residual weight
  *   y     [B][T][N][V]     readout of the UPDATED state H_t
  *   H_T   [B][N][K][V]     state after the last step
- *   H_ckpt[B][N][ceil(T/ckpt_every)][K][V]  H at t = j*ckpt_every (H_0 = 0)
+ *   H_0   [B][N][K][V]     initial state; NULL means zero (the slides' H_0)
+ *   H_ckpt[B][N][ceil(T/ckpt_every)][K][V]  H at t = j*ckpt_every (j = 0: H_0)
+ *   dH_0  [B][N][K][V]     gradient of the initial state (backward; NULL: not
+ *                          wanted)
  *
  * Any K >= 1, V >= 1 is accepted.  Return 0 on success, -1 on a bad
  * argument (null pointer, non-positive size).  nthreads <= 0 means "all
@@ -40,19 +43,22 @@ extern "C" {
 int m2rnn_ref_forward(int B, int T, int N, int K, int V,
                       const double* q, const double* k, const double* v,
                       const double* f, const double* W, const double* wr,
+                      const double* H_0, /* may be NULL */
                       double* y, double* H_T,
                       double* H_ckpt, int ckpt_every, /* H_ckpt may be NULL */
                       int nthreads);
 
-/* Gradients of L = sum(y * dy) + sum(H_T * dH_T).  dH_T may be NULL (zero).
+/* Gradients of L = sum(y * dy) + sum(H_T * dH_T) for the run that started
+ * from H_0 (NULL: zero).  dH_T may be NULL (zero); dH_0 may be NULL.
  * dq, dk [B][T][K] are summed over the N heads (ascending n); dW [N][V][V]
  * and dwr [N][V] over batch and time (ascending b, then descending t). */
 int m2rnn_ref_backward(int B, int T, int N, int K, int V,
                        const double* q, const double* k, const double* v,
                        const double* f, const double* W, const double* wr,
+                       const double* H_0,
                        const double* dy, const double* dH_T,
                        double* dq, double* dk, double* dv, double* df,
-                       double* dW, double* dwr,
+                       double* dW, double* dwr, double* dH_0,
                        int nthreads);
 
 #ifdef __cplusplus

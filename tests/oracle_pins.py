@@ -15,6 +15,9 @@ Sources (M2RNN paper-discussion slides, reading of arXiv:2603.14360v2):
         paper App. B, Eq. (25): f = 0, w_r = 0, q = k = e_1 turns row 1 of
         the state into the Elman RNN h_t = tanh(W^T h_{t-1} + v_t), y_t = h_t.
   [BW]  slide "Backup: the recurrent gradient needs both paths".
+  [H0]  a caller-given initial state: the recurrence of [EQ] resumed from a
+        stored state, and its gradient dL/dH_0 = C_0, where the recursion of
+        [BW] for C ends.
 """
 import numpy as np
 import torch
@@ -320,8 +323,117 @@ def pin_thread_invariance(o):
         assert np.array_equal(g1[name], g4[name]), name
 
 
+# ---------------------------------------------------------- initial-state pins
+
+def _rand_state(rng, B, N, K, V):
+    return np.tanh(rng.standard_normal((B, N, K, V)))   # a reachable state, |H| < 1
+
+
+def pin_initial_state_f_one(o):
+    """[H0] with f = 1 the state never moves: H_T = H_0 and
+    y_t = H_0^T q_t + w_r * v_t; D_t = 0, so dW = dk = 0,
+    dq_t = sum_n H_0 u_t and dH_0 = C_0 = dH_T + sum_t q_t u_t^T."""
+    rng = np.random.default_rng(RNG_SEED + 20)
+    B, T, N, K, V = 2, 5, 3, 6, 4
+    q, k, v, _, W, wr = _rand_inputs(rng, B, T, N, K, V)
+    f = np.ones((B, T, N))
+    H0 = _rand_state(rng, B, N, K, V)
+    y, HT = o.forward(q, k, v, f, W, wr, H_0=H0)
+    assert np.array_equal(HT, H0), "f=1: H_T must equal H_0"
+    _close(y, np.einsum("bnkv,btk->btnv", H0, q) + wr[None, None] * v, 1e-13, "f=1 y from H_0")
+    dy = rng.standard_normal((B, T, N, V))
+    dHT = rng.standard_normal((B, N, K, V))
+    g = o.backward(q, k, v, f, W, wr, dy, dHT, H_0=H0)
+    for name in ("dW", "dk"):
+        assert np.array_equal(g[name], np.zeros_like(g[name])), f"f=1: {name} must be 0"
+    _close(g["dq"], np.einsum("bnkv,btnv->btk", H0, dy), 1e-12, "f=1 dq from H_0")
+    _close(g["dH_0"], dHT + np.einsum("btk,btnv->bnkv", q, dy), 1e-12, "f=1 dH_0")
+
+
+def pin_initial_state_forgotten(o):
+    """[H0] with W = 0 and f = 0 the first step forgets H_0 entirely
+    (H_1 = tanh(k_1 v_1^T)): every output equals that of the H_0 = 0 run and
+    dH_0 = f_1 R_1 + D_1 W^T = 0."""
+    rng = np.random.default_rng(RNG_SEED + 21)
+    B, T, N, K, V = 2, 4, 2, 5, 3
+    q, k, v, _, _, wr = _rand_inputs(rng, B, T, N, K, V)
+    f = np.zeros((B, T, N))
+    W = np.zeros((N, V, V))
+    H0 = _rand_state(rng, B, N, K, V)
+    y0, H0T = o.forward(q, k, v, f, W, wr)
+    y1, H1T = o.forward(q, k, v, f, W, wr, H_0=H0)
+    assert np.array_equal(y0, y1) and np.array_equal(H0T, H1T)
+    dy = rng.standard_normal((B, T, N, V))
+    g = o.backward(q, k, v, f, W, wr, dy, H_0=H0)
+    assert np.array_equal(g["dH_0"], np.zeros_like(g["dH_0"])), "W=0, f=0: dH_0 must be 0"
+
+
+def pin_split_sequence(o):
+    """[H0]: a run over T steps equals a run over the first T1 steps followed by
+    one over the rest started from its H_T (the state carries everything); in
+    the backward, dH_0 of the second part is the dH_T of the first, and the two
+    parts together give the full run's gradients."""
+    rng = np.random.default_rng(RNG_SEED + 22)
+    B, T, N, K, V, T1 = 2, 9, 3, 6, 4, 4
+    q, k, v, f, W, wr = _rand_inputs(rng, B, T, N, K, V)
+    dy = rng.standard_normal((B, T, N, V))
+    dHT = rng.standard_normal((B, N, K, V))
+    a = lambda x: x[:, :T1]
+    z = lambda x: x[:, T1:]
+    y, HT = o.forward(q, k, v, f, W, wr)
+    ya, HA = o.forward(a(q), a(k), a(v), a(f), W, wr)
+    yb, HB = o.forward(z(q), z(k), z(v), z(f), W, wr, H_0=HA)
+    assert np.array_equal(np.concatenate([ya, yb], axis=1), y) and np.array_equal(HB, HT)
+    g = o.backward(q, k, v, f, W, wr, dy, dHT)
+    gb = o.backward(z(q), z(k), z(v), z(f), W, wr, z(dy), dHT, H_0=HA)
+    ga = o.backward(a(q), a(k), a(v), a(f), W, wr, a(dy), gb["dH_0"])
+    for name in ("dq", "dk", "dv", "df"):
+        _close(np.concatenate([ga[name], gb[name]], axis=1), g[name], 1e-12, f"split {name}")
+    for name in ("dW", "dwr"):
+        _close(ga[name] + gb[name], g[name], 1e-12, f"split {name}")
+    _close(ga["dH_0"], g["dH_0"], 1e-12, "split dH_0")
+
+
+def pin_finite_differences_initial_state(o):
+    """[BW] and [H0] against brute force, with a non-zero H_0: central
+    differences of L = sum(y * dy) + sum(H_T * dH_T) over every element of H_0
+    and of q, k, v, f, W, w_r (B=2, T=4, N=2, K=4, V=3)."""
+    rng = np.random.default_rng(RNG_SEED + 23)
+    B, T, N, K, V = 2, 4, 2, 4, 3
+    q, k, v, f, W, wr = _rand_inputs(rng, B, T, N, K, V, f_lo=0.05, f_hi=0.95)
+    H0 = _rand_state(rng, B, N, K, V)
+    dy = rng.standard_normal((B, T, N, V))
+    dHT = rng.standard_normal((B, N, K, V))
+    ins = [q, k, v, f, W, wr, H0]
+    g = o.backward(q, k, v, f, W, wr, dy, dHT, H_0=H0)
+
+    def loss():
+        y, HT = o.forward(*ins[:6], H_0=ins[6])
+        return float(np.sum(y * dy) + np.sum(HT * dHT))
+
+    h = 1e-6
+    for idx, name in enumerate(["dq", "dk", "dv", "df", "dW", "dwr", "dH_0"]):
+        x = ins[idx]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            mi = it.multi_index
+            orig = x[mi]
+            x[mi] = orig + h
+            lp = loss()
+            x[mi] = orig - h
+            lm = loss()
+            x[mi] = orig
+            fd[mi] = (lp - lm) / (2 * h)
+        scale = max(1.0, float(np.max(np.abs(fd))))
+        err = float(np.max(np.abs(fd - g[name])))
+        assert err <= 1e-6 * scale, f"FD {name} (H_0 != 0): max abs diff {err:.3e}"
+
+
 FORWARD_PINS = [pin_t1_closed_form, pin_f_one_forward, pin_zero_w_zero_f_forward, pin_readout_linear_in_q,
                 pin_checkpoints, pin_convex_bound, pin_permutations, pin_rnn_embedding_forward_backward]
 BACKWARD_PINS = [pin_f_one_backward, pin_zero_w_zero_f_backward, pin_finite_differences_small,
                  pin_finite_differences_full_state]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + [pin_thread_invariance]
+INITIAL_STATE_PINS = [pin_initial_state_f_one, pin_initial_state_forgotten, pin_split_sequence,
+                      pin_finite_differences_initial_state]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + INITIAL_STATE_PINS + [pin_thread_invariance]

@@ -47,6 +47,11 @@ MUTANTS = [
     ("dq_keeps_last_head", "sq += J.dq_part", "sq = J.dq_part"),
     ("dk_keeps_last_head", "sk += J.dk_part", "sk = J.dk_part"),
     ("dW_keeps_last_batch", "s += J.dW_part", "s = J.dW_part"),
+    ("forward_ignores_H0", "if (J->H_0) memcpy(H, J->H_0", "if (0) memcpy(H, J->H_0"),
+    ("backward_replay_ignores_H0", "if (J->H_0) memcpy(Hs, J->H_0", "if (0) memcpy(Hs, J->H_0"),
+    ("dH0_is_R", "if (J->dH_0) memcpy(J->dH_0 + ((size_t)b * N + n) * S, C,",
+     "if (J->dH_0) memcpy(J->dH_0 + ((size_t)b * N + n) * S, R,"),
+    ("H0_of_wrong_head", "memcpy(H, J->H_0 + ((size_t)b * N + n) * S", "memcpy(H, J->H_0 + ((size_t)b * N + (n + 1) % N) * S"),
 ]
 
 
