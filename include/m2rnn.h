@@ -5,7 +5,9 @@
  * Mishra, Tan, Stoica, Gonzalez, Dao, arXiv:2603.14360v2):
  *
  *   slide "Write, transform, retain, and read a matrix state" (paper
- *   Eqs. (10)-(12)): for every batch row b and value head n, with H_0 = 0,
+ *   Eqs. (10)-(12)): for every batch row b and value head n, from H_0 = 0
+ *   (the slides' start) or from a caller-given H_0 (the same recurrence
+ *   resumed from a stored state, so a sequence can span several calls),
  *       Z_t = tanh(H_{t-1} W + k_t v_t^T)
  *       H_t = f_t H_{t-1} + (1 - f_t) Z_t
  *       y_t = H_t^T q_t + w_r (.) v_t
@@ -30,11 +32,12 @@
  *   - Inputs q, k, v, f, W, w_r all have dtype `dtype` (M2RNN_F32 or
  *     M2RNN_BF16, bfloat16 as raw 16-bit words).  The state, every
  *     accumulation, y, H_T, checkpoints and all gradients are float32.
- *   - q, k, v, y, H_T, H_ckpt, dy, dH_T and every gradient buffer must be
- *     16-byte aligned; f, W, w_r need their element alignment.
+ *   - q, k, v, y, H_0, H_T, H_ckpt, dy, dH_T and every gradient buffer must
+ *     be 16-byte aligned; f, W, w_r need their element alignment.
  *   - Outputs are fully overwritten; they need no zeroing.
  *   - Sizes: B, T, N >= 0.  B == 0 or N == 0 is a no-op.  T == 0 leaves
- *     y empty and sets H_T = H_0 = 0.  This build supports K == 64 and
+ *     y empty and sets H_T = H_0 (zero when H_0 is NULL) and dH_0 = dH_T
+ *     (zero when dH_T is NULL).  This build supports K == 64 and
  *     V == 16 only (other values return M2RNN_ERR_UNSUPPORTED).
  *   - f is used as given (not clamped); the method expects f in [0, 1].
  *   - Errors are reported before anything is launched: a negative status is
@@ -69,16 +72,19 @@ typedef enum { M2RNN_F32 = 0, M2RNN_BF16 = 1 } m2rnn_dtype;
  *   f       [B][T][N]
  *   W       [N][V][V]     (H W)[i][j] = sum_l H[i][l] * W[n][l][j]
  *   w_r     [N][V]
+ *   H_0     [B][N][K][V]  float32 initial state, or NULL for zero
  *   y       [B][T][N][V]  float32 out, readout of the updated state H_t
  *   H_T     [B][N][K][V]  float32 out, state after step T
  *   H_ckpt  [B][N][ceil(T/ckpt_every)][K][V] float32 out, H at
- *           t = j * ckpt_every (j = 0 gives H_0 = 0); NULL with
+ *           t = j * ckpt_every (j = 0 gives H_0); NULL with
  *           ckpt_every == 0 stores none.  These are what m2rnn_backward
  *           restarts its recompute from.
+ * H_T may be the same buffer as H_0 (each state tile is read before it is
+ * overwritten); no other outputs may overlap the inputs.
  */
 int m2rnn_forward(int B, int T, int N, int K, int V, int dtype,
                   const void* q, const void* k, const void* v, const void* f,
-                  const void* W, const void* w_r,
+                  const void* W, const void* w_r, const float* H_0,
                   float* y, float* H_T, float* H_ckpt, int ckpt_every,
                   void* stream);
 
@@ -92,7 +98,8 @@ size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckp
  * "Backup: the recurrent gradient needs both paths", plus the chain rule
  * for q, k, v, w_r).
  *   q, k, v, f, W, w_r   the forward's inputs (dtype `dtype`)
- *   H_ckpt, ckpt_every   the forward's checkpoints (ckpt_every >= 1)
+ *   H_ckpt, ckpt_every   the forward's checkpoints (ckpt_every >= 1); the
+ *                        first holds the forward's H_0
  *   dy      [B][T][N][V] float32
  *   dH_T    [B][N][K][V] float32, or NULL for zero
  *   dq, dk  [B][T][K]    float32 out, summed over the N heads
@@ -100,6 +107,8 @@ size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckp
  *   df      [B][T][N]    float32 out
  *   dW      [N][V][V]    float32 out, summed over batch rows and time
  *   dw_r    [N][V]       float32 out, summed over batch rows and time
+ *   dH_0    [B][N][K][V] float32 out, dL/dH_0 (the end of the recursion for
+ *                        C), or NULL when not wanted
  *   workspace            device buffer of at least
  *                        m2rnn_backward_workspace_bytes(...) bytes,
  *                        16-byte aligned; contents on entry are ignored
@@ -110,8 +119,21 @@ int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
                    const float* H_ckpt, int ckpt_every,
                    const float* dy, const float* dH_T,
                    float* dq, float* dk, float* dv, float* df,
-                   float* dW, float* dw_r,
+                   float* dW, float* dw_r, float* dH_0,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One token of the recurrence for every (b, n), state held by the caller
+ * (decoding): the forward of slide "Write, transform, retain, and read a
+ * matrix state" for T = 1 from H, with H overwritten by the new state.
+ *   q, k  [B][K]; v [B][N][V]; f [B][N]; W [N][V][V]; w_r [N][V] (dtype)
+ *   H     [B][N][K][V] float32 in/out
+ *   y     [B][N][V]    float32 out
+ * Same as m2rnn_forward with T = 1, H_0 = H_T = H and no checkpoints.
+ */
+int m2rnn_decode(int B, int N, int K, int V, int dtype,
+                 const void* q, const void* k, const void* v, const void* f,
+                 const void* W, const void* w_r, float* H, float* y, void* stream);
 
 /* Message for the last non-OK status on the calling thread ("" if none). */
 const char* m2rnn_last_error(void);

@@ -87,3 +87,12 @@ def make_inputs(B, T, N, K=K_DIM, V=V_DIM, dtype="f32", f_mu=2.0, seed=0, with_d
 def make_workload(w: Workload, seed=0, with_dy=None):
     return make_inputs(w.B, w.T, w.N, w.K, w.V, w.dtype, w.f_mu, seed,
                        w.backward if with_dy is None else with_dy)
+
+
+def make_state(B, N, K=K_DIM, V=V_DIM, seed=0):
+    """A seeded float32 state [B,N,K,V] drawn uniformly from [-1, 1) (the range
+    every state takes when f lies in [0, 1]): an initial state H_0, or a
+    gradient dH_T, for the resumable scan."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed))
+    return (torch.rand(B, N, K, V, generator=g, dtype=torch.float32) * 2.0 - 1.0).contiguous()

@@ -9,6 +9,8 @@ is no CPU fallback.
     y, H_T = m2.forward(q, k, v, f, W, w_r)                    # H_0 = 0
     y, H_T, H_ckpt = m2.forward(q, k, v, f, W, w_r, ckpt_every=64)
     grads = m2.backward(q, k, v, f, W, w_r, H_ckpt, 64, dy)     # dict
+    y2, H_T2 = m2.forward(q2, k2, v2, f2, W, w_r, H_0=H_T)     # resume
+    y_t = m2.decode(q_t, k_t, v_t, f_t, W, w_r, H)              # one token, H updated
 
 Shapes (K = 64, V = 16): q, k [B,T,K]; v [B,T,N,V]; f [B,T,N]; W [N,V,V];
 w_r [N,V]; all six float32 or all six bfloat16, contiguous, on one GPU.
@@ -33,17 +35,19 @@ M2RNN_F32 = 0
 M2RNN_BF16 = 1
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m non_linear_matrix_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; run `python non_linear_matrix_amd/build.py`")
 lib = ctypes.CDLL(LIB_PATH)
 
 _i = ctypes.c_int
 _p = ctypes.c_void_p
 lib.m2rnn_forward.restype = _i
-lib.m2rnn_forward.argtypes = [_i] * 6 + [_p] * 6 + [_p, _p, _p, _i, _p]
+lib.m2rnn_forward.argtypes = [_i] * 6 + [_p] * 7 + [_p, _p, _p, _i, _p]
 lib.m2rnn_backward_workspace_bytes.restype = ctypes.c_size_t
 lib.m2rnn_backward_workspace_bytes.argtypes = [_i] * 6
 lib.m2rnn_backward.restype = _i
-lib.m2rnn_backward.argtypes = [_i] * 6 + [_p] * 6 + [_p, _i] + [_p, _p] + [_p] * 6 + [_p, ctypes.c_size_t, _p]
+lib.m2rnn_backward.argtypes = [_i] * 6 + [_p] * 6 + [_p, _i] + [_p, _p] + [_p] * 7 + [_p, ctypes.c_size_t, _p]
+lib.m2rnn_decode.restype = _i
+lib.m2rnn_decode.argtypes = [_i] * 5 + [_p] * 6 + [_p, _p, _p]
 lib.m2rnn_last_error.restype = ctypes.c_char_p
 lib.m2rnn_last_error.argtypes = []
 
@@ -81,16 +85,21 @@ def _sizes(q, v):
     return B, T, N, Kq, Vv
 
 
-def m2rnn_forward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, y, H_T, H_ckpt, ckpt_every, stream):
+def m2rnn_forward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_0, y, H_T, H_ckpt, ckpt_every, stream):
     """Raw C-ABI call with ctypes pointers; returns the status code."""
-    return lib.m2rnn_forward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, y, H_T, H_ckpt, ckpt_every, stream)
+    return lib.m2rnn_forward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_0, y, H_T, H_ckpt, ckpt_every, stream)
 
 
 def m2rnn_backward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_ckpt, ckpt_every, dy, dH_T,
-                   dq, dk, dv, df, dW, dw_r, workspace, workspace_bytes, stream):
+                   dq, dk, dv, df, dW, dw_r, dH_0, workspace, workspace_bytes, stream):
     """Raw C-ABI call with ctypes pointers; returns the status code."""
     return lib.m2rnn_backward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_ckpt, ckpt_every, dy, dH_T,
-                              dq, dk, dv, df, dW, dw_r, workspace, workspace_bytes, stream)
+                              dq, dk, dv, df, dW, dw_r, dH_0, workspace, workspace_bytes, stream)
+
+
+def m2rnn_decode(B, N, K_, V_, dtype, q, k, v, f, W, w_r, H, y, stream):
+    """Raw C-ABI call with ctypes pointers; returns the status code."""
+    return lib.m2rnn_decode(B, N, K_, V_, dtype, q, k, v, f, W, w_r, H, y, stream)
 
 
 def m2rnn_backward_workspace_bytes(B, T, N, K_=K, V_=V, ckpt_every=64):
@@ -101,10 +110,11 @@ def m2rnn_last_error():
     return lib.m2rnn_last_error().decode()
 
 
-def forward(q, k, v, f, W, w_r, ckpt_every=0, out=None):
+def forward(q, k, v, f, W, w_r, ckpt_every=0, out=None, H_0=None):
     """y [B,T,N,V], H_T [B,N,K,V] (float32) and, if ckpt_every > 0,
     H_ckpt [B,N,ceil(T/ckpt_every),K,V].  `out` may pass preallocated
-    (y, H_T[, H_ckpt]) tensors."""
+    (y, H_T[, H_ckpt]) tensors; H_0 [B,N,K,V] float32 is the initial state
+    (None: zero) and may be the same tensor as H_T."""
     B, T, N, Kq, Vv = _sizes(q, v)
     dev = q.device
     if out is None:
@@ -117,19 +127,22 @@ def forward(q, k, v, f, W, w_r, ckpt_every=0, out=None):
         y, H_T = out[0], out[1]
         H_ck = out[2] if len(out) > 2 else None
     _check(lib.m2rnn_forward(B, T, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W),
-                             _ptr(w_r), _ptr(y), _ptr(H_T), _ptr(H_ck), int(ckpt_every), _stream(dev)))
+                             _ptr(w_r), _ptr(H_0), _ptr(y), _ptr(H_T), _ptr(H_ck), int(ckpt_every), _stream(dev)))
     return (y, H_T) if H_ck is None else (y, H_T, H_ck)
 
 
-def backward(q, k, v, f, W, w_r, H_ckpt, ckpt_every, dy, dH_T=None, out=None, workspace=None):
+def backward(q, k, v, f, W, w_r, H_ckpt, ckpt_every, dy, dH_T=None, out=None, workspace=None, want_dH_0=False):
     """Gradients of sum(y*dy) + sum(H_T*dH_T): dict dq, dk [B,T,K]; dv [B,T,N,V];
-    df [B,T,N]; dW [N,V,V]; dw_r [N,V] (float32)."""
+    df [B,T,N]; dW [N,V,V]; dw_r [N,V] and, with want_dH_0 (or a "dH_0"
+    entry in `out`), dH_0 [B,N,K,V] (float32)."""
     B, T, N, Kq, Vv = _sizes(q, v)
     dev = q.device
     if out is None:
         out = dict(dq=torch.empty((B, T, Kq), device=dev), dk=torch.empty((B, T, Kq), device=dev),
                    dv=torch.empty((B, T, N, Vv), device=dev), df=torch.empty((B, T, N), device=dev),
                    dW=torch.empty((N, Vv, Vv), device=dev), dw_r=torch.empty((N, Vv), device=dev))
+        if want_dH_0:
+            out["dH_0"] = torch.empty((B, N, Kq, Vv), device=dev)
     nbytes = int(lib.m2rnn_backward_workspace_bytes(B, T, N, Kq, Vv, int(ckpt_every)))
     if workspace is None and nbytes > 0:
         workspace = torch.empty((nbytes,), device=dev, dtype=torch.uint8)
@@ -137,5 +150,18 @@ def backward(q, k, v, f, W, w_r, H_ckpt, ckpt_every, dy, dH_T=None, out=None, wo
     _check(lib.m2rnn_backward(B, T, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W),
                               _ptr(w_r), _ptr(H_ckpt), int(ckpt_every), _ptr(dy), _ptr(dH_T),
                               _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["df"]),
-                              _ptr(out["dW"]), _ptr(out["dw_r"]), _ptr(workspace), wbytes, _stream(dev)))
+                              _ptr(out["dW"]), _ptr(out["dw_r"]), _ptr(out.get("dH_0")), _ptr(workspace), wbytes,
+                              _stream(dev)))
     return out
+
+
+def decode(q, k, v, f, W, w_r, H, y=None):
+    """One token for every (b, n): q, k [B,K]; v [B,N,V]; f [B,N]; H [B,N,K,V]
+    float32, advanced in place.  Returns y [B,N,V] float32."""
+    B, Kq = q.shape
+    N, Vv = v.shape[1], v.shape[2]
+    if y is None:
+        y = torch.empty((B, N, Vv), device=q.device, dtype=torch.float32)
+    _check(lib.m2rnn_decode(B, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r),
+                            _ptr(H), _ptr(y), _stream(q.device)))
+    return y

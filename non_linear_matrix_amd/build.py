@@ -1,6 +1,8 @@
 """Build libm2rnn.so (HIP for gfx950) in-tree with hipcc.
 
-    python -m non_linear_matrix_amd.build
+    python non_linear_matrix_amd/build.py
+
+(Run it as a script: importing the package loads the library this builds.)
 """
 import glob
 import os

@@ -52,7 +52,7 @@ extern "C" const char* m2rnn_last_error(void) { return g_err; }
 
 extern "C" int m2rnn_forward(int B, int T, int N, int K, int V, int dtype,
                              const void* q, const void* k, const void* v, const void* f,
-                             const void* W, const void* w_r,
+                             const void* W, const void* w_r, const float* H_0,
                              float* y, float* H_T, float* H_ckpt, int ckpt_every,
                              void* stream) {
   g_err[0] = 0;
@@ -68,17 +68,19 @@ extern "C" int m2rnn_forward(int B, int T, int N, int K, int V, int dtype,
       (st = need(w_r, "w_r", (long long)N * V * (BN > 0), es)) || (st = need(y, "y", BTN * V, 16)) ||
       (st = need(H_T, "H_T", BN * K * V, 16)))
     return st;
+  if (H_0 && !aligned(H_0, 16)) return fail(M2RNN_ERR_INVALID_ARG, "H_0 must be 16-byte aligned");
   const int nck = ckpt_every > 0 ? (T + ckpt_every - 1) / ckpt_every : 0;
   if (ckpt_every > 0 && (st = need(H_ckpt, "H_ckpt", BN * nck * K * V, 16))) return st;
   if (BN == 0) return M2RNN_OK;
 
   hipStream_t s = (hipStream_t)stream;
-  if (T == 0) {  // H_T = H_0 = 0; y is empty
-    hipError_t e = m2rnn::launch_fill_zero(H_T, (size_t)BN * K * V, s);
-    return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "zero fill: %s", hipGetErrorString(e));
+  if (T == 0) {  // H_T = H_0; y is empty
+    hipError_t e = H_0 ? m2rnn::launch_copy(H_T, H_0, (size_t)BN * K * V, s)
+                       : m2rnn::launch_fill_zero(H_T, (size_t)BN * K * V, s);
+    return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "H_T = H_0: %s", hipGetErrorString(e));
   }
   m2rnn::FwdArgs a;
-  a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.wr = w_r;
+  a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.wr = w_r; a.H_0 = H_0;
   a.y = y; a.H_T = H_T; a.H_ckpt = ckpt_every > 0 ? H_ckpt : nullptr;
   a.B = B; a.T = T; a.N = N; a.ckpt_every = ckpt_every; a.nck = nck;
   hipError_t e = m2rnn::launch_forward(a, dtype, s);
@@ -97,7 +99,7 @@ extern "C" int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
                               const void* q, const void* k, const void* v, const void* f,
                               const void* W, const void* w_r, const float* H_ckpt, int ckpt_every,
                               const float* dy, const float* dH_T, float* dq, float* dk, float* dv,
-                              float* df, float* dW, float* dw_r, void* workspace,
+                              float* df, float* dW, float* dw_r, float* dH_0, void* workspace,
                               size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   int st = check_sizes(B, T, N, K, V, dtype);
@@ -114,10 +116,14 @@ extern "C" int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
       (st = need(dw_r, "dw_r", (long long)N * V, 16)))
     return st;
   if (dH_T && !aligned(dH_T, 16)) return fail(M2RNN_ERR_INVALID_ARG, "dH_T must be 16-byte aligned");
+  if (dH_0 && !aligned(dH_0, 16)) return fail(M2RNN_ERR_INVALID_ARG, "dH_0 must be 16-byte aligned");
   hipStream_t s = (hipStream_t)stream;
   if (BTN == 0) {
-    // nothing flows back: dq, dk (if any) and the summed dW, dw_r are zero
+    // nothing flows back through the steps: dq, dk (if any) and the summed
+    // dW, dw_r are zero, and dH_0 = dH_T
     hipError_t e = hipSuccess;
+    if (dH_0 && BN > 0)
+      e = dH_T ? m2rnn::launch_copy(dH_0, dH_T, (size_t)BN * K * V, s) : m2rnn::launch_fill_zero(dH_0, (size_t)BN * K * V, s);
     if (BT > 0) {
       if (e == hipSuccess) e = m2rnn::launch_fill_zero(dq, (size_t)BT * K, s);
       if (e == hipSuccess) e = m2rnn::launch_fill_zero(dk, (size_t)BT * K, s);
@@ -140,7 +146,7 @@ extern "C" int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
   m2rnn::BwdArgs a;
   a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.wr = w_r;
   a.H_ckpt = H_ckpt; a.dy = dy; a.dH_T = dH_T;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.df = df; a.dW = dW; a.dw_r = dw_r;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.df = df; a.dW = dW; a.dw_r = dw_r; a.dH_0 = dH_0;
   a.ws_dqk = ws + o_dqk; a.ws_dW = ws + o_dW; a.ws_dwr = ws + o_dwr;
   a.B = B; a.T = T; a.N = N;
   a.ckpt_every = ckpt_every; a.nck = nck; a.ngroups = ng;
@@ -154,4 +160,13 @@ extern "C" int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
   hipError_t e = m2rnn::launch_backward(a, rp, dtype, s);
   if (e != hipSuccess) return fail(M2RNN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
   return M2RNN_OK;
+}
+
+extern "C" int m2rnn_decode(int B, int N, int K, int V, int dtype, const void* q, const void* k, const void* v,
+                            const void* f, const void* W, const void* w_r, float* H, float* y, void* stream) {
+  g_err[0] = 0;
+  int st = check_sizes(B, 1, N, K, V, dtype);
+  if (st) return st;
+  if ((long long)B * N > 0 && !H) return fail(M2RNN_ERR_INVALID_ARG, "H must not be NULL");
+  return m2rnn_forward(B, 1, N, K, V, dtype, q, k, v, f, W, w_r, H, y, H, nullptr, 0, stream);
 }

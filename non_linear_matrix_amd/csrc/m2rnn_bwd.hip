@@ -428,6 +428,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     float* dst = a.ws_dW + (head * 4 + j) * 256;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[(4 * g + i) * 16 + m] = dW[i] * kInvScale;
+    // the recursion for C ends at C_0 = dL/dH_0
+    if (a.dH_0) *(f4*)(a.dH_0 + head * 1024 + kk * 16 + 4 * g) = C;
   }
   // dw_r: the dv waves hold one partial per (step slot, head, v'); sum the
   // step slots in a fixed order

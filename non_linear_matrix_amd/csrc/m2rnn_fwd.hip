@@ -177,9 +177,12 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
   f4 P[TPW];
 #pragma unroll
   for (int j = 0; j < TPW; ++j) P[j] = f4{0.f, 0.f, 0.f, 0.f};
-  if constexpr (DENSE) {
-    if (live) {
-      const float* src = a.H_src + (((size_t)b * a.N + n) * a.src_nck + tb / a.src_every) * 1024;
+  if (live) {
+    // the restart state: a stored checkpoint (replay) or the caller's H_0
+    const float* src = nullptr;
+    if constexpr (DENSE) src = a.H_src + (((size_t)b * a.N + n) * a.src_nck + tb / a.src_every) * 1024;
+    else if (a.H_0) src = a.H_0 + ((size_t)b * a.N + n) * 1024;
+    if (src) {
 #pragma unroll
       for (int j = 0; j < TPW; ++j) P[j] = *(const f4*)(src + (16 * (j0 + j) + m) * 16 + 4 * g) * kScale;
     }
@@ -317,6 +320,18 @@ hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream) {
   size_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
+
+__global__ void copy_kernel(float* dst, const float* src, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) dst[i] = src[i];
+}
+
+hipError_t launch_copy(float* dst, const float* src, size_t n, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, dst, src, n);
   return hipGetLastError();
 }
 

@@ -8,6 +8,7 @@ namespace m2rnn {
 
 struct FwdArgs {
   const void *q, *k, *v, *f, *W, *wr;
+  const float* H_0 = nullptr;  // initial state, nullptr for zero
   float *y, *H_T, *H_ckpt;
   int B, T, N;
   int ckpt_every;  // > 0 when H_ckpt != nullptr
@@ -26,6 +27,7 @@ struct BwdArgs {
   const void *q, *k, *v, *f, *W, *wr;
   const float *H_ckpt, *dy, *dH_T;  // H_ckpt: states every ckpt_every (<= sub-step count) steps
   float *dq, *dk, *dv, *df, *dW, *dw_r;
+  float* dH_0;                      // nullptr when not wanted
   float *ws_dqk, *ws_dW, *ws_dwr;   // workspace regions
   int B, T, N;
   int ckpt_every, nck, ngroups;
@@ -42,5 +44,7 @@ hipError_t launch_backward(const BwdArgs& a, const FwdArgs& replay, int dtype, h
 
 // Zero `n` floats with a plain fill kernel (graph-capture friendly).
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
+// dst[i] = src[i] for `n` floats with a plain copy kernel; dst == src is allowed.
+hipError_t launch_copy(float* dst, const float* src, size_t n, hipStream_t stream);
 
 }  // namespace m2rnn

@@ -24,7 +24,7 @@ def m2():
 
 
 def test_header_declares_the_entry_points():
-    assert declared() == ["m2rnn_backward", "m2rnn_backward_workspace_bytes", "m2rnn_forward",
+    assert declared() == ["m2rnn_backward", "m2rnn_backward_workspace_bytes", "m2rnn_decode", "m2rnn_forward",
                           "m2rnn_last_error"]
 
 
@@ -48,22 +48,27 @@ def test_argument_errors_without_launch(m2):
     dummy = ctypes.c_void_p(256)   # never dereferenced: validation fails first
     args6 = [dummy] * 6
     f = m2.lib.m2rnn_forward
-    assert f(1, 4, 2, 32, 16, 0, *args6, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert f(1, 4, 2, 32, 16, 0, *args6, None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
     assert "K=64" in m2.m2rnn_last_error()
-    assert f(1, 4, 2, 64, 8, 0, *args6, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
-    assert f(1, 4, 2, 64, 16, 5, *args6, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
-    assert f(-1, 4, 2, 64, 16, 0, *args6, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
-    assert f(1, 4, 2, 64, 16, 0, None, *args6[1:], dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 8, 0, *args6, None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert f(1, 4, 2, 64, 16, 5, *args6, None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(-1, 4, 2, 64, 16, 0, *args6, None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 16, 0, None, *args6[1:], None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
     assert "q" in m2.m2rnn_last_error()
     odd = ctypes.c_void_p(256 + 4)   # y must be 16-byte aligned
-    assert f(1, 4, 2, 64, 16, 0, *args6, odd, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
-    assert f(1, 4, 2, 64, 16, 0, *args6, dummy, dummy, dummy, 0, None) == m2.M2RNN_ERR_INVALID_ARG
-    assert f(1, 4, 2, 64, 16, 0, *args6, dummy, dummy, None, -3, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 16, 0, *args6, None, odd, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 16, 0, *args6, None, dummy, dummy, dummy, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 16, 0, *args6, None, dummy, dummy, None, -3, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 16, 0, *args6, odd, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert "H_0" in m2.m2rnn_last_error()
+    d = m2.lib.m2rnn_decode
+    assert d(1, 2, 64, 16, 0, *args6, None, dummy, None) == m2.M2RNN_ERR_INVALID_ARG   # H is required
+    assert d(1, 2, 32, 16, 0, *args6, dummy, dummy, None) == m2.M2RNN_ERR_UNSUPPORTED
     b = m2.lib.m2rnn_backward
     grads = [dummy] * 6
-    assert b(1, 4, 2, 64, 16, 0, *args6, dummy, 0, dummy, None, *grads, dummy, 1 << 30, None) == \
+    assert b(1, 4, 2, 64, 16, 0, *args6, dummy, 0, dummy, None, *grads, None, dummy, 1 << 30, None) == \
         m2.M2RNN_ERR_INVALID_ARG          # ckpt_every must be >= 1
-    assert b(1, 4, 2, 64, 16, 0, *args6, dummy, 64, dummy, None, *grads, dummy, 16, None) == \
+    assert b(1, 4, 2, 64, 16, 0, *args6, dummy, 64, dummy, None, *grads, None, dummy, 16, None) == \
         m2.M2RNN_ERR_WORKSPACE            # too small
     assert "workspace" in m2.m2rnn_last_error()
-    assert b(1, 4, 2, 64, 16, 0, *args6, dummy, 64, dummy, None, *grads, None, 0, None) == m2.M2RNN_ERR_WORKSPACE
+    assert b(1, 4, 2, 64, 16, 0, *args6, dummy, 64, dummy, None, *grads, None, None, 0, None) == m2.M2RNN_ERR_WORKSPACE

@@ -130,18 +130,18 @@ def test_forward_rejects_bad_arguments():
     P = m2._ptr
     s = m2._stream(dev)
     args = [P(x[n]) for n in ("q", "k", "v", "f", "W", "wr")]
-    assert m2.m2rnn_forward(1, 4, 2, 32, 16, 0, *args, P(y), P(H), None, 0, s) == m2.M2RNN_ERR_UNSUPPORTED
-    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 7, *args, P(y), P(H), None, 0, s) == m2.M2RNN_ERR_INVALID_ARG
-    assert m2.m2rnn_forward(-1, 4, 2, 64, 16, 0, *args, P(y), P(H), None, 0, s) == m2.M2RNN_ERR_INVALID_ARG
+    assert m2.m2rnn_forward(1, 4, 2, 32, 16, 0, *args, None, P(y), P(H), None, 0, s) == m2.M2RNN_ERR_UNSUPPORTED
+    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 7, *args, None, P(y), P(H), None, 0, s) == m2.M2RNN_ERR_INVALID_ARG
+    assert m2.m2rnn_forward(-1, 4, 2, 64, 16, 0, *args, None, P(y), P(H), None, 0, s) == m2.M2RNN_ERR_INVALID_ARG
     bad = list(args)
     bad[0] = None
-    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 0, *bad, P(y), P(H), None, 0, s) == m2.M2RNN_ERR_INVALID_ARG
+    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 0, *bad, None, P(y), P(H), None, 0, s) == m2.M2RNN_ERR_INVALID_ARG
     assert "q" in m2.m2rnn_last_error()
     mis = torch.empty(1, 4, 2, 16 + 1, device=dev)
-    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 0, *args, ctypes.c_void_p(mis.data_ptr() + 4), P(H), None, 0,
+    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 0, *args, None, ctypes.c_void_p(mis.data_ptr() + 4), P(H), None, 0,
                             s) == m2.M2RNN_ERR_INVALID_ARG
     # checkpoint pointer without an interval
-    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 0, *args, P(y), P(H), P(H), 0, s) == m2.M2RNN_ERR_INVALID_ARG
+    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 0, *args, None, P(y), P(H), P(H), 0, s) == m2.M2RNN_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("name,chains", [
