@@ -85,26 +85,33 @@ struct BwdStage {
   static constexpr int kF = kSub * HPW;        // lanes carrying f
   raw x;
   f4 uu;
-  float ff;
+  TIn fr;     // f as stored (converted when staged, so nothing waits on the load early)
+  bool fset;  // f of a real step (else the identity step's f = 1)
 
+  // Addresses are a wave-uniform base for the sub-chunk plus a small per-lane
+  // offset, so no 64-bit per-lane pointer stays live across the loop.
   __device__ void load(const BwdArgs& a, int w, int lane, int b, int n0, int t0, int len) {
     x = Vec4<TIn>::zero();
+    uu = f4{0.f, 0.f, 0.f, 0.f};
+    fset = false;
     if (w >= 6) {
-      const TIn* src = (const TIn*)(w == 7 ? a.k : a.q) + ((size_t)b * a.T + t0) * 64;
-      if (lane < len * 16) x = Vec4<TIn>::load(src + lane * 4);
+      const TIn* base = (const TIn*)(w == 7 ? a.k : a.q) + ((size_t)b * a.T + t0) * 64;
+      if (lane < len * 16) x = Vec4<TIn>::load(base + lane * 4);
     } else if (w == 5) {
-      uu = f4{0.f, 0.f, 0.f, 0.f};
-      ff = 1.0f;
+      const size_t row0 = ((size_t)b * a.T + t0) * a.N + n0;   // (b, t0, n0)
       if (lane < kVU) {
         const int t = lane / (HPW * 4), h = (lane / 4) % HPW, c4 = lane % 4;
         if (t < len && n0 + h < a.N) {
-          const size_t off = (((size_t)b * a.T + t0 + t) * a.N + n0 + h) * 16 + 4 * c4;
-          x = Vec4<TIn>::load((const TIn*)a.v + off);
-          uu = *(const f4*)(a.dy + off);
+          const unsigned off = (unsigned)(t * a.N + h) * 16u + 4u * c4;
+          x = Vec4<TIn>::load((const TIn*)a.v + row0 * 16 + off);
+          uu = *(const f4*)(a.dy + row0 * 16 + off);
         }
       } else if (lane < kVU + kF) {
         const int t = (lane - kVU) / HPW, h = (lane - kVU) % HPW;
-        if (t < len && n0 + h < a.N) ff = to_f32(((const TIn*)a.f)[((size_t)b * a.T + t0 + t) * a.N + n0 + h]);
+        if (t < len && n0 + h < a.N) {
+          fr = ((const TIn*)a.f)[row0 + (unsigned)(t * a.N + h)];
+          fset = true;
+        }
       }
     }
   }
@@ -131,6 +138,7 @@ struct BwdStage {
         *(f4*)(V_s + lane * 4) = Vec4<TIn>::to_f4(x);
         *(f4*)(U_s + lane * 4) = uu;
       } else if (lane < kVU + kF) {
+        const float ff = fset ? to_f32(fr) : 1.0f;
         const float gg = 1.0f - ff;
         *(f4*)(F_s + (lane - kVU) * 4) = f4{ff, kScale * gg, -2.0f * kScale * gg, gg};
       }
@@ -282,24 +290,28 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     for (int s = 0; s < 2 * kSub; ++s) qkbuf[s * HPW * 256 + qk_slot] = 0.f;
   }
 
-  BwdStage<TIn, HPW> st;
   {
+    BwdStage<TIn, HPW> st;
     const int t0 = (ns - 1) * L;
     st.load(a, w, lane, b, n0, t0, min(L, a.T - t0));
     st.store(smem, w, lane);
   }
-  f4 Pnext = {0.f, 0.f, 0.f, 0.f};
-  if (live) Pnext = *(const f4*)(Hs + (size_t)(ns - 1) * 1024) * kScale;
+  // the next restart state, prefetched one sub-chunk ahead and scaled by c
+  // only when it is used (so nothing waits on the load early)
+  f4 Hnext = {0.f, 0.f, 0.f, 0.f};
+  if (live) Hnext = *(const f4*)(Hs + (size_t)(ns - 1) * 1024);
   __syncthreads();
 
   for (int sb = ns - 1, it = 0; sb >= 0; --sb, ++it) {
     const int t0 = sb * L, len = min(L, a.T - t0);
-    const bool more = sb > 0;
-    f4 P = Pnext;
-    if (more) {
-      st.load(a, w, lane, b, n0, t0 - L, L);
-      if (live) Pnext = *(const f4*)(Hs + (size_t)(sb - 1) * 1024) * kScale;
-    }
+    f4 P = Hnext * kScale;
+    // prefetch the next sub-chunk (registers live for this iteration only).
+    // The last iteration fetches sub-chunk 0 again and stages it into the
+    // buffer no one reads: no branch, so nothing in flight gets copied.
+    const int sn = sb > 0 ? sb - 1 : 0;
+    BwdStage<TIn, HPW> st;
+    st.load(a, w, lane, b, n0, sn * L, min(L, a.T - sn * L));
+    if (live) Hnext = *(const f4*)(Hs + (size_t)sn * 1024);
     const float* buf = smem + (it & 1) * Cfg::kBuf;
     const float* K_s = buf;
     const float* Q_s = K_s + kSub * 64;
@@ -420,7 +432,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       const int s = s0 + (g & 1), hh = g >> 1;
       if (m == 0 && s < len && n0 + hh < a.N) a.df[((size_t)b * a.T + t0 + s) * a.N + n0 + hh] = tot;
     }
-    if (more) st.store(smem + ((it + 1) & 1) * Cfg::kBuf, w, lane);
+    st.store(smem + ((it + 1) & 1) * Cfg::kBuf, w, lane);
     __syncthreads();
   }
 
