@@ -75,73 +75,110 @@ struct BwdCfg {
 };
 
 // Staging of one sub-chunk (kSub steps from t0, the first len of them real)
-// through registers into an LDS buffer.  Wave 7 carries k, wave 6 q (lane =
-// 4 consecutive elements of one step), wave 5 v and u (lanes 0..31) and f
-// (lanes 32..39).  Steps past len are staged as f = 1, q = k = v = u = 0.
-template <typename TIn, int HPW>
+// through registers into an LDS buffer.  The last NL waves load: thread u of
+// them fetches one 16-byte chunk of q, k, v or u = dy, and one f value.  The
+// load path is the same straight line for every loading thread (addresses of
+// steps past len, of a missing head, and of idle threads are clamped to valid
+// data), so no register of an in-flight load is ever merged or copied and
+// nothing waits on the loads before they are staged.  Steps past len are
+// staged as f = 1, q = k = v = u = 0.
+template <typename TIn, int HPW, int NWAVES>
 struct BwdStage {
-  typedef typename Vec4<TIn>::raw raw;
-  static constexpr int kVU = kSub * HPW * 4;   // lanes carrying v, u
-  static constexpr int kF = kSub * HPW;        // lanes carrying f
-  raw x;
-  f4 uu;
-  TIn fr;     // f as stored (converted when staged, so nothing waits on the load early)
-  bool fset;  // f of a real step (else the identity step's f = 1)
+  static constexpr int EPC = 16 / (int)sizeof(TIn);          // elements per chunk
+  static constexpr int nQ = kSub * 64 / EPC;                  // q chunks (and k chunks)
+  static constexpr int nV = kSub * HPW * 16 / EPC;            // v chunks
+  static constexpr int nU = kSub * HPW * 16 / 4;              // dy chunks (fp32)
+  static constexpr int nChunks = 2 * nQ + nV + nU;
+  static constexpr int NL = (nChunks + 63) / 64;              // loading waves
+  static_assert(NL <= NWAVES && kSub * HPW <= 64 * NL, "staging threads");
+  u32x4 r;
+  TIn fr;
 
-  // Addresses are a wave-uniform base for the sub-chunk plus a small per-lane
-  // offset, so no 64-bit per-lane pointer stays live across the loop.
-  __device__ void load(const BwdArgs& a, int w, int lane, int b, int n0, int t0, int len) {
-    x = Vec4<TIn>::zero();
-    uu = f4{0.f, 0.f, 0.f, 0.f};
-    fset = false;
-    if (w >= 6) {
-      const TIn* base = (const TIn*)(w == 7 ? a.k : a.q) + ((size_t)b * a.T + t0) * 64;
-      if (lane < len * 16) x = Vec4<TIn>::load(base + lane * 4);
-    } else if (w == 5) {
-      const size_t row0 = ((size_t)b * a.T + t0) * a.N + n0;   // (b, t0, n0)
-      if (lane < kVU) {
-        const int t = lane / (HPW * 4), h = (lane / 4) % HPW, c4 = lane % 4;
-        if (t < len && n0 + h < a.N) {
-          const unsigned off = (unsigned)(t * a.N + h) * 16u + 4u * c4;
-          x = Vec4<TIn>::load((const TIn*)a.v + row0 * 16 + off);
-          uu = *(const f4*)(a.dy + row0 * 16 + off);
-        }
-      } else if (lane < kVU + kF) {
-        const int t = (lane - kVU) / HPW, h = (lane - kVU) % HPW;
-        if (t < len && n0 + h < a.N) {
-          fr = ((const TIn*)a.f)[row0 + (unsigned)(t * a.N + h)];
-          fset = true;
-        }
-      }
-    }
+  // chunk u -> kind (0 q, 1 k, 2 v, 3 dy, 4 idle), step t, element offset e0
+  // within the step's row (q, k: of 64; v, dy: of the HPW heads' 16 each)
+  __device__ static void decode(int u, int& kind, int& t, int& e0) {
+    if (u < nQ) { kind = 0; t = u / (64 / EPC); e0 = (u % (64 / EPC)) * EPC; }
+    else if (u < 2 * nQ) { u -= nQ; kind = 1; t = u / (64 / EPC); e0 = (u % (64 / EPC)) * EPC; }
+    else if (u < 2 * nQ + nV) { u -= 2 * nQ; kind = 2; t = u / (HPW * 16 / EPC); e0 = (u % (HPW * 16 / EPC)) * EPC; }
+    else if (u < nChunks) { u -= 2 * nQ + nV; kind = 3; t = u / (HPW * 4); e0 = (u % (HPW * 4)) * 4; }
+    else { kind = 4; t = 0; e0 = 0; }
   }
 
-  __device__ void store(float* buf, int w, int lane) const {
+  __device__ void load(const BwdArgs& a, int w, int lane, int b, int n0, int t0, int len) {
+    if (w < NWAVES - NL) return;
+    const int u = (w - (NWAVES - NL)) * 64 + lane;
+    int kind, t, e0;
+    decode(u, kind, t, e0);
+    const bool ok = t < len && (kind < 2 || n0 + e0 / 16 < a.N);
+    const int tt = ok ? t : 0;
+    const int ee = ok ? e0 : e0 % 16;                     // a missing head reads head n0
+    const size_t row = (size_t)b * a.T + t0 + tt;         // (b, t0 + tt)
+    const char* p;
+    if (kind == 0) p = (const char*)((const TIn*)a.q + row * 64 + ee);
+    else if (kind == 1) p = (const char*)((const TIn*)a.k + row * 64 + ee);
+    else if (kind == 2) p = (const char*)((const TIn*)a.v + (row * a.N + n0) * 16 + ee);
+    else if (kind == 3) p = (const char*)(a.dy + (row * a.N + n0) * 16 + ee);
+    else p = (const char*)((const TIn*)a.q + row * 64);
+    r = *(const u32x4*)p;
+    // f of (step, head) for threads u < kSub * HPW
+    const int ft = u / HPW, fh = u % HPW;
+    const bool fok = u < kSub * HPW && ft < len && n0 + fh < a.N;
+    fr = ((const TIn*)a.f)[((size_t)b * a.T + t0 + (fok ? ft : 0)) * a.N + n0 + (fok ? fh : 0)];
+  }
+
+  __device__ void store(float* buf, int w, int lane, int n0, int len, int N) const {
+    if (w < NWAVES - NL) return;
     float* K_s = buf;
     float* Q_s = K_s + kSub * 64;
     float* V_s = Q_s + kSub * 64;
     float* F_s = V_s + kSub * HPW * 16;
     float* U_s = F_s + kSub * HPW * 4;
     float* Kp_s = U_s + kSub * HPW * 16;
-    if (w == 7) {
-      const f4 xv = Vec4<TIn>::to_f4(x) * kScale;
-      *(f4*)(K_s + lane * 4) = xv;
-      // element e = 4 (lane % 16) + i of step lane / 16 goes to [tile][g][r]
-      // with row e = 16 tile + 4 r + g
-      float* kp = Kp_s + (lane / 16) * 64 + ((lane % 16) / 4) * 16 + lane % 4;
+    const int u = (w - (NWAVES - NL)) * 64 + lane;
+    int kind, t, e0;
+    decode(u, kind, t, e0);
+    const bool ok = t < len && (kind < 2 || n0 + e0 / 16 < N);
+    float x[EPC];
+    if (kind == 3 || sizeof(TIn) == 4) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kp[i * 4] = xv[i];
-    } else if (w == 6) {
-      *(f4*)(Q_s + lane * 4) = Vec4<TIn>::to_f4(x);
-    } else if (w == 5) {
-      if (lane < kVU) {
-        *(f4*)(V_s + lane * 4) = Vec4<TIn>::to_f4(x);
-        *(f4*)(U_s + lane * 4) = uu;
-      } else if (lane < kVU + kF) {
-        const float ff = fset ? to_f32(fr) : 1.0f;
-        const float gg = 1.0f - ff;
-        *(f4*)(F_s + (lane - kVU) * 4) = f4{ff, kScale * gg, -2.0f * kScale * gg, gg};
+      for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(r[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(r[i] << 16);
+        x[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
       }
+    }
+    const int n = kind == 3 ? 4 : EPC;                    // values in this chunk
+    if (!ok) {
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) x[i] = 0.f;
+    }
+    if (kind == 0) {
+#pragma unroll
+      for (int i = 0; i < EPC; i += 4) *(f4*)(Q_s + t * 64 + e0 + i) = f4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+    } else if (kind == 1) {
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) x[i] *= kScale;
+#pragma unroll
+      for (int i = 0; i < EPC; i += 4) *(f4*)(K_s + t * 64 + e0 + i) = f4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+      // row e = 16 tile + 4 r + g goes to [tile][g][r]; a chunk starts at a
+      // multiple of 4, so element i sits at base + (i % 4) * 4 + i / 4
+      float* kp = Kp_s + t * 64 + (e0 / 16) * 16 + (e0 % 16) / 4;
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) kp[(i % 4) * 4 + i / 4] = x[i];
+    } else if (kind == 2) {
+#pragma unroll
+      for (int i = 0; i < EPC; i += 4) *(f4*)(V_s + t * HPW * 16 + e0 + i) = f4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+    } else if (kind == 3) {
+      *(f4*)(U_s + t * HPW * 16 + e0) = f4{x[0], x[1], x[2], x[3]};
+    }
+    (void)n;
+    if (u < kSub * HPW) {
+      const int ft = u / HPW, fh = u % HPW;
+      const float ff = (ft < len && n0 + fh < N) ? to_f32(fr) : 1.0f;
+      const float gg = 1.0f - ff;
+      *(f4*)(F_s + u * 4) = f4{ff, kScale * gg, -2.0f * kScale * gg, gg};
     }
   }
 };
@@ -291,10 +328,10 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   }
 
   {
-    BwdStage<TIn, HPW> st;
-    const int t0 = (ns - 1) * L;
-    st.load(a, w, lane, b, n0, t0, min(L, a.T - t0));
-    st.store(smem, w, lane);
+    BwdStage<TIn, HPW, Cfg::NWAVES> st;
+    const int t0 = (ns - 1) * L, len0 = min(L, a.T - t0);
+    st.load(a, w, lane, b, n0, t0, len0);
+    st.store(smem, w, lane, n0, len0, a.N);
   }
   // the next restart state, prefetched one sub-chunk ahead and scaled by c
   // only when it is used (so nothing waits on the load early)
@@ -309,8 +346,9 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     // The last iteration fetches sub-chunk 0 again and stages it into the
     // buffer no one reads: no branch, so nothing in flight gets copied.
     const int sn = sb > 0 ? sb - 1 : 0;
-    BwdStage<TIn, HPW> st;
-    st.load(a, w, lane, b, n0, sn * L, min(L, a.T - sn * L));
+    BwdStage<TIn, HPW, Cfg::NWAVES> st;
+    const int lenn = min(L, a.T - sn * L);
+    st.load(a, w, lane, b, n0, sn * L, lenn);
     if (live) Hnext = *(const f4*)(Hs + (size_t)sn * 1024);
     const float* buf = smem + (it & 1) * Cfg::kBuf;
     const float* K_s = buf;
@@ -409,7 +447,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) acc += *(const f4*)(src + hh * 256 + gg * 64 + (((r4 + 4 * gg) & 15) << 2));
       if (w == 0) acc *= kInvScale;
-      if (s < len) *(f4*)(a.ws_dqk + (((size_t)b * ngroups + grp) * a.T + t0 + s) * 128 + w * 64 + 4 * r4) = acc;
+      float* dst = a.ws_dqk + (((size_t)b * ngroups + grp) * a.T + t0) * 128;   // uniform
+      if (s < len) *(f4*)(dst + (unsigned)(s * 128 + w * 64 + 4 * r4)) = acc;
     } else if (w < 4) {
       // dv[b][t][n][v'] = (1/c) (sum of the 16 (tile, g) partials) + w_r u; dw_r
       const int hh = w - 2, s = lane / 16, e = lane % 16;
@@ -417,8 +456,9 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       const f4 p = (*(const f4*)d + *(const f4*)(d + 4)) + (*(const f4*)(d + 8) + *(const f4*)(d + 12));
       const float uu = U_s[(s * HPW + hh) * 16 + e];
       dwr = fmaf(uu, V_s[(s * HPW + hh) * 16 + e], dwr);
+      float* dst = a.dv + (((size_t)b * a.T + t0) * a.N + n0) * 16;   // uniform
       if (s < len && n0 + hh < a.N)
-        a.dv[(((size_t)b * a.T + t0 + s) * a.N + n0 + hh) * 16 + e] = fmaf(wr_e, uu, ((p[0] + p[1]) + (p[2] + p[3])) * kInvScale);
+        dst[(unsigned)((s * a.N + hh) * 16 + e)] = fmaf(wr_e, uu, ((p[0] + p[1]) + (p[2] + p[3])) * kInvScale);
     } else if (w < 6) {
       // df[b][t][n]: wave 4 steps 0, 1, wave 5 steps 2, 3; both heads
       const int s0 = 2 * (w - 4);
@@ -430,9 +470,10 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       }
       const float tot = sum4_over_lanes(x[0], x[1], x[2], x[3]);
       const int s = s0 + (g & 1), hh = g >> 1;
-      if (m == 0 && s < len && n0 + hh < a.N) a.df[((size_t)b * a.T + t0 + s) * a.N + n0 + hh] = tot;
+      float* dst = a.df + ((size_t)b * a.T + t0) * a.N + n0;   // uniform
+      if (m == 0 && s < len && n0 + hh < a.N) dst[(unsigned)(s * a.N + hh)] = tot;
     }
-    st.store(smem + ((it + 1) & 1) * Cfg::kBuf, w, lane);
+    st.store(smem + ((it + 1) & 1) * Cfg::kBuf, w, lane, n0, lenn, a.N);
     __syncthreads();
   }
 
