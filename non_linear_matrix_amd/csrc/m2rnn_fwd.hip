@@ -54,37 +54,39 @@ struct FwdStager {
   static constexpr int kV = (TC * HPW * 4 + NT - 1) / NT;   // 4-vectors of v
   raw qk[kQK];
   raw vv[kV];
-  float ff;
+  TIn fr;   // f as stored, converted when staged
 
+  // Every thread issues the same loads; a slot past the chunk's end, of a
+  // missing head or beyond the staged counts reads valid data (step t0, head
+  // n0) and is zeroed when staged.  No register of an in-flight load is then
+  // merged or copied, and the conversions wait until the data is staged, so
+  // the prefetch overlaps the chunk's steps.
   __device__ void load(const FwdArgs& a, int b, int n0, int t0, int t_end, int tid) {
 #pragma unroll
     for (int r = 0; r < kQK; ++r) {
-      int u = tid + r * NT;                 // [0, 2*TC*16)
-      int which = u / (TC * 16);            // 0: q, 1: k
-      int t = (u / 16) % TC, e0 = (u % 16) * 4;
-      qk[r] = Vec4<TIn>::zero();
-      if (u < 2 * TC * 16 && t0 + t < t_end) {
-        const TIn* src = (const TIn*)(which ? a.k : a.q);
-        qk[r] = Vec4<TIn>::load(src + ((size_t)b * a.T + t0 + t) * 64 + e0);
-      }
+      const int u = tid + r * NT;           // [0, 2*TC*16)
+      const int which = u / (TC * 16);      // 0: q, 1: k
+      const int t = (u / 16) % TC, e0 = (u % 16) * 4;
+      const bool ok = u < 2 * TC * 16 && t0 + t < t_end;
+      const TIn* src = (const TIn*)(which == 1 ? a.k : a.q);
+      qk[r] = Vec4<TIn>::load(src + ((size_t)b * a.T + t0 + (ok ? t : 0)) * 64 + (ok ? e0 : 0));
     }
 #pragma unroll
     for (int r = 0; r < kV; ++r) {
-      int u = tid + r * NT;                 // [0, TC*HPW*4)
-      int t = u / (HPW * 4), h = (u / 4) % HPW, c4 = u % 4;
-      vv[r] = Vec4<TIn>::zero();
-      if (u < TC * HPW * 4 && t0 + t < t_end && n0 + h < a.N)
-        vv[r] = Vec4<TIn>::load((const TIn*)a.v + (((size_t)b * a.T + t0 + t) * a.N + n0 + h) * 16 + 4 * c4);
+      const int u = tid + r * NT;           // [0, TC*HPW*4)
+      const int t = u / (HPW * 4), h = (u / 4) % HPW, c4 = u % 4;
+      const bool ok = u < TC * HPW * 4 && t0 + t < t_end && n0 + h < a.N;
+      vv[r] = Vec4<TIn>::load((const TIn*)a.v + (((size_t)b * a.T + t0 + (ok ? t : 0)) * a.N + n0 + (ok ? h : 0)) * 16 +
+                              (ok ? 4 * c4 : 0));
     }
-    ff = 1.0f;
     {
-      int t = tid / HPW, h = tid % HPW;
-      if (tid < TC * HPW && t0 + t < t_end && n0 + h < a.N)
-        ff = to_f32(((const TIn*)a.f)[((size_t)b * a.T + t0 + t) * a.N + n0 + h]);
+      const int t = tid / HPW, h = tid % HPW;
+      const bool ok = tid < TC * HPW && t0 + t < t_end && n0 + h < a.N;
+      fr = ((const TIn*)a.f)[((size_t)b * a.T + t0 + (ok ? t : 0)) * a.N + n0 + (ok ? h : 0)];
     }
   }
 
-  __device__ void store(float* buf, int tid) const {
+  __device__ void store(float* buf, const FwdArgs& a, int n0, int t0, int t_end, int tid) const {
     float* K_s = buf;
     float* Q_s = buf + TC * 64;
     float* V_s = buf + 2 * TC * 64;
@@ -96,6 +98,7 @@ struct FwdStager {
         int which = u / (TC * 16);
         int t = (u / 16) % TC, e0 = (u % 16) * 4;
         f4 x = Vec4<TIn>::to_f4(qk[r]);
+        if (t0 + t >= t_end) x = f4{0.f, 0.f, 0.f, 0.f};
         // element e = 16 j + m goes to [t][m][j]: a lane with column m reads
         // its tiles' values as one contiguous word.
         float* dst = (which ? K_s : Q_s) + t * 64;
@@ -110,10 +113,17 @@ struct FwdStager {
 #pragma unroll
     for (int r = 0; r < kV; ++r) {
       int u = tid + r * NT;
-      if (u < TC * HPW * 4) *(f4*)(V_s + u * 4) = Vec4<TIn>::to_f4(vv[r]);
+      if (u < TC * HPW * 4) {
+        const int t = u / (HPW * 4), h = (u / 4) % HPW;
+        f4 x = Vec4<TIn>::to_f4(vv[r]);
+        if (t0 + t >= t_end || n0 + h >= a.N) x = f4{0.f, 0.f, 0.f, 0.f};
+        *(f4*)(V_s + u * 4) = x;
+      }
     }
     if (tid < TC * HPW) {
-      float gg = 1.0f - ff;
+      const int t = tid / HPW, h = tid % HPW;
+      const float ff = (t0 + t < t_end && n0 + h < a.N) ? to_f32(fr) : 1.0f;
+      const float gg = 1.0f - ff;
       *(f4*)(F_s + tid * 4) = f4{ff, kScale * gg, -2.0f * kScale * gg, 0.0f};
     }
   }
@@ -189,17 +199,26 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
   }
 
   const int nchunks = (te - tb + TC - 1) / TC;
-  FwdStager<TIn, HPW, Cfg::NT, TC> st;
-  st.load(a, b, n0, tb, te, tid);
-  st.store(smem, tid);
+  {
+    FwdStager<TIn, HPW, Cfg::NT, TC> st;
+    st.load(a, b, n0, tb, te, tid);
+    st.store(smem, a, n0, tb, te, tid);
+  }
   __syncthreads();
 
   // next step whose incoming state is checkpointed
-  int next_ck = a.H_ckpt ? (tb + a.ckpt_every - 1) / a.ckpt_every * a.ckpt_every : a.T;
+  int ck_idx = a.H_ckpt ? (tb + a.ckpt_every - 1) / a.ckpt_every : 0;   // its checkpoint slot
+  int next_ck = a.H_ckpt ? ck_idx * a.ckpt_every : a.T;
   for (int c = 0; c < nchunks; ++c) {
     const int t0 = tb + c * TC;
     const bool more = c + 1 < nchunks;
-    if (more) st.load(a, b, n0, t0 + TC, te, tid);
+    // prefetch the next chunk (the last chunk fetches itself again and stages
+    // it into the buffer no one reads).  Waves with steps to run issue it in
+    // their first step: loads still in flight where the step loop (which
+    // holds the checkpoint stores) is entered would be waited for there.
+    const int tn = more ? t0 + TC : t0;
+    FwdStager<TIn, HPW, Cfg::NT, TC> st;
+    if (DENSE || !live) st.load(a, b, n0, tn, te, tid);
 
     const float* buf = smem + (c & 1) * Cfg::kBuf;
     const float* K_s = buf;
@@ -209,10 +228,12 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
     const int steps = min(TC, te - t0);
     if (live) {
       for (int tt = 0; tt < steps; ++tt) {
+        if (!DENSE && tt == 0) st.load(a, b, n0, tn, te, tid);
         const int t = t0 + tt;
         if (t == next_ck) {
-          float* dst = a.H_ckpt + (((size_t)b * a.N + n) * a.nck + t / a.ckpt_every) * 1024;
+          float* dst = a.H_ckpt + (((size_t)b * a.N + n) * a.nck + ck_idx) * 1024;
           next_ck += a.ckpt_every;
+          ++ck_idx;
 #pragma unroll
           for (int j = 0; j < TPW; ++j) *(f4*)(dst + (16 * (j0 + j) + m) * 16 + 4 * g) = P[j] * kInvScale;
         }
@@ -273,7 +294,7 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
         *(f4*)(a.y + (((size_t)b * a.T + t0 + tt) * a.N + n0 + hh) * 16 + 4 * c4) = acc;
       }
     }
-    if (more) st.store(smem + ((c + 1) & 1) * Cfg::kBuf, tid);
+    st.store(smem + ((c + 1) & 1) * Cfg::kBuf, a, n0, tn, te, tid);
     __syncthreads();
   }
 
