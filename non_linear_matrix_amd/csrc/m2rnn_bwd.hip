@@ -45,8 +45,11 @@ constexpr int kSub = 4;  // steps between restart states; their H_{t-1}, Z_t sta
 
 template <int HPW>
 struct BwdCfg {
-  // the reduction pass gives each of the 8 waves of two heads a fixed role
-  static_assert(HPW == 2 && kSub == 4, "backward workgroup shape: lane = (step, 16 values)");
+  // the reduction pass gives each wave a fixed role (lane = (step, 16 values))
+  static_assert((HPW == 2 || HPW == 4) && kSub == 4, "backward workgroup shape");
+  // pass roles: dq, dk; one dv wave per head; one df wave per two heads and
+  // two steps
+  static constexpr int kDvWave = 2, kDfWave = 2 + HPW, kRoleWaves = 2 + HPW + HPW;
   static constexpr int NWAVES = HPW * 4;
   static constexpr int NT = 64 * NWAVES;
   // per staged step: K_s[64] (c k), Q_s[64] (q), V_s[HPW][16], F_s[HPW][4],
@@ -315,10 +318,12 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   f4 C = {0.f, 0.f, 0.f, 0.f};
   if (live && a.dH_T) C = *(const f4*)(a.dH_T + head * 1024 + kk * 16 + 4 * g);
   f4 dW = {0.f, 0.f, 0.f, 0.f};   // lane (g, m), register i: c * dW[4g + i][m] partial
-  // dv waves (2, 3): w_r of their (head, v') and the dw_r partial of their step slot
+  // dv waves (one per head): w_r of their (head, v') and the dw_r partial of
+  // their step slot
+  const bool dv_wave = w >= Cfg::kDvWave && w < Cfg::kDvWave + HPW;
   float wr_e = 0.f, dwr = 0.f;
-  if (w == 2 || w == 3) {
-    const int hh = w - 2;
+  if (dv_wave) {
+    const int hh = w - Cfg::kDvWave;
     if (n0 + hh < a.N) wr_e = to_f32(((const TIn*)a.wr)[(size_t)(n0 + hh) * 16 + m]);
   }
   if (!live) {
@@ -449,9 +454,9 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       if (w == 0) acc *= kInvScale;
       float* dst = a.ws_dqk + (((size_t)b * ngroups + grp) * a.T + t0) * 128;   // uniform
       if (s < len) *(f4*)(dst + (unsigned)(s * 128 + w * 64 + 4 * r4)) = acc;
-    } else if (w < 4) {
+    } else if (dv_wave) {
       // dv[b][t][n][v'] = (1/c) (sum of the 16 (tile, g) partials) + w_r u; dw_r
-      const int hh = w - 2, s = lane / 16, e = lane % 16;
+      const int hh = w - Cfg::kDvWave, s = lane / 16, e = lane % 16;
       const float* d = dvbuf + (s * HPW + hh) * 320 + e * 20;
       const f4 p = (*(const f4*)d + *(const f4*)(d + 4)) + (*(const f4*)(d + 8) + *(const f4*)(d + 12));
       const float uu = U_s[(s * HPW + hh) * 16 + e];
@@ -459,17 +464,17 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       float* dst = a.dv + (((size_t)b * a.T + t0) * a.N + n0) * 16;   // uniform
       if (s < len && n0 + hh < a.N)
         dst[(unsigned)((s * a.N + hh) * 16 + e)] = fmaf(wr_e, uu, ((p[0] + p[1]) + (p[2] + p[3])) * kInvScale);
-    } else if (w < 6) {
-      // df[b][t][n]: wave 4 steps 0, 1, wave 5 steps 2, 3; both heads
-      const int s0 = 2 * (w - 4);
+    } else if (w < Cfg::kRoleWaves) {
+      // df[b][t][n]: each wave two steps of two heads
+      const int d = w - Cfg::kDfWave, s0 = 2 * (d & 1), h0 = 2 * (d >> 1);
       float x[4];
 #pragma unroll
       for (int o = 0; o < 4; ++o) {
-        const f4 p = *(const f4*)(dfbuf + ((s0 + o / 2) * HPW + o % 2) * 256 + lane * 4);
+        const f4 p = *(const f4*)(dfbuf + ((s0 + o / 2) * HPW + h0 + o % 2) * 256 + lane * 4);
         x[o] = (p[0] + p[1]) + (p[2] + p[3]);
       }
       const float tot = sum4_over_lanes(x[0], x[1], x[2], x[3]);
-      const int s = s0 + (g & 1), hh = g >> 1;
+      const int s = s0 + (g & 1), hh = h0 + (g >> 1);
       float* dst = a.df + ((size_t)b * a.T + t0) * a.N + n0;   // uniform
       if (m == 0 && s < len && n0 + hh < a.N) dst[(unsigned)(s * a.N + hh)] = tot;
     }
@@ -486,7 +491,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   }
   // dw_r: the dv waves hold one partial per (step slot, head, v'); sum the
   // step slots in a fixed order
-  if (w == 2 || w == 3) dfbuf[(w - 2) * 64 + lane] = dwr;
+  if (dv_wave) dfbuf[(w - Cfg::kDvWave) * 64 + lane] = dwr;
   __syncthreads();
   if (w == 0 && lane < HPW * 16) {
     const int hh = lane / 16, e = lane % 16;
@@ -532,7 +537,7 @@ __global__ void m2rnn_bwd_reduce_kernel(BwdArgs a) {
   }
 }
 
-constexpr int kBwdHPW = 2;
+constexpr int kBwdHPW = 4;
 
 size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* off_dense, size_t* off_dqk,
                                  size_t* off_dW, size_t* off_dwr, int* ngroups) {
