@@ -35,6 +35,13 @@ class Oracle:
         bwd.restype = ctypes.c_int
         bwd.argtypes = [ctypes.c_int] * 5 + [_dbl_p] * 7 + [_dbl_p, _dbl_p] + [_dbl_p] * 7 + [ctypes.c_int]
 
+        gf = self.lib.m2rnn_ref_gate_forward
+        gf.restype = ctypes.c_int
+        gf.argtypes = [ctypes.c_int] * 3 + [_dbl_p] * 4
+        gb = self.lib.m2rnn_ref_gate_backward
+        gb.restype = ctypes.c_int
+        gb.argtypes = [ctypes.c_int] * 3 + [_dbl_p] * 7
+
     @staticmethod
     def _arr(x, shape=None):
         a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
@@ -94,6 +101,33 @@ class Oracle:
         return out
 
 
+    def gate_forward(self, a, alpha, beta):
+        """f = exp(-alpha[n] softplus(a + beta[n])) for a [B,T,N], alpha, beta [N]."""
+        a = self._arr(a)
+        B, T, N = a.shape
+        alpha = self._arr(alpha, (N,))
+        beta = self._arr(beta, (N,))
+        f = np.empty((B, T, N))
+        st = self.lib.m2rnn_ref_gate_forward(B, T, N, self._p(a), self._p(alpha), self._p(beta), self._p(f))
+        if st != 0:
+            raise RuntimeError(f"m2rnn_ref_gate_forward failed with status {st}")
+        return f
+
+    def gate_backward(self, a, alpha, beta, df):
+        """(da [B,T,N], dalpha [N], dbeta [N]) from df [B,T,N]."""
+        a = self._arr(a)
+        B, T, N = a.shape
+        alpha = self._arr(alpha, (N,))
+        beta = self._arr(beta, (N,))
+        df = self._arr(df, (B, T, N))
+        da, dal, dbe = np.empty((B, T, N)), np.empty(N), np.empty(N)
+        st = self.lib.m2rnn_ref_gate_backward(B, T, N, self._p(a), self._p(alpha), self._p(beta), self._p(df),
+                                              self._p(da), self._p(dal), self._p(dbe))
+        if st != 0:
+            raise RuntimeError(f"m2rnn_ref_gate_backward failed with status {st}")
+        return da, dal, dbe
+
+
 _default = None
 
 
@@ -114,3 +148,11 @@ def forward(*args, **kw):
 
 def backward(*args, **kw):
     return get().backward(*args, **kw)
+
+
+def gate_forward(*args, **kw):
+    return get().gate_forward(*args, **kw)
+
+
+def gate_backward(*args, **kw):
+    return get().gate_backward(*args, **kw)

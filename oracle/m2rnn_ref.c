@@ -326,3 +326,46 @@ int m2rnn_ref_backward(int B, int T, int N, int K, int V,
   free(J.dq_part); free(J.dk_part); free(J.dW_part); free(J.dwr_part);
   return st;
 }
+
+/* ------------------------------------------------------------------ gate
+ * Forget gate from a pre-activation, slide "The gate preserves a direct path
+ * through time" (paper Sec. 3.1, Eqs. (13), (17)):
+ *     f[b][t][n] = exp(-alpha[n] * softplus(a[b][t][n] + beta[n])),
+ * softplus(x) = log(1 + e^x), evaluated as max(x, 0) + log1p(exp(-|x|)).
+ * Backward, by the chain rule with softplus'(x) = 1 / (1 + e^{-x}):
+ *     da    = df * f * (-alpha) * sigmoid(a + beta)
+ *     dalpha = sum_{b,t} df * f * (-softplus(a + beta))
+ *     dbeta  = sum_{b,t} da
+ * (sums over b ascending, then t ascending). */
+static double softplus(double x) { return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x))); }
+
+int m2rnn_ref_gate_forward(int B, int T, int N, const double* a, const double* alpha, const double* beta,
+                           double* f) {
+  if (B < 0 || T < 0 || N < 1 || !a || !alpha || !beta || !f) return -1;
+  for (int b = 0; b < B; ++b)
+    for (int t = 0; t < T; ++t)
+      for (int n = 0; n < N; ++n) {
+        const size_t i = ((size_t)b * T + t) * N + n;
+        f[i] = exp(-alpha[n] * softplus(a[i] + beta[n]));
+      }
+  return 0;
+}
+
+int m2rnn_ref_gate_backward(int B, int T, int N, const double* a, const double* alpha, const double* beta,
+                            const double* df, double* da, double* dalpha, double* dbeta) {
+  if (B < 0 || T < 0 || N < 1 || !a || !alpha || !beta || !df || !da || !dalpha || !dbeta) return -1;
+  for (int n = 0; n < N; ++n) { dalpha[n] = 0.0; dbeta[n] = 0.0; }
+  for (int b = 0; b < B; ++b)
+    for (int t = 0; t < T; ++t)
+      for (int n = 0; n < N; ++n) {
+        const size_t i = ((size_t)b * T + t) * N + n;
+        const double x = a[i] + beta[n];
+        const double sp = softplus(x);
+        const double f = exp(-alpha[n] * sp);
+        const double sig = 1.0 / (1.0 + exp(-x));
+        da[i] = df[i] * f * (-alpha[n]) * sig;
+        dalpha[n] += df[i] * f * (-sp);
+        dbeta[n] += da[i];
+      }
+  return 0;
+}

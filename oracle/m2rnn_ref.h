@@ -61,6 +61,16 @@ int m2rnn_ref_backward(int B, int T, int N, int K, int V,
                        double* dW, double* dwr, double* dH_0,
                        int nthreads);
 
+/* Forget gate from a pre-activation (slide "The gate preserves a direct path
+ * through time", paper Eqs. (13), (17)): f = exp(-alpha[n] softplus(a + beta[n]))
+ * for a, f [B][T][N] and alpha, beta [N]; and its backward from df [B][T][N]:
+ * da [B][T][N], dalpha and dbeta [N] summed over batch and time.  Return 0, or
+ * -1 on a bad argument. */
+int m2rnn_ref_gate_forward(int B, int T, int N, const double* a, const double* alpha, const double* beta,
+                           double* f);
+int m2rnn_ref_gate_backward(int B, int T, int N, const double* a, const double* alpha, const double* beta,
+                            const double* df, double* da, double* dalpha, double* dbeta);
+
 #ifdef __cplusplus
 }
 #endif

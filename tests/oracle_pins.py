@@ -18,6 +18,8 @@ Sources (M2RNN paper-discussion slides, reading of arXiv:2603.14360v2):
   [H0]  a caller-given initial state: the recurrence of [EQ] resumed from a
         stored state, and its gradient dL/dH_0 = C_0, where the recursion of
         [BW] for C ends.
+  [GT]  slide "The gate preserves a direct path through time", paper Sec. 3.1,
+        Eqs. (13), (17): f = exp(-alpha softplus(a + beta)), alpha >= 0.
 """
 import numpy as np
 import torch
@@ -430,10 +432,98 @@ def pin_finite_differences_initial_state(o):
         assert err <= 1e-6 * scale, f"FD {name} (H_0 != 0): max abs diff {err:.3e}"
 
 
+
+# ----------------------------------------------------------------- gate pins
+
+def _gate_inputs(rng, B, T, N):
+    a = rng.standard_normal((B, T, N)) * 2.0
+    a[0, 0, :] = [50.0, -50.0, 0.0][:N] + [0.0] * max(0, N - 3)   # saturated arguments
+    alpha = rng.uniform(0.2, 2.5, N)
+    beta = rng.uniform(-3.0, 1.0, N)
+    return a, alpha, beta
+
+
+def pin_gate_sigmoid_identity(o):
+    """[GT] with alpha = 1: exp(-softplus(x)) = 1 / (1 + e^x), here via
+    scipy's expit, including saturated arguments x = +-50."""
+    from scipy.special import expit
+    rng = np.random.default_rng(RNG_SEED + 30)
+    a, _, beta = _gate_inputs(rng, 2, 7, 3)
+    f = o.gate_forward(a, np.ones(3), beta)
+    _close(f, expit(-(a + beta)), 1e-15, "gate alpha=1")
+
+
+def pin_gate_alpha_zero(o):
+    """[GT] alpha = 0 keeps the state (f = 1, the slide's endpoint): da = 0,
+    dbeta = 0 and dalpha = -sum df * softplus(a + beta) (numpy's logaddexp)."""
+    rng = np.random.default_rng(RNG_SEED + 31)
+    a, _, beta = _gate_inputs(rng, 2, 5, 3)
+    alpha = np.zeros(3)
+    assert np.array_equal(o.gate_forward(a, alpha, beta), np.ones_like(a))
+    df = rng.standard_normal(a.shape)
+    da, dal, dbe = o.gate_backward(a, alpha, beta, df)
+    assert np.array_equal(da, np.zeros_like(da)) and np.array_equal(dbe, np.zeros_like(dbe))
+    _close(dal, -np.sum(df * np.logaddexp(0.0, a + beta), axis=(0, 1)), 1e-12, "gate alpha=0 dalpha")
+
+
+def pin_gate_power_law_and_range(o):
+    """[GT]: f(alpha) = f(1)^alpha, and alpha >= 0 keeps f in [0, 1]."""
+    rng = np.random.default_rng(RNG_SEED + 32)
+    a, alpha, beta = _gate_inputs(rng, 3, 6, 4)
+    f = o.gate_forward(a, alpha, beta)
+    f1 = o.gate_forward(a, np.ones(4), beta)
+    _close(f, f1 ** alpha, 1e-14, "gate power law")
+    assert np.all(f >= 0.0) and np.all(f <= 1.0)
+
+
+def pin_gate_large_arguments(o):
+    """[GT] for x = a + beta >= 40, softplus(x) = x in double precision, so
+    f = exp(-alpha x) exactly; with a small alpha f stays well above zero even
+    where e^x overflows (x = 750), and the gradients stay finite."""
+    a = np.array([[[40.0, 300.0, 750.0]]])
+    alpha = np.array([0.5, 0.02, 0.01])
+    beta = np.zeros(3)
+    f = o.gate_forward(a, alpha, beta)
+    _close(f, np.exp(-alpha * a), 1e-15, "gate large x")
+    da, dal, dbe = o.gate_backward(a, alpha, beta, np.ones_like(a))
+    assert np.all(np.isfinite(da)) and np.all(np.isfinite(dal)) and np.all(np.isfinite(dbe))
+    _close(dal, -(np.exp(-alpha * a) * a)[0, 0], 1e-12, "gate large x dalpha")
+
+
+def pin_gate_finite_differences(o):
+    """[GT] backward against central differences of L = sum(f * df) over every
+    element of a, alpha and beta."""
+    rng = np.random.default_rng(RNG_SEED + 33)
+    B, T, N = 2, 4, 3
+    a = rng.standard_normal((B, T, N)) * 2.0
+    alpha = rng.uniform(0.2, 2.5, N)
+    beta = rng.uniform(-3.0, 1.0, N)
+    df = rng.standard_normal((B, T, N))
+    da, dal, dbe = o.gate_backward(a, alpha, beta, df)
+    h = 1e-6
+    ins = [a, alpha, beta]
+    for idx, got in enumerate([da, dal, dbe]):
+        x = ins[idx]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            mi = it.multi_index
+            orig = x[mi]
+            x[mi] = orig + h
+            lp = float(np.sum(o.gate_forward(*ins) * df))
+            x[mi] = orig - h
+            lm = float(np.sum(o.gate_forward(*ins) * df))
+            x[mi] = orig
+            fd[mi] = (lp - lm) / (2 * h)
+        _close(got, fd, 1e-7 * max(1.0, float(np.max(np.abs(fd)))), f"gate FD {['da', 'dalpha', 'dbeta'][idx]}")
+
+
 FORWARD_PINS = [pin_t1_closed_form, pin_f_one_forward, pin_zero_w_zero_f_forward, pin_readout_linear_in_q,
                 pin_checkpoints, pin_convex_bound, pin_permutations, pin_rnn_embedding_forward_backward]
 BACKWARD_PINS = [pin_f_one_backward, pin_zero_w_zero_f_backward, pin_finite_differences_small,
                  pin_finite_differences_full_state]
 INITIAL_STATE_PINS = [pin_initial_state_f_one, pin_initial_state_forgotten, pin_split_sequence,
                       pin_finite_differences_initial_state]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + INITIAL_STATE_PINS + [pin_thread_invariance]
+GATE_PINS = [pin_gate_sigmoid_identity, pin_gate_alpha_zero, pin_gate_power_law_and_range,
+             pin_gate_large_arguments, pin_gate_finite_differences]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + INITIAL_STATE_PINS + GATE_PINS + [pin_thread_invariance]

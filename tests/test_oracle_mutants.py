@@ -52,6 +52,14 @@ MUTANTS = [
     ("dH0_is_R", "if (J->dH_0) memcpy(J->dH_0 + ((size_t)b * N + n) * S, C,",
      "if (J->dH_0) memcpy(J->dH_0 + ((size_t)b * N + n) * S, R,"),
     ("H0_of_wrong_head", "memcpy(H, J->H_0 + ((size_t)b * N + n) * S", "memcpy(H, J->H_0 + ((size_t)b * N + (n + 1) % N) * S"),
+    ("softplus_naive", "return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));", "return log(1.0 + exp(x));"),
+    ("softplus_drops_linear_part", "return (x > 0.0 ? x : 0.0) + log1p(exp(-fabs(x)));", "return log1p(exp(-fabs(x)));"),
+    ("gate_sign", "f[i] = exp(-alpha[n] * softplus(a[i] + beta[n]));", "f[i] = exp(alpha[n] * softplus(a[i] + beta[n]));"),
+    ("gate_beta_subtracted", "f[i] = exp(-alpha[n] * softplus(a[i] + beta[n]));", "f[i] = exp(-alpha[n] * softplus(a[i] - beta[n]));"),
+    ("da_drops_f", "da[i] = df[i] * f * (-alpha[n]) * sig;", "da[i] = df[i] * (-alpha[n]) * sig;"),
+    ("da_wrong_derivative", "da[i] = df[i] * f * (-alpha[n]) * sig;", "da[i] = df[i] * f * (-alpha[n]) * (1.0 - sig);"),
+    ("dalpha_drops_f", "dalpha[n] += df[i] * f * (-sp);", "dalpha[n] += df[i] * (-sp);"),
+    ("dbeta_is_df", "dbeta[n] += da[i];", "dbeta[n] += df[i];"),
 ]
 
 
