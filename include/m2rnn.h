@@ -89,7 +89,26 @@ int m2rnn_forward(int B, int T, int N, int K, int V, int dtype,
                   void* stream);
 
 /*
- * Bytes of device workspace m2rnn_backward needs for these sizes (0 if none).
+ * Forward scan with the forget gate computed in the kernel from a
+ * pre-activation (slide "The gate preserves a direct path through time",
+ * paper Eqs. (13), (17)):
+ *       f_t = exp(-alpha[n] * softplus(a_t + beta[n]))
+ * which for alpha = 1 is sigmoid(-(a_t + beta)); f lies in [0, 1] for
+ * alpha >= 0 and is 1 everywhere for alpha = 0.
+ *   a       [B][T][N]     gate pre-activation (dtype `dtype`), in place of f
+ *   alpha   [N], beta [N] per-head gate parameters (dtype `dtype`)
+ * Every other argument, and the result for the same f, as m2rnn_forward.
+ */
+int m2rnn_forward_gated(int B, int T, int N, int K, int V, int dtype,
+                        const void* q, const void* k, const void* v, const void* a,
+                        const void* alpha, const void* beta,
+                        const void* W, const void* w_r, const float* H_0,
+                        float* y, float* H_T, float* H_ckpt, int ckpt_every,
+                        void* stream);
+
+/*
+ * Bytes of device workspace m2rnn_backward and m2rnn_backward_gated need
+ * for these sizes (0 if none).
  */
 size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckpt_every);
 
@@ -121,6 +140,28 @@ int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
                    float* dq, float* dk, float* dv, float* df,
                    float* dW, float* dw_r, float* dH_0,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward scan of m2rnn_forward_gated: the gradients of m2rnn_backward with
+ * df carried through the gate (slide "The gate preserves a direct path
+ * through time", paper Eqs. (13), (17)): with s = softplus(a_t + beta[n]),
+ *       da_t     = df_t * f_t * (-alpha[n]) * sigmoid(a_t + beta[n])
+ *       dalpha[n] = sum over b, t of df_t * f_t * (-s)
+ *       dbeta[n]  = sum over b, t of da_t
+ *   a, alpha, beta       the forward's gate inputs (dtype `dtype`)
+ *   da      [B][T][N]    float32 out, in place of df
+ *   dalpha, dbeta [N]    float32 out, 4-byte aligned
+ * Every other argument as m2rnn_backward; the same workspace size.
+ */
+int m2rnn_backward_gated(int B, int T, int N, int K, int V, int dtype,
+                         const void* q, const void* k, const void* v, const void* a,
+                         const void* alpha, const void* beta,
+                         const void* W, const void* w_r,
+                         const float* H_ckpt, int ckpt_every,
+                         const float* dy, const float* dH_T,
+                         float* dq, float* dk, float* dv, float* da,
+                         float* dalpha, float* dbeta, float* dW, float* dw_r, float* dH_0,
+                         void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * One token of the recurrence for every (b, n), state held by the caller

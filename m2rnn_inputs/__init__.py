@@ -13,6 +13,15 @@ paper Fig. 2: q, k, v come out of a SiLU; the forget gate lies in [0, 1]):
     w_r  = N(0, 1)                 [N, V]
     dy   = N(0, 1)                 [B, T, N, V]  (float32, backward only)
 
+For the gated scan (f computed in the kernel from a pre-activation, slide
+"The gate preserves a direct path through time", paper Eqs. (13), (17)),
+make_gate draws, from its own generator:
+
+    a     = N(-mu, 1)              [B, T, N]   mu = 2: with alpha = 1, beta = 0
+                                               f has the distribution above
+    alpha = U[0.5, 2)              [N]
+    beta  = U[-1, 1)               [N]
+
 Draw order is fixed (q, k, v, f, W, w_r, dy) from one CPU torch.Generator
 seeded with `seed`; every tensor is drawn in float32 and, for bfloat16
 workloads, rounded to bfloat16 with round-to-nearest-even.  dy stays float32.
@@ -96,3 +105,15 @@ def make_state(B, N, K=K_DIM, V=V_DIM, seed=0):
     g = torch.Generator(device="cpu")
     g.manual_seed(int(seed))
     return (torch.rand(B, N, K, V, generator=g, dtype=torch.float32) * 2.0 - 1.0).contiguous()
+
+
+def make_gate(B, T, N, dtype="f32", mu=2.0, seed=0):
+    """Seeded gate inputs for the gated scan: dict of CPU tensors a [B,T,N],
+    alpha [N], beta [N] in `dtype` (drawn in float32, then rounded)."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 7919)
+    td = torch_dtype(dtype)
+    a = torch.randn(B, T, N, generator=g, dtype=torch.float32) - mu
+    alpha = torch.rand(N, generator=g, dtype=torch.float32) * 1.5 + 0.5
+    beta = torch.rand(N, generator=g, dtype=torch.float32) * 2.0 - 1.0
+    return {"a": a.to(td).contiguous(), "alpha": alpha.to(td).contiguous(), "beta": beta.to(td).contiguous()}

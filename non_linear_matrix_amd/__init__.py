@@ -11,9 +11,12 @@ is no CPU fallback.
     grads = m2.backward(q, k, v, f, W, w_r, H_ckpt, 64, dy)     # dict
     y2, H_T2 = m2.forward(q2, k2, v2, f2, W, w_r, H_0=H_T)     # resume
     y_t = m2.decode(q_t, k_t, v_t, f_t, W, w_r, H)              # one token, H updated
+    y, H_T = m2.forward_gated(q, k, v, a, alpha, beta, W, w_r)  # f from the gate
+    grads = m2.backward_gated(q, k, v, a, alpha, beta, W, w_r, H_ckpt, 64, dy)
 
 Shapes (K = 64, V = 16): q, k [B,T,K]; v [B,T,N,V]; f [B,T,N]; W [N,V,V];
-w_r [N,V]; all six float32 or all six bfloat16, contiguous, on one GPU.
+w_r [N,V]; gate pre-activation a [B,T,N] and alpha, beta [N] in place of f;
+all inputs float32 or all bfloat16, contiguous, on one GPU.
 Outputs and gradients are float32.
 """
 import ctypes
@@ -46,6 +49,11 @@ lib.m2rnn_backward_workspace_bytes.restype = ctypes.c_size_t
 lib.m2rnn_backward_workspace_bytes.argtypes = [_i] * 6
 lib.m2rnn_backward.restype = _i
 lib.m2rnn_backward.argtypes = [_i] * 6 + [_p] * 6 + [_p, _i] + [_p, _p] + [_p] * 7 + [_p, ctypes.c_size_t, _p]
+lib.m2rnn_forward_gated.restype = _i
+lib.m2rnn_forward_gated.argtypes = [_i] * 6 + [_p] * 9 + [_p, _p, _p, _i, _p]
+lib.m2rnn_backward_gated.restype = _i
+lib.m2rnn_backward_gated.argtypes = ([_i] * 6 + [_p] * 8 + [_p, _i] + [_p, _p] + [_p] * 9
+                                     + [_p, ctypes.c_size_t, _p])
 lib.m2rnn_decode.restype = _i
 lib.m2rnn_decode.argtypes = [_i] * 5 + [_p] * 6 + [_p, _p, _p]
 lib.m2rnn_last_error.restype = ctypes.c_char_p
@@ -97,6 +105,21 @@ def m2rnn_backward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_ckpt, ckpt_ever
                               dq, dk, dv, df, dW, dw_r, dH_0, workspace, workspace_bytes, stream)
 
 
+def m2rnn_forward_gated(B, T, N, K_, V_, dtype, q, k, v, a, alpha, beta, W, w_r, H_0, y, H_T, H_ckpt, ckpt_every,
+                        stream):
+    """Raw C-ABI call with ctypes pointers; returns the status code."""
+    return lib.m2rnn_forward_gated(B, T, N, K_, V_, dtype, q, k, v, a, alpha, beta, W, w_r, H_0, y, H_T, H_ckpt,
+                                   ckpt_every, stream)
+
+
+def m2rnn_backward_gated(B, T, N, K_, V_, dtype, q, k, v, a, alpha, beta, W, w_r, H_ckpt, ckpt_every, dy, dH_T,
+                         dq, dk, dv, da, dalpha, dbeta, dW, dw_r, dH_0, workspace, workspace_bytes, stream):
+    """Raw C-ABI call with ctypes pointers; returns the status code."""
+    return lib.m2rnn_backward_gated(B, T, N, K_, V_, dtype, q, k, v, a, alpha, beta, W, w_r, H_ckpt, ckpt_every,
+                                    dy, dH_T, dq, dk, dv, da, dalpha, dbeta, dW, dw_r, dH_0, workspace,
+                                    workspace_bytes, stream)
+
+
 def m2rnn_decode(B, N, K_, V_, dtype, q, k, v, f, W, w_r, H, y, stream):
     """Raw C-ABI call with ctypes pointers; returns the status code."""
     return lib.m2rnn_decode(B, N, K_, V_, dtype, q, k, v, f, W, w_r, H, y, stream)
@@ -110,11 +133,7 @@ def m2rnn_last_error():
     return lib.m2rnn_last_error().decode()
 
 
-def forward(q, k, v, f, W, w_r, ckpt_every=0, out=None, H_0=None):
-    """y [B,T,N,V], H_T [B,N,K,V] (float32) and, if ckpt_every > 0,
-    H_ckpt [B,N,ceil(T/ckpt_every),K,V].  `out` may pass preallocated
-    (y, H_T[, H_ckpt]) tensors; H_0 [B,N,K,V] float32 is the initial state
-    (None: zero) and may be the same tensor as H_T."""
+def _fwd_outputs(q, v, ckpt_every, out):
     B, T, N, Kq, Vv = _sizes(q, v)
     dev = q.device
     if out is None:
@@ -126,8 +145,30 @@ def forward(q, k, v, f, W, w_r, ckpt_every=0, out=None, H_0=None):
     else:
         y, H_T = out[0], out[1]
         H_ck = out[2] if len(out) > 2 else None
+    return y, H_T, H_ck
+
+
+def forward(q, k, v, f, W, w_r, ckpt_every=0, out=None, H_0=None):
+    """y [B,T,N,V], H_T [B,N,K,V] (float32) and, if ckpt_every > 0,
+    H_ckpt [B,N,ceil(T/ckpt_every),K,V].  `out` may pass preallocated
+    (y, H_T[, H_ckpt]) tensors; H_0 [B,N,K,V] float32 is the initial state
+    (None: zero) and may be the same tensor as H_T."""
+    B, T, N, Kq, Vv = _sizes(q, v)
+    y, H_T, H_ck = _fwd_outputs(q, v, ckpt_every, out)
     _check(lib.m2rnn_forward(B, T, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W),
-                             _ptr(w_r), _ptr(H_0), _ptr(y), _ptr(H_T), _ptr(H_ck), int(ckpt_every), _stream(dev)))
+                             _ptr(w_r), _ptr(H_0), _ptr(y), _ptr(H_T), _ptr(H_ck), int(ckpt_every),
+                             _stream(q.device)))
+    return (y, H_T) if H_ck is None else (y, H_T, H_ck)
+
+
+def forward_gated(q, k, v, a, alpha, beta, W, w_r, ckpt_every=0, out=None, H_0=None):
+    """forward() with f = exp(-alpha[n] softplus(a + beta[n])) computed in the
+    kernel from the gate pre-activation a [B,T,N] and alpha, beta [N]."""
+    B, T, N, Kq, Vv = _sizes(q, v)
+    y, H_T, H_ck = _fwd_outputs(q, v, ckpt_every, out)
+    _check(lib.m2rnn_forward_gated(B, T, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                   _ptr(alpha), _ptr(beta), _ptr(W), _ptr(w_r), _ptr(H_0), _ptr(y), _ptr(H_T),
+                                   _ptr(H_ck), int(ckpt_every), _stream(q.device)))
     return (y, H_T) if H_ck is None else (y, H_T, H_ck)
 
 
@@ -152,6 +193,32 @@ def backward(q, k, v, f, W, w_r, H_ckpt, ckpt_every, dy, dH_T=None, out=None, wo
                               _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["df"]),
                               _ptr(out["dW"]), _ptr(out["dw_r"]), _ptr(out.get("dH_0")), _ptr(workspace), wbytes,
                               _stream(dev)))
+    return out
+
+
+def backward_gated(q, k, v, a, alpha, beta, W, w_r, H_ckpt, ckpt_every, dy, dH_T=None, out=None, workspace=None,
+                   want_dH_0=False):
+    """backward() of forward_gated(): the dict holds da [B,T,N] and dalpha,
+    dbeta [N] in place of df."""
+    B, T, N, Kq, Vv = _sizes(q, v)
+    dev = q.device
+    if out is None:
+        out = dict(dq=torch.empty((B, T, Kq), device=dev), dk=torch.empty((B, T, Kq), device=dev),
+                   dv=torch.empty((B, T, N, Vv), device=dev), da=torch.empty((B, T, N), device=dev),
+                   dalpha=torch.empty((N,), device=dev), dbeta=torch.empty((N,), device=dev),
+                   dW=torch.empty((N, Vv, Vv), device=dev), dw_r=torch.empty((N, Vv), device=dev))
+        if want_dH_0:
+            out["dH_0"] = torch.empty((B, N, Kq, Vv), device=dev)
+    nbytes = int(lib.m2rnn_backward_workspace_bytes(B, T, N, Kq, Vv, int(ckpt_every)))
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty((nbytes,), device=dev, dtype=torch.uint8)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.m2rnn_backward_gated(B, T, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
+                                    _ptr(alpha), _ptr(beta), _ptr(W), _ptr(w_r), _ptr(H_ckpt), int(ckpt_every),
+                                    _ptr(dy), _ptr(dH_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                                    _ptr(out["da"]), _ptr(out["dalpha"]), _ptr(out["dbeta"]), _ptr(out["dW"]),
+                                    _ptr(out["dw_r"]), _ptr(out.get("dH_0")), _ptr(workspace), wbytes,
+                                    _stream(dev)))
     return out
 
 

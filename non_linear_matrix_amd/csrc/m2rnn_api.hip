@@ -50,11 +50,11 @@ int need(const void* p, const char* name, long long elems, size_t align) {
 
 extern "C" const char* m2rnn_last_error(void) { return g_err; }
 
-extern "C" int m2rnn_forward(int B, int T, int N, int K, int V, int dtype,
-                             const void* q, const void* k, const void* v, const void* f,
-                             const void* W, const void* w_r, const float* H_0,
-                             float* y, float* H_T, float* H_ckpt, int ckpt_every,
-                             void* stream) {
+// f is given, or computed from the gate pre-activation ga and (galpha, gbeta).
+static int forward_impl(bool gated, int B, int T, int N, int K, int V, int dtype, const void* q, const void* k,
+                        const void* v, const void* f, const void* ga, const void* galpha, const void* gbeta,
+                        const void* W, const void* w_r, const float* H_0, float* y, float* H_T, float* H_ckpt,
+                        int ckpt_every, void* stream) {
   g_err[0] = 0;
   int st = check_sizes(B, T, N, K, V, dtype);
   if (st) return st;
@@ -64,7 +64,10 @@ extern "C" int m2rnn_forward(int B, int T, int N, int K, int V, int dtype,
   if ((H_ckpt != nullptr) != (ckpt_every > 0))
     return fail(M2RNN_ERR_INVALID_ARG, "H_ckpt and ckpt_every > 0 go together");
   if ((st = need(q, "q", BT * K, 16)) || (st = need(k, "k", BT * K, 16)) || (st = need(v, "v", BTN * V, 16)) ||
-      (st = need(f, "f", BTN, es)) || (st = need(W, "W", (long long)N * V * V * (BN > 0), es)) ||
+      (st = need(gated ? ga : f, gated ? "a" : "f", BTN, es)) ||
+      (st = need(galpha, "alpha", gated ? (long long)N * (BN > 0) : 0, es)) ||
+      (st = need(gbeta, "beta", gated ? (long long)N * (BN > 0) : 0, es)) ||
+      (st = need(W, "W", (long long)N * V * V * (BN > 0), es)) ||
       (st = need(w_r, "w_r", (long long)N * V * (BN > 0), es)) || (st = need(y, "y", BTN * V, 16)) ||
       (st = need(H_T, "H_T", BN * K * V, 16)))
     return st;
@@ -81,6 +84,7 @@ extern "C" int m2rnn_forward(int B, int T, int N, int K, int V, int dtype,
   }
   m2rnn::FwdArgs a;
   a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.wr = w_r; a.H_0 = H_0;
+  if (gated) { a.ga = ga; a.galpha = galpha; a.gbeta = gbeta; }
   a.y = y; a.H_T = H_T; a.H_ckpt = ckpt_every > 0 ? H_ckpt : nullptr;
   a.B = B; a.T = T; a.N = N; a.ckpt_every = ckpt_every; a.nck = nck;
   hipError_t e = m2rnn::launch_forward(a, dtype, s);
@@ -88,19 +92,35 @@ extern "C" int m2rnn_forward(int B, int T, int N, int K, int V, int dtype,
   return M2RNN_OK;
 }
 
-extern "C" size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckpt_every) {
-  if (B <= 0 || T <= 0 || N <= 0 || K != 64 || V != 16 || ckpt_every < 1) return 0;
-  size_t o1, o2, o3, o4;
-  int ng;
-  return sizeof(float) * m2rnn::backward_workspace_floats(B, T, N, ckpt_every, &o1, &o2, &o3, &o4, &ng);
+extern "C" int m2rnn_forward(int B, int T, int N, int K, int V, int dtype, const void* q, const void* k,
+                             const void* v, const void* f, const void* W, const void* w_r, const float* H_0,
+                             float* y, float* H_T, float* H_ckpt, int ckpt_every, void* stream) {
+  return forward_impl(false, B, T, N, K, V, dtype, q, k, v, f, nullptr, nullptr, nullptr, W, w_r, H_0, y, H_T, H_ckpt,
+                      ckpt_every, stream);
 }
 
-extern "C" int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
-                              const void* q, const void* k, const void* v, const void* f,
-                              const void* W, const void* w_r, const float* H_ckpt, int ckpt_every,
-                              const float* dy, const float* dH_T, float* dq, float* dk, float* dv,
-                              float* df, float* dW, float* dw_r, float* dH_0, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+extern "C" int m2rnn_forward_gated(int B, int T, int N, int K, int V, int dtype, const void* q, const void* k,
+                                   const void* v, const void* a, const void* alpha, const void* beta,
+                                   const void* W, const void* w_r, const float* H_0, float* y, float* H_T,
+                                   float* H_ckpt, int ckpt_every, void* stream) {
+  return forward_impl(true, B, T, N, K, V, dtype, q, k, v, nullptr, a, alpha, beta, W, w_r, H_0, y, H_T, H_ckpt,
+                      ckpt_every, stream);
+}
+
+extern "C" size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckpt_every) {
+  if (B <= 0 || T <= 0 || N <= 0 || K != 64 || V != 16 || ckpt_every < 1) return 0;
+  size_t o1, o2, o3, o4, o5;
+  int ng;
+  return sizeof(float) * m2rnn::backward_workspace_floats(B, T, N, ckpt_every, &o1, &o2, &o3, &o4, &o5, &ng);
+}
+
+// f is given (df out) or computed from the gate (da in the df slot, dalpha and
+// dbeta out).
+static int backward_impl(bool gated, int B, int T, int N, int K, int V, int dtype, const void* q, const void* k, const void* v,
+                         const void* f, const void* ga, const void* galpha, const void* gbeta, const void* W,
+                         const void* w_r, const float* H_ckpt, int ckpt_every, const float* dy, const float* dH_T,
+                         float* dq, float* dk, float* dv, float* df, float* dalpha, float* dbeta, float* dW,
+                         float* dw_r, float* dH_0, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   int st = check_sizes(B, T, N, K, V, dtype);
   if (st) return st;
@@ -109,10 +129,15 @@ extern "C" int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
   const long long BT = (long long)B * T, BTN = BT * N, BN = (long long)B * N;
   const int nck = T > 0 ? (T + ckpt_every - 1) / ckpt_every : 0;
   if ((st = need(q, "q", BT * K * (N > 0), 16)) || (st = need(k, "k", BT * K * (N > 0), 16)) ||
-      (st = need(v, "v", BTN * V, 16)) || (st = need(f, "f", BTN, es)) || (st = need(W, "W", (long long)N * V * V, es)) ||
+      (st = need(v, "v", BTN * V, 16)) || (st = need(gated ? ga : f, gated ? "a" : "f", BTN, es)) ||
+      (st = need(galpha, "alpha", gated ? (long long)N : 0, es)) ||
+      (st = need(gbeta, "beta", gated ? (long long)N : 0, es)) ||
+      (st = need(dalpha, "dalpha", gated ? (long long)N : 0, 4)) ||
+      (st = need(dbeta, "dbeta", gated ? (long long)N : 0, 4)) ||
+      (st = need(W, "W", (long long)N * V * V, es)) ||
       (st = need(w_r, "w_r", (long long)N * V, es)) || (st = need(H_ckpt, "H_ckpt", BN * nck * K * V, 16)) ||
       (st = need(dy, "dy", BTN * V, 16)) || (st = need(dq, "dq", BT * K, 16)) || (st = need(dk, "dk", BT * K, 16)) ||
-      (st = need(dv, "dv", BTN * V, 16)) || (st = need(df, "df", BTN, 4)) || (st = need(dW, "dW", (long long)N * V * V, 16)) ||
+      (st = need(dv, "dv", BTN * V, 16)) || (st = need(df, gated ? "da" : "df", BTN, 4)) || (st = need(dW, "dW", (long long)N * V * V, 16)) ||
       (st = need(dw_r, "dw_r", (long long)N * V, 16)))
     return st;
   if (dH_T && !aligned(dH_T, 16)) return fail(M2RNN_ERR_INVALID_ARG, "dH_T must be 16-byte aligned");
@@ -131,13 +156,15 @@ extern "C" int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
     if (N > 0) {
       if (e == hipSuccess) e = m2rnn::launch_fill_zero(dW, (size_t)N * V * V, s);
       if (e == hipSuccess) e = m2rnn::launch_fill_zero(dw_r, (size_t)N * V, s);
+      if (gated && e == hipSuccess) e = m2rnn::launch_fill_zero(dalpha, (size_t)N, s);
+      if (gated && e == hipSuccess) e = m2rnn::launch_fill_zero(dbeta, (size_t)N, s);
     }
     return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "zero fill: %s", hipGetErrorString(e));
   }
-  size_t o_dense, o_dqk, o_dW, o_dwr;
+  size_t o_dense, o_dqk, o_dW, o_dwr, o_dgate;
   int ng;
   const size_t need_bytes = sizeof(float) * m2rnn::backward_workspace_floats(B, T, N, ckpt_every, &o_dense, &o_dqk,
-                                                                              &o_dW, &o_dwr, &ng);
+                                                                              &o_dW, &o_dwr, &o_dgate, &ng);
   if (!workspace || workspace_bytes < need_bytes)
     return fail(M2RNN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need_bytes,
                 workspace ? workspace_bytes : (size_t)0);
@@ -147,19 +174,40 @@ extern "C" int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
   a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.wr = w_r;
   a.H_ckpt = H_ckpt; a.dy = dy; a.dH_T = dH_T;
   a.dq = dq; a.dk = dk; a.dv = dv; a.df = df; a.dW = dW; a.dw_r = dw_r; a.dH_0 = dH_0;
-  a.ws_dqk = ws + o_dqk; a.ws_dW = ws + o_dW; a.ws_dwr = ws + o_dwr;
+  a.ws_dqk = ws + o_dqk; a.ws_dW = ws + o_dW; a.ws_dwr = ws + o_dwr; a.ws_dgate = ws + o_dgate;
+  if (gated) { a.ga = ga; a.galpha = galpha; a.gbeta = gbeta; a.dalpha = dalpha; a.dbeta = dbeta; }
   a.B = B; a.T = T; a.N = N;
   a.ckpt_every = ckpt_every; a.nck = nck; a.ngroups = ng;
   // replay of the caller's checkpoint chunks into states every sub-step count
   const int L = m2rnn::backward_sub_steps();
   m2rnn::FwdArgs rp;
   rp.q = q; rp.k = k; rp.v = v; rp.f = f; rp.W = W; rp.wr = w_r;
+  if (gated) { rp.ga = ga; rp.galpha = galpha; rp.gbeta = gbeta; }
   rp.y = nullptr; rp.H_T = nullptr; rp.H_ckpt = ws + o_dense;
   rp.B = B; rp.T = T; rp.N = N; rp.ckpt_every = L; rp.nck = (T + L - 1) / L;
   rp.H_src = H_ckpt; rp.src_every = ckpt_every; rp.src_nck = nck;
   hipError_t e = m2rnn::launch_backward(a, rp, dtype, s);
   if (e != hipSuccess) return fail(M2RNN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
   return M2RNN_OK;
+}
+
+extern "C" int m2rnn_backward(int B, int T, int N, int K, int V, int dtype, const void* q, const void* k,
+                              const void* v, const void* f, const void* W, const void* w_r, const float* H_ckpt,
+                              int ckpt_every, const float* dy, const float* dH_T, float* dq, float* dk, float* dv,
+                              float* df, float* dW, float* dw_r, float* dH_0, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return backward_impl(false, B, T, N, K, V, dtype, q, k, v, f, nullptr, nullptr, nullptr, W, w_r, H_ckpt, ckpt_every, dy,
+                       dH_T, dq, dk, dv, df, nullptr, nullptr, dW, dw_r, dH_0, workspace, workspace_bytes, stream);
+}
+
+extern "C" int m2rnn_backward_gated(int B, int T, int N, int K, int V, int dtype, const void* q, const void* k,
+                                    const void* v, const void* a, const void* alpha, const void* beta,
+                                    const void* W, const void* w_r, const float* H_ckpt, int ckpt_every,
+                                    const float* dy, const float* dH_T, float* dq, float* dk, float* dv, float* da,
+                                    float* dalpha, float* dbeta, float* dW, float* dw_r, float* dH_0,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(true, B, T, N, K, V, dtype, q, k, v, nullptr, a, alpha, beta, W, w_r, H_ckpt, ckpt_every, dy,
+                       dH_T, dq, dk, dv, da, dalpha, dbeta, dW, dw_r, dH_0, workspace, workspace_bytes, stream);
 }
 
 extern "C" int m2rnn_decode(int B, int N, int K, int V, int dtype, const void* q, const void* k, const void* v,

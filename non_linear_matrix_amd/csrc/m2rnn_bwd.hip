@@ -43,7 +43,7 @@ namespace m2rnn {
 
 constexpr int kSub = 4;  // steps between restart states; their H_{t-1}, Z_t stay in registers
 
-template <int HPW>
+template <int HPW, bool GATE>
 struct BwdCfg {
   // the reduction pass gives each wave a fixed role (lane = (step, 16 values))
   static_assert((HPW == 2 || HPW == 4) && kSub == 4, "backward workgroup shape");
@@ -53,8 +53,11 @@ struct BwdCfg {
   static constexpr int NWAVES = HPW * 4;
   static constexpr int NT = 64 * NWAVES;
   // per staged step: K_s[64] (c k), Q_s[64] (q), V_s[HPW][16], F_s[HPW][4],
-  // U_s[HPW][16], Kp_s[64] (c k permuted: [tile][g][r] = row 16 tile + 4 r + g)
-  static constexpr int kStep = 192 + HPW * 36;
+  // U_s[HPW][16], Kp_s[64] (c k permuted: [tile][g][r] = row 16 tile + 4 r + g),
+  // and with the gate G_s[HPW][2] (df -> da and df -> dalpha factors, in the
+  // df waves' row order: (s, h) at df wave (s >> 1) + 2 (h >> 1), row
+  // (s & 1) + 2 (h & 1))
+  static constexpr int kStep = 192 + HPW * (GATE ? 38 : 36);
   static constexpr int kBuf = kSub * kStep;
   // per wave, two slots of {H_{t-1} tile, D tile}; a tile is stored as
   // [v / 4][kk][v % 4] with a 72-float stride between the v / 4 blocks, which
@@ -73,7 +76,10 @@ struct BwdCfg {
   static constexpr int kQK = kSub * 2 * HPW * 256;
   static constexpr int kDV = kSub * HPW * 320;
   static constexpr int kDF = kSub * HPW * 256;
-  static constexpr int kFloats = 2 * kBuf + kXpose + kQK + kDV + kDF;
+  // with the gate: alpha, beta of the HPW heads, [h][2], then the dalpha,
+  // dbeta sums of each df wave's four lane rows, [wave][row][2]
+  static constexpr int kGpar = GATE ? 2 * HPW + HPW * 8 : 0;
+  static constexpr int kFloats = 2 * kBuf + kXpose + kQK + kDV + kDF + kGpar;
   static constexpr int kBytes = kFloats * 4;
 };
 
@@ -85,7 +91,7 @@ struct BwdCfg {
 // data), so no register of an in-flight load is ever merged or copied and
 // nothing waits on the loads before they are staged.  Steps past len are
 // staged as f = 1, q = k = v = u = 0.
-template <typename TIn, int HPW, int NWAVES>
+template <typename TIn, int HPW, int NWAVES, bool GATE>
 struct BwdStage {
   static constexpr int EPC = 16 / (int)sizeof(TIn);          // elements per chunk
   static constexpr int nQ = kSub * 64 / EPC;                  // q chunks (and k chunks)
@@ -126,10 +132,12 @@ struct BwdStage {
     // f of (step, head) for threads u < kSub * HPW
     const int ft = u / HPW, fh = u % HPW;
     const bool fok = u < kSub * HPW && ft < len && n0 + fh < a.N;
-    fr = ((const TIn*)a.f)[((size_t)b * a.T + t0 + (fok ? ft : 0)) * a.N + n0 + (fok ? fh : 0)];
+    const TIn* fsrc = (const TIn*)(GATE ? a.ga : a.f);   // f, or the gate's pre-activation
+    fr = fsrc[((size_t)b * a.T + t0 + (fok ? ft : 0)) * a.N + n0 + (fok ? fh : 0)];
   }
 
-  __device__ void store(float* buf, int w, int lane, int n0, int len, int N) const {
+  // gpar: alpha, beta of the HPW heads, [h][2] (with the gate)
+  __device__ void store(float* buf, int w, int lane, int n0, int len, int N, const float* gpar) const {
     if (w < NWAVES - NL) return;
     float* K_s = buf;
     float* Q_s = K_s + kSub * 64;
@@ -137,6 +145,7 @@ struct BwdStage {
     float* F_s = V_s + kSub * HPW * 16;
     float* U_s = F_s + kSub * HPW * 4;
     float* Kp_s = U_s + kSub * HPW * 16;
+    float* G_s = Kp_s + kSub * 64;
     const int u = (w - (NWAVES - NL)) * 64 + lane;
     int kind, t, e0;
     decode(u, kind, t, e0);
@@ -179,9 +188,21 @@ struct BwdStage {
     (void)n;
     if (u < kSub * HPW) {
       const int ft = u / HPW, fh = u % HPW;
-      const float ff = (ft < len && n0 + fh < N) ? to_f32(fr) : 1.0f;
+      const bool real = ft < len && n0 + fh < N;
+      float ff = 1.0f;
+      f2 gf = {0.f, 0.f};
+      if (GATE && real) {
+        // f = exp(-alpha sp), df/da = -alpha f sigmoid, df/dalpha = -sp f
+        const f2 ab = *(const f2*)(gpar + fh * 2);
+        const GateVal gv = gate_value(to_f32(fr), ab[0], ab[1]);
+        ff = gv.f;
+        gf = f2{-ab[0] * gv.f * gv.sig, -gv.sp * gv.f};
+      } else if (real) {
+        ff = to_f32(fr);
+      }
       const float gg = 1.0f - ff;
       *(f4*)(F_s + u * 4) = f4{ff, kScale * gg, -2.0f * kScale * gg, gg};
+      if (GATE) *(f2*)(G_s + (((ft >> 1) + 2 * (fh >> 1)) * 4 + (ft & 1) + 2 * (fh & 1)) * 2) = gf;
     }
   }
 };
@@ -278,9 +299,9 @@ __device__ __forceinline__ float sum4_over_lanes(float x0, float x1, float x2, f
   return row_sum16(__builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]));
 }
 
-template <typename TIn, int HPW>
+template <typename TIn, int HPW, bool GATE>
 __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) void m2rnn_bwd_kernel(BwdArgs a) {
-  typedef BwdCfg<HPW> Cfg;
+  typedef BwdCfg<HPW, GATE> Cfg;
   extern __shared__ float smem[];
   float* xpose = smem + 2 * Cfg::kBuf;
   float* qkbuf = xpose + Cfg::kXpose;
@@ -322,6 +343,21 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   // their step slot
   const bool dv_wave = w >= Cfg::kDvWave && w < Cfg::kDvWave + HPW;
   float wr_e = 0.f, dwr = 0.f;
+  // the gate parameters of the group's heads, read by the threads that stage
+  // f; the df waves' dalpha, dbeta sums (row r of df wave d: step parity r & 1
+  // and head 2 (d >> 1) + (r >> 1))
+  float* gpar = dfbuf + Cfg::kDF;
+  float* gacc = gpar + 2 * HPW;
+  if (GATE) {
+    if (tid < HPW) {
+      const bool ok = n0 + tid < a.N;
+      gpar[tid * 2] = ok ? to_f32(((const TIn*)a.galpha)[n0 + tid]) : 0.f;
+      gpar[tid * 2 + 1] = ok ? to_f32(((const TIn*)a.gbeta)[n0 + tid]) : 0.f;
+    }
+    if (tid < HPW * 8) gacc[tid] = 0.f;
+    __syncthreads();
+  }
+  constexpr bool gate = GATE;
   if (dv_wave) {
     const int hh = w - Cfg::kDvWave;
     if (n0 + hh < a.N) wr_e = to_f32(((const TIn*)a.wr)[(size_t)(n0 + hh) * 16 + m]);
@@ -333,10 +369,10 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   }
 
   {
-    BwdStage<TIn, HPW, Cfg::NWAVES> st;
+    BwdStage<TIn, HPW, Cfg::NWAVES, GATE> st;
     const int t0 = (ns - 1) * L, len0 = min(L, a.T - t0);
     st.load(a, w, lane, b, n0, t0, len0);
-    st.store(smem, w, lane, n0, len0, a.N);
+    st.store(smem, w, lane, n0, len0, a.N, gpar);
   }
   // the next restart state, prefetched one sub-chunk ahead and scaled by c
   // only when it is used (so nothing waits on the load early)
@@ -351,7 +387,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     // The last iteration fetches sub-chunk 0 again and stages it into the
     // buffer no one reads: no branch, so nothing in flight gets copied.
     const int sn = sb > 0 ? sb - 1 : 0;
-    BwdStage<TIn, HPW, Cfg::NWAVES> st;
+    BwdStage<TIn, HPW, Cfg::NWAVES, GATE> st;
     const int lenn = min(L, a.T - sn * L);
     st.load(a, w, lane, b, n0, sn * L, lenn);
     if (live) Hnext = *(const f4*)(Hs + (size_t)sn * 1024);
@@ -362,6 +398,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     const float* F_s = V_s + kSub * HPW * 16;
     const float* U_s = F_s + kSub * HPW * 4;
     const float* Kp_s = U_s + kSub * HPW * 16;     // c k permuted, [s][tile][g][r]
+    const float* G_s = Kp_s + kSub * 64;            // gate factors, [df wave][row][2]
 
     if (live) {
       // replay the sub-chunk keeping H_{t-1} and Z_t on chip
@@ -475,10 +512,22 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       }
       const float tot = sum4_over_lanes(x[0], x[1], x[2], x[3]);
       const int s = s0 + (g & 1), hh = h0 + (g >> 1);
+      float out = tot;
+      if (gate) {
+        // chain rule through f = exp(-alpha softplus(a + beta)): da, and the
+        // per-head sums for dalpha, dbeta
+        const f2 gf = *(const f2*)(G_s + (d * 4 + g) * 2);
+        out = tot * gf[0];
+        if (m == 0 && s < len && n0 + hh < a.N) {
+          f2* acc = (f2*)(gacc + (d * 4 + g) * 2);   // this lane's own slot
+          *acc = *acc + f2{tot * gf[1], out};
+        }
+      }
       float* dst = a.df + ((size_t)b * a.T + t0) * a.N + n0;   // uniform
-      if (m == 0 && s < len && n0 + hh < a.N) dst[(unsigned)(s * a.N + hh)] = tot;
+      if (GATE) dst = sgpr_ptr(dst);
+      if (m == 0 && s < len && n0 + hh < a.N) dst[(unsigned)(s * a.N + hh)] = out;
     }
-    st.store(smem + ((it + 1) & 1) * Cfg::kBuf, w, lane, n0, lenn, a.N);
+    st.store(smem + ((it + 1) & 1) * Cfg::kBuf, w, lane, n0, lenn, a.N, gpar);
     __syncthreads();
   }
 
@@ -500,6 +549,15 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     for (int s = 0; s < kSub; ++s) acc += dfbuf[hh * 64 + s * 16 + e];
     if (n0 + hh < a.N) a.ws_dwr[((size_t)b * a.N + n0 + hh) * 16 + e] = acc;
   }
+  if (gate && w == 1 && lane < HPW && n0 + lane < a.N) {
+    const int hh = lane, d0 = 2 * (hh >> 1), r0 = 2 * (hh & 1);
+    f2 acc = {0.f, 0.f};
+#pragma unroll
+    for (int dd = 0; dd < 2; ++dd)
+#pragma unroll
+      for (int rr = 0; rr < 2; ++rr) acc += *(const f2*)(gacc + ((d0 + dd) * 4 + r0 + rr) * 2);
+    *(f2*)(a.ws_dgate + ((size_t)b * a.N + n0 + hh) * 2) = acc;
+  }
 }
 
 // Fixed-order sums over workgroups (dq, dk), batch rows and row tiles (dW),
@@ -508,7 +566,8 @@ __global__ void m2rnn_bwd_reduce_kernel(BwdArgs a) {
   const size_t nqk = (size_t)a.B * a.T * 32;   // float4 groups of dq and dk
   const size_t nW = (size_t)a.N * 64;          // float4 groups of dW
   const size_t nwr = (size_t)a.N * 4;
-  const size_t total = nqk + nW + nwr;
+  const size_t ngate = a.ga ? (size_t)a.N : 0;   // dalpha, dbeta of each head
+  const size_t total = nqk + nW + nwr + ngate;
   for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (size_t)gridDim.x * blockDim.x) {
     if (u < nqk) {
       const size_t bt = u / 32;
@@ -526,13 +585,19 @@ __global__ void m2rnn_bwd_reduce_kernel(BwdArgs a) {
       for (int b = 0; b < a.B; ++b)
         for (int jt = 0; jt < 4; ++jt) acc += *(const f4*)(a.ws_dW + (((size_t)b * a.N + n) * 4 + jt) * 256 + e);
       *(f4*)(a.dW + n * 256 + e) = acc;
-    } else {
+    } else if (u < nqk + nW + nwr) {
       const size_t v = u - nqk - nW;
       const size_t n = v / 4;
       const int e = (int)(v % 4) * 4;
       f4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int b = 0; b < a.B; ++b) acc += *(const f4*)(a.ws_dwr + ((size_t)b * a.N + n) * 16 + e);
       *(f4*)(a.dw_r + n * 16 + e) = acc;
+    } else {
+      const size_t n = u - nqk - nW - nwr;
+      f2 acc = {0.f, 0.f};
+      for (int b = 0; b < a.B; ++b) acc += *(const f2*)(a.ws_dgate + ((size_t)b * a.N + n) * 2);
+      a.dalpha[n] = acc[0];
+      a.dbeta[n] = acc[1];
     }
   }
 }
@@ -540,7 +605,7 @@ __global__ void m2rnn_bwd_reduce_kernel(BwdArgs a) {
 constexpr int kBwdHPW = 4;
 
 size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* off_dense, size_t* off_dqk,
-                                 size_t* off_dW, size_t* off_dwr, int* ngroups) {
+                                 size_t* off_dW, size_t* off_dwr, size_t* off_dgate, int* ngroups) {
   const int ng = (N + kBwdHPW - 1) / kBwdHPW;
   auto up = [](size_t x) { return (x + 63) & ~(size_t)63; };   // 256-byte aligned regions
   size_t o = 0;
@@ -549,26 +614,27 @@ size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* of
   *off_dqk = o;  o += up((size_t)B * ng * T * 128);
   *off_dW = o;   o += up((size_t)B * N * 4 * 256);
   *off_dwr = o;  o += up((size_t)B * N * 16);
+  *off_dgate = o; o += up((size_t)B * N * 2);
   *ngroups = ng;
   return o;
 }
 
-template <typename TIn>
+template <typename TIn, bool GATE>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  typedef BwdCfg<kBwdHPW> Cfg;
+  typedef BwdCfg<kBwdHPW, GATE> Cfg;
   static_assert(Cfg::kBytes <= 160 * 1024, "backward LDS budget");
   static bool attr_set = false;   // per process; the attribute is per kernel
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)m2rnn_bwd_kernel<TIn, kBwdHPW>,
+    hipError_t e = hipFuncSetAttribute((const void*)m2rnn_bwd_kernel<TIn, kBwdHPW, GATE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid((unsigned)(a.B * a.ngroups)), block(Cfg::NT);
-  hipLaunchKernelGGL((m2rnn_bwd_kernel<TIn, kBwdHPW>), grid, block, Cfg::kBytes, stream, a);
+  hipLaunchKernelGGL((m2rnn_bwd_kernel<TIn, kBwdHPW, GATE>), grid, block, Cfg::kBytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t total = (size_t)a.B * a.T * 32 + (size_t)a.N * 68;
+  const size_t total = (size_t)a.B * a.T * 32 + (size_t)a.N * (68 + (a.ga ? 1 : 0));
   size_t blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL(m2rnn_bwd_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
@@ -585,7 +651,8 @@ hipError_t launch_backward(const BwdArgs& a0, const FwdArgs& replay, int dtype, 
     a.ckpt_every = kSub;
     a.nck = (a.T + kSub - 1) / kSub;
   }
-  return dtype == 0 ? launch_bwd_t<float>(a, stream) : launch_bwd_t<bf16_t>(a, stream);
+  if (a.ga) return dtype == 0 ? launch_bwd_t<float, true>(a, stream) : launch_bwd_t<bf16_t, true>(a, stream);
+  return dtype == 0 ? launch_bwd_t<float, false>(a, stream) : launch_bwd_t<bf16_t, false>(a, stream);
 }
 
 int backward_sub_steps() { return kSub; }

@@ -25,6 +25,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kScale = 2.8853900817779268f;     // 2 / ln 2
 constexpr float kInvScale = 0.34657359027997264f; // ln 2 / 2
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 struct bf16_t {
   uint16_t bits;
@@ -50,6 +52,35 @@ template <> struct Vec4<bf16_t> {
   }
   __device__ static raw zero() { return uint2{0u, 0u}; }
 };
+
+// ------------------------------------------------------------ forget gate
+// f = exp(-alpha softplus(a + beta)) (slide "The gate preserves a direct path
+// through time", paper Eqs. (13), (17)), with softplus(x) = max(x, 0) +
+// log(1 + e^{-|x|}) so that no exponential overflows.  Also returns
+// softplus(x) and sigmoid(x) = softplus'(x) for the backward.
+// A wave-uniform pointer read back into scalar registers: the compiler then
+// does not fold a per-lane offset into it and keep that sum in vector
+// registers across a loop.
+template <typename T>
+__device__ __forceinline__ T* sgpr_ptr(T* p) {
+  const unsigned long long u = (unsigned long long)p;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)u);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(u >> 32));
+  return (T*)(((unsigned long long)hi << 32) | lo);
+}
+
+struct GateVal { float f, sp, sig; };
+__device__ __forceinline__ GateVal gate_value(float a, float alpha, float beta) {
+  const float x = a + beta;
+  const float e = __builtin_amdgcn_exp2f(-fabsf(x) * kLog2e);            // e^{-|x|}
+  const float sp = fmaxf(x, 0.0f) + kLn2 * __builtin_amdgcn_logf(1.0f + e);
+  const float r = __builtin_amdgcn_rcpf(1.0f + e);
+  GateVal g;
+  g.sp = sp;
+  g.sig = x >= 0.0f ? r : e * r;
+  g.f = __builtin_amdgcn_exp2f(-alpha * sp * kLog2e);
+  return g;
+}
 
 // ------------------------------------------------------- bf16 hi/lo splitting
 // x = hi + lo + O(2^-17 |x|) with hi = bf16(x), lo = bf16(x - hi), both

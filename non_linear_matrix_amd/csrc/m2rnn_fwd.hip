@@ -47,7 +47,7 @@ struct FwdCfg {
   static constexpr int kBytes = kFloats * 4;
 };
 
-template <typename TIn, int HPW, int NT, int TC>
+template <typename TIn, int HPW, int NT, int TC, bool GATE>
 struct FwdStager {
   typedef typename Vec4<TIn>::raw raw;
   static constexpr int kQK = (2 * TC * 16 + NT - 1) / NT;   // 4-vectors of q and k
@@ -82,11 +82,14 @@ struct FwdStager {
     {
       const int t = tid / HPW, h = tid % HPW;
       const bool ok = tid < TC * HPW && t0 + t < t_end && n0 + h < a.N;
-      fr = ((const TIn*)a.f)[((size_t)b * a.T + t0 + (ok ? t : 0)) * a.N + n0 + (ok ? h : 0)];
+      const TIn* fsrc = (const TIn*)(GATE ? a.ga : a.f);   // f, or the gate's pre-activation
+      fr = fsrc[((size_t)b * a.T + t0 + (ok ? t : 0)) * a.N + n0 + (ok ? h : 0)];
     }
   }
 
-  __device__ void store(float* buf, const FwdArgs& a, int n0, int t0, int t_end, int tid) const {
+  // galpha, gbeta: the gate parameters of head n0 + tid % HPW (gate mode)
+  __device__ void store(float* buf, const FwdArgs& a, int n0, int t0, int t_end, int tid, float galpha,
+                        float gbeta) const {
     float* K_s = buf;
     float* Q_s = buf + TC * 64;
     float* V_s = buf + 2 * TC * 64;
@@ -122,7 +125,8 @@ struct FwdStager {
     }
     if (tid < TC * HPW) {
       const int t = tid / HPW, h = tid % HPW;
-      const float ff = (t0 + t < t_end && n0 + h < a.N) ? to_f32(fr) : 1.0f;
+      float ff = 1.0f;
+      if (t0 + t < t_end && n0 + h < a.N) ff = GATE ? gate_value(to_f32(fr), galpha, gbeta).f : to_f32(fr);
       const float gg = 1.0f - ff;
       *(f4*)(F_s + tid * 4) = f4{ff, kScale * gg, -2.0f * kScale * gg, 0.0f};
     }
@@ -150,7 +154,7 @@ template <int TPW> __device__ __forceinline__ TileVals<TPW> load_tiles(const flo
 // chunk [c * src_every, (c+1) * src_every) of HPW heads, restarts from the
 // stored H there and writes H every ckpt_every steps (no readout), so all
 // chunks of a sequence run in parallel.
-template <typename TIn, int HPW, int TPW, int TC, bool DENSE>
+template <typename TIn, int HPW, int TPW, int TC, bool DENSE, bool GATE>
 __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
   typedef FwdCfg<HPW, TPW, TC> Cfg;
   constexpr int WPH = Cfg::WPH;
@@ -198,11 +202,18 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
     }
   }
 
+  // gate parameters of the head whose f this thread stages
+  float galpha = 0.0f, gbeta = 0.0f;
+  if (GATE && tid < TC * HPW && n0 + tid % HPW < a.N) {
+    galpha = to_f32(((const TIn*)a.galpha)[n0 + tid % HPW]);
+    gbeta = to_f32(((const TIn*)a.gbeta)[n0 + tid % HPW]);
+  }
+
   const int nchunks = (te - tb + TC - 1) / TC;
   {
-    FwdStager<TIn, HPW, Cfg::NT, TC> st;
+    FwdStager<TIn, HPW, Cfg::NT, TC, GATE> st;
     st.load(a, b, n0, tb, te, tid);
-    st.store(smem, a, n0, tb, te, tid);
+    st.store(smem, a, n0, tb, te, tid, galpha, gbeta);
   }
   __syncthreads();
 
@@ -217,7 +228,7 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
     // their first step: loads still in flight where the step loop (which
     // holds the checkpoint stores) is entered would be waited for there.
     const int tn = more ? t0 + TC : t0;
-    FwdStager<TIn, HPW, Cfg::NT, TC> st;
+    FwdStager<TIn, HPW, Cfg::NT, TC, GATE> st;
     if (DENSE || !live) st.load(a, b, n0, tn, te, tid);
 
     const float* buf = smem + (c & 1) * Cfg::kBuf;
@@ -294,7 +305,7 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
         *(f4*)(a.y + (((size_t)b * a.T + t0 + tt) * a.N + n0 + hh) * 16 + 4 * c4) = acc;
       }
     }
-    st.store(smem + ((c + 1) & 1) * Cfg::kBuf, a, n0, tn, te, tid);
+    st.store(smem + ((c + 1) & 1) * Cfg::kBuf, a, n0, tn, te, tid, galpha, gbeta);
     __syncthreads();
   }
 
@@ -305,13 +316,13 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
   }
 }
 
-template <typename TIn, int HPW, int TPW, int TC, bool DENSE = false>
+template <typename TIn, int HPW, int TPW, int TC, bool DENSE = false, bool GATE = false>
 static hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   typedef FwdCfg<HPW, TPW, TC> Cfg;
   static_assert(Cfg::kBytes <= 64 * 1024, "forward LDS budget");
   const int ngroups = (a.N + HPW - 1) / HPW;
   dim3 grid((unsigned)(a.B * ngroups * (DENSE ? a.src_nck : 1))), block(Cfg::NT);
-  hipLaunchKernelGGL((m2rnn_fwd_kernel<TIn, HPW, TPW, TC, DENSE>), grid, block, Cfg::kBytes, stream, a);
+  hipLaunchKernelGGL((m2rnn_fwd_kernel<TIn, HPW, TPW, TC, DENSE, GATE>), grid, block, Cfg::kBytes, stream, a);
   return hipGetLastError();
 }
 
@@ -325,6 +336,7 @@ static int fwd_tiles_per_wave() {
 
 template <typename TIn>
 static hipError_t dispatch_fwd(const FwdArgs& a, hipStream_t stream) {
+  if (a.ga) return launch_fwd<TIn, 4, 4, 32, false, true>(a, stream);
   switch (fwd_tiles_per_wave()) {
     case 4: return launch_fwd<TIn, 4, 4, 32>(a, stream);
     case 2: return launch_fwd<TIn, 4, 2, 16>(a, stream);
@@ -361,6 +373,9 @@ hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t stream) {
 }
 
 hipError_t launch_densify(const FwdArgs& a, int dtype, hipStream_t stream) {
+  if (a.ga)
+    return dtype == 0 ? launch_fwd<float, 4, 4, 32, true, true>(a, stream)
+                      : launch_fwd<bf16_t, 4, 4, 32, true, true>(a, stream);
   return dtype == 0 ? launch_fwd<float, 4, 4, 32, true>(a, stream) : launch_fwd<bf16_t, 4, 4, 32, true>(a, stream);
 }
 

@@ -8,6 +8,9 @@ namespace m2rnn {
 
 struct FwdArgs {
   const void *q, *k, *v, *f, *W, *wr;
+  // forget gate from a pre-activation: when ga is set, f = exp(-alpha
+  // softplus(ga + beta)) with alpha = galpha[n], beta = gbeta[n] (f unused)
+  const void *ga = nullptr, *galpha = nullptr, *gbeta = nullptr;
   const float* H_0 = nullptr;  // initial state, nullptr for zero
   float *y, *H_T, *H_ckpt;
   int B, T, N;
@@ -25,17 +28,20 @@ hipError_t launch_densify(const FwdArgs& a, int dtype, hipStream_t stream);
 
 struct BwdArgs {
   const void *q, *k, *v, *f, *W, *wr;
+  const void *ga = nullptr, *galpha = nullptr, *gbeta = nullptr;   // gate (see FwdArgs)
   const float *H_ckpt, *dy, *dH_T;  // H_ckpt: states every ckpt_every (<= sub-step count) steps
-  float *dq, *dk, *dv, *df, *dW, *dw_r;
+  float *dq, *dk, *dv, *df, *dW, *dw_r;   // with the gate, df holds da
   float* dH_0;                      // nullptr when not wanted
+  float *dalpha = nullptr, *dbeta = nullptr;   // gate parameters' gradients
   float *ws_dqk, *ws_dW, *ws_dwr;   // workspace regions
+  float* ws_dgate = nullptr;        // [B][N][2] per-row dalpha, dbeta partials
   int B, T, N;
   int ckpt_every, nck, ngroups;
 };
 
 // Workspace layout (in floats) for the backward; returns the total.
 size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* off_dense, size_t* off_dqk,
-                                 size_t* off_dW, size_t* off_dwr, int* ngroups);
+                                 size_t* off_dW, size_t* off_dwr, size_t* off_dgate, int* ngroups);
 // Steps between the states the reverse sweep restarts from.
 int backward_sub_steps();
 // When a.ckpt_every exceeds the sub-step count, `replay` (a densify launch

@@ -24,8 +24,8 @@ def m2():
 
 
 def test_header_declares_the_entry_points():
-    assert declared() == ["m2rnn_backward", "m2rnn_backward_workspace_bytes", "m2rnn_decode", "m2rnn_forward",
-                          "m2rnn_last_error"]
+    assert declared() == ["m2rnn_backward", "m2rnn_backward_gated", "m2rnn_backward_workspace_bytes",
+                          "m2rnn_decode", "m2rnn_forward", "m2rnn_forward_gated", "m2rnn_last_error"]
 
 
 def test_library_exports_every_declared_symbol(m2):
@@ -72,3 +72,30 @@ def test_argument_errors_without_launch(m2):
         m2.M2RNN_ERR_WORKSPACE            # too small
     assert "workspace" in m2.m2rnn_last_error()
     assert b(1, 4, 2, 64, 16, 0, *args6, dummy, 64, dummy, None, *grads, None, None, 0, None) == m2.M2RNN_ERR_WORKSPACE
+
+
+def test_gated_argument_errors_without_launch(m2):
+    dummy = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    q3 = [dummy] * 3
+    fg = m2.lib.m2rnn_forward_gated
+    # q, k, v, a, alpha, beta, W, w_r
+    assert fg(1, 4, 2, 64, 16, 0, *q3, None, dummy, dummy, dummy, dummy, None, dummy, dummy, None, 0, None) \
+        == m2.M2RNN_ERR_INVALID_ARG
+    assert "a must" in m2.m2rnn_last_error()
+    assert fg(1, 4, 2, 64, 16, 0, *q3, dummy, None, dummy, dummy, dummy, None, dummy, dummy, None, 0, None) \
+        == m2.M2RNN_ERR_INVALID_ARG
+    assert "alpha" in m2.m2rnn_last_error()
+    assert fg(1, 4, 2, 64, 16, 1, *q3, dummy, dummy, ctypes.c_void_p(257), dummy, dummy, None, dummy, dummy,
+              None, 0, None) == m2.M2RNN_ERR_INVALID_ARG   # bf16 beta needs 2-byte alignment
+    assert "beta" in m2.m2rnn_last_error()
+    bg = m2.lib.m2rnn_backward_gated
+    g3 = [dummy] * 3
+    # ... H_ckpt, ckpt_every, dy, dH_T, dq, dk, dv, da, dalpha, dbeta, dW, dw_r, dH_0, ws, bytes, stream
+    assert bg(1, 4, 2, 64, 16, 0, *q3, dummy, dummy, dummy, dummy, dummy, dummy, 64, dummy, None, *g3, dummy,
+              None, dummy, dummy, dummy, None, dummy, 1 << 30, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert "dalpha" in m2.m2rnn_last_error()
+    assert bg(1, 4, 2, 64, 16, 0, *q3, dummy, dummy, dummy, dummy, dummy, dummy, 64, dummy, None, *g3, None,
+              dummy, dummy, dummy, dummy, None, dummy, 1 << 30, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert "da must" in m2.m2rnn_last_error()
+    assert bg(1, 4, 2, 64, 16, 0, *q3, dummy, dummy, dummy, dummy, dummy, dummy, 64, dummy, None, *g3, dummy,
+              dummy, dummy, dummy, dummy, None, dummy, 16, None) == m2.M2RNN_ERR_WORKSPACE
