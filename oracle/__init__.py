@@ -41,6 +41,12 @@ class Oracle:
         gb = self.lib.m2rnn_ref_gate_backward
         gb.restype = ctypes.c_int
         gb.argtypes = [ctypes.c_int] * 3 + [_dbl_p] * 7
+        nf = self.lib.m2rnn_ref_gate_rmsnorm_forward
+        nf.restype = ctypes.c_int
+        nf.argtypes = [ctypes.c_int] * 2 + [_dbl_p] * 3 + [ctypes.c_double] + [_dbl_p] * 2
+        nb = self.lib.m2rnn_ref_gate_rmsnorm_backward
+        nb.restype = ctypes.c_int
+        nb.argtypes = [ctypes.c_int] * 2 + [_dbl_p] * 3 + [ctypes.c_double] + [_dbl_p] * 4
 
     @staticmethod
     def _arr(x, shape=None):
@@ -113,6 +119,36 @@ class Oracle:
             raise RuntimeError(f"m2rnn_ref_gate_forward failed with status {st}")
         return f
 
+    def gate_rmsnorm_forward(self, y, g, w, eps=0.0):
+        """Output gate and RMSNorm over the last axis: y, g [..., d], w [d].
+        Returns (o [..., d], rstd [...])."""
+        y = self._arr(y)
+        d = y.shape[-1]
+        g = self._arr(g, y.shape)
+        w = self._arr(w, (d,))
+        ntok = y.size // d
+        o, rstd = np.empty(y.shape), np.empty(y.shape[:-1])
+        st = self.lib.m2rnn_ref_gate_rmsnorm_forward(ntok, d, self._p(y), self._p(g), self._p(w), float(eps),
+                                                     self._p(o), self._p(rstd))
+        if st != 0:
+            raise RuntimeError(f"m2rnn_ref_gate_rmsnorm_forward failed with status {st}")
+        return o, rstd
+
+    def gate_rmsnorm_backward(self, y, g, w, dout, eps=0.0):
+        """(dy [..., d], dg [..., d], dw [d]) from dout [..., d]."""
+        y = self._arr(y)
+        d = y.shape[-1]
+        g = self._arr(g, y.shape)
+        w = self._arr(w, (d,))
+        dout = self._arr(dout, y.shape)
+        ntok = y.size // d
+        dy, dg, dw = np.empty(y.shape), np.empty(y.shape), np.empty(d)
+        st = self.lib.m2rnn_ref_gate_rmsnorm_backward(ntok, d, self._p(y), self._p(g), self._p(w), float(eps),
+                                                      self._p(dout), self._p(dy), self._p(dg), self._p(dw))
+        if st != 0:
+            raise RuntimeError(f"m2rnn_ref_gate_rmsnorm_backward failed with status {st}")
+        return dy, dg, dw
+
     def gate_backward(self, a, alpha, beta, df):
         """(da [B,T,N], dalpha [N], dbeta [N]) from df [B,T,N]."""
         a = self._arr(a)
@@ -148,6 +184,14 @@ def forward(*args, **kw):
 
 def backward(*args, **kw):
     return get().backward(*args, **kw)
+
+
+def gate_rmsnorm_forward(*args, **kw):
+    return get().gate_rmsnorm_forward(*args, **kw)
+
+
+def gate_rmsnorm_backward(*args, **kw):
+    return get().gate_rmsnorm_backward(*args, **kw)
 
 
 def gate_forward(*args, **kw):

@@ -369,3 +369,59 @@ int m2rnn_ref_gate_backward(int B, int T, int N, const double* a, const double* 
       }
   return 0;
 }
+
+/* ---------------------------------------------------- output gate, RMSNorm
+ * After the readout the block multiplies by the output gate g and applies
+ * RMSNorm over the token's d = N V features (slide "Most of the block can be
+ * computed before recurrence", paper Fig. 2), with the statistic of slide
+ * "Backup: RMSNormTP synchronizes per-token statistics" (paper App. C, Eqs.
+ * (26)-(33)), here over one device's whole feature vector:
+ *     x = y (.) g,   s = [ (1/d) sum_j x_j^2 + eps ]^{-1/2},   o_i = w_i x_i s
+ * (the pages omit eps; eps = 0 is their form).  Backward, as on that slide:
+ *     p_i = w_i do_i,   r = sum_j p_j x_j,   dx_i = s p_i - r s^3 x_i / d
+ * and by the chain rule through x = y (.) g and o = w (.) (x s):
+ *     dy = dx (.) g,   dg = dx (.) y,   dw_i = sum over tokens of do_i x_i s
+ * (tokens in ascending order).  One token is a row of d values. */
+int m2rnn_ref_gate_rmsnorm_forward(int ntok, int d, const double* y, const double* g, const double* w,
+                                   double eps, double* o, double* rstd) {
+  if (ntok < 0 || d < 1 || eps < 0.0 || !y || !g || !w || !o) return -1;
+  for (int t = 0; t < ntok; ++t) {
+    const double* yt = y + (size_t)t * d;
+    const double* gt = g + (size_t)t * d;
+    double ss = 0.0;
+    for (int j = 0; j < d; ++j) ss += (yt[j] * gt[j]) * (yt[j] * gt[j]);
+    const double s = 1.0 / sqrt(ss / d + eps);
+    for (int j = 0; j < d; ++j) o[(size_t)t * d + j] = w[j] * (yt[j] * gt[j]) * s;
+    if (rstd) rstd[t] = s;
+  }
+  return 0;
+}
+
+int m2rnn_ref_gate_rmsnorm_backward(int ntok, int d, const double* y, const double* g, const double* w,
+                                    double eps, const double* dout, double* dy, double* dg, double* dw) {
+  if (ntok < 0 || d < 1 || eps < 0.0 || !y || !g || !w || !dout || !dy || !dg || !dw) return -1;
+  double* x = (double*)malloc(sizeof(double) * d);
+  if (!x) return -2;
+  for (int j = 0; j < d; ++j) dw[j] = 0.0;
+  for (int t = 0; t < ntok; ++t) {
+    const double* yt = y + (size_t)t * d;
+    const double* gt = g + (size_t)t * d;
+    const double* dt = dout + (size_t)t * d;
+    double ss = 0.0;
+    for (int j = 0; j < d; ++j) {
+      x[j] = yt[j] * gt[j];
+      ss += x[j] * x[j];
+    }
+    const double s = 1.0 / sqrt(ss / d + eps);
+    double r = 0.0;
+    for (int j = 0; j < d; ++j) r += (w[j] * dt[j]) * x[j];
+    for (int j = 0; j < d; ++j) {
+      const double dx = s * (w[j] * dt[j]) - r * s * s * s * x[j] / d;
+      dy[(size_t)t * d + j] = dx * gt[j];
+      dg[(size_t)t * d + j] = dx * yt[j];
+      dw[j] += dt[j] * x[j] * s;
+    }
+  }
+  free(x);
+  return 0;
+}

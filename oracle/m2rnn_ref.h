@@ -71,6 +71,18 @@ int m2rnn_ref_gate_forward(int B, int T, int N, const double* a, const double* a
 int m2rnn_ref_gate_backward(int B, int T, int N, const double* a, const double* alpha, const double* beta,
                             const double* df, double* da, double* dalpha, double* dbeta);
 
+/* Output gate and RMSNorm after the readout (slide "Most of the block can be
+ * computed before recurrence", paper Fig. 2; statistic and backward of slide
+ * "Backup: RMSNormTP synchronizes per-token statistics", paper App. C, Eqs.
+ * (26)-(33)): per token row of d features, x = y (.) g,
+ * s = ((1/d) sum x^2 + eps)^{-1/2}, o = w (.) x s; rstd [ntok] (may be NULL)
+ * receives s.  Backward from dout: dy, dg [ntok][d] and dw [d] summed over
+ * tokens.  Return 0, -1 on a bad argument, -2 when out of memory. */
+int m2rnn_ref_gate_rmsnorm_forward(int ntok, int d, const double* y, const double* g, const double* w,
+                                   double eps, double* o, double* rstd);
+int m2rnn_ref_gate_rmsnorm_backward(int ntok, int d, const double* y, const double* g, const double* w,
+                                    double eps, const double* dout, double* dy, double* dg, double* dw);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,6 +20,10 @@ Sources (M2RNN paper-discussion slides, reading of arXiv:2603.14360v2):
         [BW] for C ends.
   [GT]  slide "The gate preserves a direct path through time", paper Sec. 3.1,
         Eqs. (13), (17): f = exp(-alpha softplus(a + beta)), alpha >= 0.
+  [NRM] slide "Most of the block can be computed before recurrence", paper
+        Fig. 2 (after the readout: times the output gate, then RMSNorm), with
+        the statistic and backward of slide "Backup: RMSNormTP synchronizes
+        per-token statistics", paper App. C, Eqs. (26)-(33).
 """
 import numpy as np
 import torch
@@ -518,6 +522,92 @@ def pin_gate_finite_differences(o):
         _close(got, fd, 1e-7 * max(1.0, float(np.max(np.abs(fd)))), f"gate FD {['da', 'dalpha', 'dbeta'][idx]}")
 
 
+def _norm_inputs(rng, ntok, d):
+    y = rng.standard_normal((ntok, d))
+    g = rng.standard_normal((ntok, d))
+    w = rng.standard_normal(d)
+    return y, g, w
+
+
+def pin_norm_torch_rms_norm(o):
+    """[NRM] against torch.nn.functional.rms_norm in float64 applied to the
+    gated features y * g, forward and (through torch autograd, including the
+    product with g) backward, with and without eps."""
+    rng = np.random.default_rng(RNG_SEED + 40)
+    y, g, w = _norm_inputs(rng, 6, 48)
+    dout = rng.standard_normal(y.shape)
+    for eps in (0.0, 1e-3):
+        out, rstd = o.gate_rmsnorm_forward(y, g, w, eps)
+        ty = torch.tensor(y, requires_grad=True)
+        tg = torch.tensor(g, requires_grad=True)
+        tw = torch.tensor(w, requires_grad=True)
+        ref = torch.nn.functional.rms_norm(ty * tg, (48,), weight=tw, eps=eps)
+        (ref * torch.tensor(dout)).sum().backward()
+        _close(out, ref.detach().numpy(), 1e-13, f"rmsnorm eps={eps}")
+        _close(rstd, 1.0 / np.sqrt(np.mean((y * g) ** 2, axis=-1) + eps), 1e-13, f"rstd eps={eps}")
+        dy, dg, dw = o.gate_rmsnorm_backward(y, g, w, dout, eps)
+        _close(dy, ty.grad.numpy(), 1e-12, f"rmsnorm dy eps={eps}")
+        _close(dg, tg.grad.numpy(), 1e-12, f"rmsnorm dg eps={eps}")
+        _close(dw, tw.grad.numpy(), 1e-12, f"rmsnorm dw eps={eps}")
+
+
+def pin_norm_invariances(o):
+    """[NRM] at eps = 0: the output does not change when a token's y is scaled
+    by c > 0 and flips sign with it; o / w has unit mean square per token; and
+    the gradient is orthogonal to the scaling direction (sum_j dy_j y_j = 0 and
+    sum_j dg_j g_j = 0 per token)."""
+    rng = np.random.default_rng(RNG_SEED + 41)
+    y, g, w = _norm_inputs(rng, 5, 32)
+    out, _ = o.gate_rmsnorm_forward(y, g, w)
+    c = np.array([0.01, 1.0, 3.0, 250.0, 7.5])[:, None]
+    _close(o.gate_rmsnorm_forward(y * c, g, w)[0], out, 1e-13, "rmsnorm scale invariance")
+    _close(o.gate_rmsnorm_forward(-y, g, w)[0], -out, 1e-15, "rmsnorm odd")
+    _close(np.mean((out / w) ** 2, axis=-1), np.ones(5), 1e-13, "rmsnorm unit rms")
+    dy, dg, _ = o.gate_rmsnorm_backward(y, g, w, rng.standard_normal(y.shape))
+    _close(np.sum(dy * y, axis=-1), np.zeros(5), 1e-12, "rmsnorm dy orthogonal to y")
+    _close(np.sum(dg * g, axis=-1), np.zeros(5), 1e-12, "rmsnorm dg orthogonal to g")
+
+
+def pin_norm_constant_token(o):
+    """[NRM] a token whose gated features all equal c: s = 1/|c| and
+    o = w sign(c) (eps = 0); with eps, s = 1/sqrt(c^2 + eps)."""
+    d = 20
+    y = np.array([[0.5] * d, [-4.0] * d])
+    g = np.array([[3.0] * d, [0.25] * d])
+    w = np.linspace(-1.0, 2.0, d)
+    out, rstd = o.gate_rmsnorm_forward(y, g, w)
+    _close(out, np.stack([w, -w]), 1e-15, "rmsnorm constant token")
+    _close(rstd, np.array([1.0 / 1.5, 1.0]), 1e-15, "rmsnorm constant rstd")
+    _, rstd = o.gate_rmsnorm_forward(y, g, w, 0.75)
+    _close(rstd, np.array([1.0 / np.sqrt(1.5 ** 2 + 0.75), 1.0 / np.sqrt(1.0 + 0.75)]), 1e-15, "rmsnorm eps rstd")
+
+
+def pin_norm_finite_differences(o):
+    """[NRM] backward against central differences of L = sum(o * dout) over
+    every element of y, g and w (eps = 1e-3)."""
+    rng = np.random.default_rng(RNG_SEED + 42)
+    y, g, w = _norm_inputs(rng, 3, 8)
+    dout = rng.standard_normal(y.shape)
+    eps = 1e-3
+    dy, dg, dw = o.gate_rmsnorm_backward(y, g, w, dout, eps)
+    ins = [y, g, w]
+    h = 1e-6
+    for idx, got in enumerate([dy, dg, dw]):
+        x = ins[idx]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            mi = it.multi_index
+            orig = x[mi]
+            x[mi] = orig + h
+            lp = float(np.sum(o.gate_rmsnorm_forward(*ins, eps)[0] * dout))
+            x[mi] = orig - h
+            lm = float(np.sum(o.gate_rmsnorm_forward(*ins, eps)[0] * dout))
+            x[mi] = orig
+            fd[mi] = (lp - lm) / (2 * h)
+        _close(got, fd, 1e-7 * max(1.0, float(np.max(np.abs(fd)))), f"rmsnorm FD {['dy', 'dg', 'dw'][idx]}")
+
+
 FORWARD_PINS = [pin_t1_closed_form, pin_f_one_forward, pin_zero_w_zero_f_forward, pin_readout_linear_in_q,
                 pin_checkpoints, pin_convex_bound, pin_permutations, pin_rnn_embedding_forward_backward]
 BACKWARD_PINS = [pin_f_one_backward, pin_zero_w_zero_f_backward, pin_finite_differences_small,
@@ -526,4 +616,5 @@ INITIAL_STATE_PINS = [pin_initial_state_f_one, pin_initial_state_forgotten, pin_
                       pin_finite_differences_initial_state]
 GATE_PINS = [pin_gate_sigmoid_identity, pin_gate_alpha_zero, pin_gate_power_law_and_range,
              pin_gate_large_arguments, pin_gate_finite_differences]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + INITIAL_STATE_PINS + GATE_PINS + [pin_thread_invariance]
+NORM_PINS = [pin_norm_torch_rms_norm, pin_norm_invariances, pin_norm_constant_token, pin_norm_finite_differences]
+ALL_PINS = FORWARD_PINS + BACKWARD_PINS + INITIAL_STATE_PINS + GATE_PINS + NORM_PINS + [pin_thread_invariance]

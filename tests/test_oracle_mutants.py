@@ -60,6 +60,24 @@ MUTANTS = [
     ("da_wrong_derivative", "da[i] = df[i] * f * (-alpha[n]) * sig;", "da[i] = df[i] * f * (-alpha[n]) * (1.0 - sig);"),
     ("dalpha_drops_f", "dalpha[n] += df[i] * f * (-sp);", "dalpha[n] += df[i] * (-sp);"),
     ("dbeta_is_df", "dbeta[n] += da[i];", "dbeta[n] += df[i];"),
+    ("norm_drops_mean", "const double s = 1.0 / sqrt(ss / d + eps);\n    for (int j = 0; j < d; ++j) o[",
+     "const double s = 1.0 / sqrt(ss + eps);\n    for (int j = 0; j < d; ++j) o["),
+    ("norm_eps_outside_root", "const double s = 1.0 / sqrt(ss / d + eps);\n    for (int j = 0; j < d; ++j) o[",
+     "const double s = 1.0 / sqrt(ss / d) + eps;\n    for (int j = 0; j < d; ++j) o["),
+    ("norm_forward_drops_gate", "o[(size_t)t * d + j] = w[j] * (yt[j] * gt[j]) * s;", "o[(size_t)t * d + j] = w[j] * yt[j] * s;"),
+    ("norm_forward_drops_weight", "o[(size_t)t * d + j] = w[j] * (yt[j] * gt[j]) * s;",
+     "o[(size_t)t * d + j] = (yt[j] * gt[j]) * s;"),
+    ("norm_dx_drops_r", "const double dx = s * (w[j] * dt[j]) - r * s * s * s * x[j] / d;",
+     "const double dx = s * (w[j] * dt[j]);"),
+    ("norm_dx_s_squared", "const double dx = s * (w[j] * dt[j]) - r * s * s * s * x[j] / d;",
+     "const double dx = s * (w[j] * dt[j]) - r * s * s * x[j] / d;"),
+    ("norm_dx_drops_weight", "const double dx = s * (w[j] * dt[j]) - r * s * s * s * x[j] / d;",
+     "const double dx = s * dt[j] - r * s * s * s * x[j] / d;"),
+    ("norm_r_drops_weight", "r += (w[j] * dt[j]) * x[j];", "r += dt[j] * x[j];"),
+    ("norm_dy_uses_y", "dy[(size_t)t * d + j] = dx * gt[j];", "dy[(size_t)t * d + j] = dx * yt[j];"),
+    ("norm_dg_uses_g", "dg[(size_t)t * d + j] = dx * yt[j];", "dg[(size_t)t * d + j] = dx * gt[j];"),
+    ("norm_dw_drops_s", "dw[j] += dt[j] * x[j] * s;", "dw[j] += dt[j] * x[j];"),
+    ("norm_dw_uses_y", "dw[j] += dt[j] * x[j] * s;", "dw[j] += dt[j] * yt[j] * s;"),
 ]
 
 
