@@ -33,7 +33,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--pass", dest="which", choices=["fwdbwd", "fwd"], default="fwdbwd")
+    ap.add_argument("--pass", dest="which", choices=["fwdbwd", "fwd", "epilogue"], default="fwdbwd",
+                    help="epilogue: the output gate and RMSNorm after the readout, forward + backward")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
@@ -120,8 +121,102 @@ def cpu_baseline(w, x, which, threads, seconds):
                       f"{dt:.1f} s on {min(nthreads, Bs * Ns)} threads"}
 
 
+def bench_epilogue(args):
+    """Output gate and RMSNorm over the B=32, T=4096, N=64 readout (d = 1024
+    features per token, bf16 gate and weight): forward then backward per step.
+    HBM-bound, so the roofline object prices the backward launch's algorithmic
+    bytes (y, g, dout read; dy, dg written) against MI355X's 8 TB/s."""
+    import torch
+    import m2rnn_inputs
+    import non_linear_matrix_amd as m2
+    B, T, N, dtype = 32, 4096, 64, "bf16"
+    name = f"gate_rmsnorm_{dtype}_B{B}_T{T}_N{N}"
+    d = N * V_DIM
+    x_cpu = m2rnn_inputs.make_epilogue(B, T, N, dtype, seed=args.seed)
+    x = {k: v.cuda() for k, v in x_cpu.items()}
+    dev = x["y"].device
+    out = torch.empty_like(x["y"])
+    rstd = torch.empty((B, T), device=dev)
+    grads = (torch.empty_like(x["y"]), torch.empty_like(x["y"]), torch.empty((d,), device=dev))
+    ws = torch.empty((m2.m2rnn_gate_rmsnorm_backward_workspace_bytes(B, T, N, V_DIM),), device=dev, dtype=torch.uint8)
+    stream = torch.cuda.current_stream(dev)
+    if args.copy_calibration_bytes > 0:
+        src = torch.empty(args.copy_calibration_bytes // 4, device=dev, dtype=torch.float32).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        m2.gate_rmsnorm_forward(x["y"], x["g"], x["w"], out=out, rstd=rstd)
+        if ev is not None:
+            ev[1].record(stream)
+        m2.gate_rmsnorm_backward(x["y"], x["g"], x["w"], x["dout"], out=grads, workspace=ws)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    ntok = B * T
+    es = 2 if dtype == "bf16" else 4
+    fwd_bytes = ntok * d * (4 + es + 4) + ntok * 4            # y, g read; out, rstd written
+    bwd_bytes = ntok * d * (4 + es + 4 + 4 + 4)               # y, g, dout read; dy, dg written
+    achieved = bwd_bytes / (bwd_ms * 1e-3) / 1e9
+    htok = ntok * N
+    res = {
+        "metric": "M2RNN output gate + RMSNorm head-tokens/s (N*V = 1024 features per token) fwd & bwd; "
+                  "% of HBM roofline",
+        "value": htok * args.steps / (total_ms * 1e-3),
+        "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; y = 3 N(0,1), g = sigmoid(N(0,1)), w = 1 + N(0,1/100), dout = N(0,1))",
+        "config": {"workload": name, "pass": "forward+backward", "B": B, "T": T, "N": N, "V": V_DIM,
+                   "input_dtype": dtype, "eps": 0.0},
+        "copy_calibration_bytes": args.copy_calibration_bytes,
+        "fwd_ms": fwd_ms, "bwd_ms": bwd_ms,
+        "fwd_GBs": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(name, "bwd"),
+                     "kernel": "m2rnn_gate_rmsnorm_backward (norm_bwd_kernel + two dw reduction launches)",
+                     "kernel_ms": bwd_ms,
+                     "algorithmic": f"{bwd_bytes // ntok} B/token x {ntok} tokens per launch"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = max(1, min(ntok, int(args.cpu_seconds * 2.0e5)))   # ~5 us per token row fwd + bwd
+        yy = x_cpu["y"].reshape(-1, d)[:rows].double().numpy()
+        gg = x_cpu["g"].reshape(-1, d)[:rows].double().numpy()
+        ww = x_cpu["w"].reshape(d).double().numpy()
+        dd = x_cpu["dout"].reshape(-1, d)[:rows].double().numpy()
+        c0 = time.perf_counter()
+        oracle.gate_rmsnorm_forward(yy, gg, ww)
+        oracle.gate_rmsnorm_backward(yy, gg, ww, dd)
+        dt = time.perf_counter() - c0
+        res["cpu_baseline"] = {"value": rows * N / dt, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"forward+backward of the fp64 oracle on the first {rows} token rows "
+                                         f"(d = {d}) of the same inputs, {dt:.1f} s on 1 thread"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main():
     args = parse()
+    if args.which == "epilogue" and args.gpus == 1:
+        return bench_epilogue(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the scan shards over batch rows/heads with no communication, "
@@ -196,8 +291,9 @@ def main():
     # dominant kernel and its algorithmic MFMA work per launch
     if args.which == "fwdbwd" and bwd_ms > fwd_ms:
         # the backward call: replay, reverse-sweep and reduction launches on one stream
-        dom, dom_ms, flops = ("m2rnn_backward (m2rnn_fwd_kernel<...,true> replay + m2rnn_bwd_kernel + "
-                              "m2rnn_bwd_reduce_kernel)"), bwd_ms, 3 * FLOP_PER_CONTRACTION * htok
+        dom = ("m2rnn_backward (m2rnn_fwd_kernel<...,true> replay + m2rnn_bwd_kernel + "
+               "m2rnn_bwd_reduce_qk_kernel + m2rnn_bwd_reduce_head_kernel)")
+        dom_ms, flops = bwd_ms, 3 * FLOP_PER_CONTRACTION * htok
         traffic = profiled_traffic(name, "bwd")
     else:
         dom, dom_ms, flops = "m2rnn_fwd_kernel", fwd_ms, FLOP_PER_CONTRACTION * htok

@@ -164,6 +164,47 @@ int m2rnn_backward_gated(int B, int T, int N, int K, int V, int dtype,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Output gate and RMSNorm after the readout (slide "Most of the block can be
+ * computed before recurrence", paper Fig. 2), with the per-token statistic of
+ * slide "Backup: RMSNormTP synchronizes per-token statistics" (paper App. C,
+ * Eqs. (26)-(33)) over the token's d = N V features on this GPU:
+ *       x = y (.) g,   s = ((1/d) sum_j x_j^2 + eps)^{-1/2},   out = w (.) x s
+ * (the pages omit eps: eps = 0 is their form; a token whose x is all zero
+ * then gives non-finite output).
+ *   y     [B][T][N][V] float32 (the scan's readout)
+ *   g     [B][T][N][V] output gate (dtype `dtype`), 4-element aligned
+ *   w     [N][V]       RMSNorm weight (dtype `dtype`), 4-element aligned
+ *   eps   >= 0, finite
+ *   out   [B][T][N][V] float32 out; may be the same buffer as y
+ *   rstd  [B][T] float32 out (s of each token), or NULL
+ * N V must be a multiple of 4 and at most 2048 (else M2RNN_ERR_UNSUPPORTED).
+ */
+int m2rnn_gate_rmsnorm_forward(int B, int T, int N, int V, int dtype,
+                               const float* y, const void* g, const void* w, float eps,
+                               float* out, float* rstd, void* stream);
+
+/* Bytes of device workspace m2rnn_gate_rmsnorm_backward needs (0 if none). */
+size_t m2rnn_gate_rmsnorm_backward_workspace_bytes(int B, int T, int N, int V);
+
+/*
+ * Backward of m2rnn_gate_rmsnorm_forward, as on slide "Backup: RMSNormTP
+ * synchronizes per-token statistics": with p = w (.) dout and
+ * r = sum_j p_j x_j per token, dx = s p - (r s^3 / d) x, and then
+ *       dy = dx (.) g,   dg = dx (.) y,   dw = sum over tokens of dout (.) x s.
+ *   y, g, w, eps   the forward's inputs
+ *   dout  [B][T][N][V] float32
+ *   dy, dg [B][T][N][V] float32 out (dy may be the same buffer as dout)
+ *   dw    [N][V] float32 out, summed over tokens in a fixed order
+ *   workspace      m2rnn_gate_rmsnorm_backward_workspace_bytes(...) bytes,
+ *                  16-byte aligned; contents on entry are ignored
+ * B T == 0 sets dw = 0.
+ */
+int m2rnn_gate_rmsnorm_backward(int B, int T, int N, int V, int dtype,
+                                const float* y, const void* g, const void* w, float eps,
+                                const float* dout, float* dy, float* dg, float* dw,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * One token of the recurrence for every (b, n), state held by the caller
  * (decoding): the forward of slide "Write, transform, retain, and read a
  * matrix state" for T = 1 from H, with H overwritten by the new state.

@@ -22,6 +22,15 @@ make_gate draws, from its own generator:
     alpha = U[0.5, 2)              [N]
     beta  = U[-1, 1)               [N]
 
+For the output gate and RMSNorm after the readout (slide "Most of the block
+can be computed before recurrence", paper Fig. 2), make_epilogue draws, from
+its own generator, in this order:
+
+    y    = 3 N(0, 1)               [B, T, N, V]  float32 (the scale of a readout)
+    g    = sigmoid(N(0, 1))        [B, T, N, V]  output gate
+    w    = 1 + N(0, 1/100)         [N, V]        RMSNorm weight
+    dout = N(0, 1)                 [B, T, N, V]  float32
+
 Draw order is fixed (q, k, v, f, W, w_r, dy) from one CPU torch.Generator
 seeded with `seed`; every tensor is drawn in float32 and, for bfloat16
 workloads, rounded to bfloat16 with round-to-nearest-even.  dy stays float32.
@@ -117,3 +126,16 @@ def make_gate(B, T, N, dtype="f32", mu=2.0, seed=0):
     alpha = torch.rand(N, generator=g, dtype=torch.float32) * 1.5 + 0.5
     beta = torch.rand(N, generator=g, dtype=torch.float32) * 2.0 - 1.0
     return {"a": a.to(td).contiguous(), "alpha": alpha.to(td).contiguous(), "beta": beta.to(td).contiguous()}
+
+
+def make_epilogue(B, T, N, dtype="f32", seed=0, V=V_DIM):
+    """Seeded inputs of the output gate and RMSNorm: dict of CPU tensors y,
+    dout (float32) and g, w in `dtype`."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 104729)
+    td = torch_dtype(dtype)
+    y = torch.randn(B, T, N, V, generator=g, dtype=torch.float32) * 3.0
+    gate = torch.sigmoid(torch.randn(B, T, N, V, generator=g, dtype=torch.float32))
+    w = 1.0 + 0.1 * torch.randn(N, V, generator=g, dtype=torch.float32)
+    dout = torch.randn(B, T, N, V, generator=g, dtype=torch.float32)
+    return {"y": y.contiguous(), "g": gate.to(td).contiguous(), "w": w.to(td).contiguous(), "dout": dout.contiguous()}

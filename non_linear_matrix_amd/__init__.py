@@ -13,6 +13,8 @@ is no CPU fallback.
     y_t = m2.decode(q_t, k_t, v_t, f_t, W, w_r, H)              # one token, H updated
     y, H_T = m2.forward_gated(q, k, v, a, alpha, beta, W, w_r)  # f from the gate
     grads = m2.backward_gated(q, k, v, a, alpha, beta, W, w_r, H_ckpt, 64, dy)
+    o = m2.gate_rmsnorm_forward(y, g, w_o)                      # RMSNorm(y * g) * w_o
+    dy, dg, dw_o = m2.gate_rmsnorm_backward(y, g, w_o, do)
 
 Shapes (K = 64, V = 16): q, k [B,T,K]; v [B,T,N,V]; f [B,T,N]; W [N,V,V];
 w_r [N,V]; gate pre-activation a [B,T,N] and alpha, beta [N] in place of f;
@@ -54,6 +56,13 @@ lib.m2rnn_forward_gated.argtypes = [_i] * 6 + [_p] * 9 + [_p, _p, _p, _i, _p]
 lib.m2rnn_backward_gated.restype = _i
 lib.m2rnn_backward_gated.argtypes = ([_i] * 6 + [_p] * 8 + [_p, _i] + [_p, _p] + [_p] * 9
                                      + [_p, ctypes.c_size_t, _p])
+lib.m2rnn_gate_rmsnorm_forward.restype = _i
+lib.m2rnn_gate_rmsnorm_forward.argtypes = [_i] * 5 + [_p] * 3 + [ctypes.c_float] + [_p, _p, _p]
+lib.m2rnn_gate_rmsnorm_backward_workspace_bytes.restype = ctypes.c_size_t
+lib.m2rnn_gate_rmsnorm_backward_workspace_bytes.argtypes = [_i] * 4
+lib.m2rnn_gate_rmsnorm_backward.restype = _i
+lib.m2rnn_gate_rmsnorm_backward.argtypes = ([_i] * 5 + [_p] * 3 + [ctypes.c_float] + [_p] * 4
+                                            + [_p, ctypes.c_size_t, _p])
 lib.m2rnn_decode.restype = _i
 lib.m2rnn_decode.argtypes = [_i] * 5 + [_p] * 6 + [_p, _p, _p]
 lib.m2rnn_last_error.restype = ctypes.c_char_p
@@ -232,3 +241,50 @@ def decode(q, k, v, f, W, w_r, H, y=None):
     _check(lib.m2rnn_decode(B, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r),
                             _ptr(H), _ptr(y), _stream(q.device)))
     return y
+
+
+def m2rnn_gate_rmsnorm_forward(B, T, N, V_, dtype, y, g, w, eps, out, rstd, stream):
+    """Raw C-ABI call with ctypes pointers; returns the status code."""
+    return lib.m2rnn_gate_rmsnorm_forward(B, T, N, V_, dtype, y, g, w, eps, out, rstd, stream)
+
+
+def m2rnn_gate_rmsnorm_backward(B, T, N, V_, dtype, y, g, w, eps, dout, dy, dg, dw, workspace, workspace_bytes,
+                                stream):
+    """Raw C-ABI call with ctypes pointers; returns the status code."""
+    return lib.m2rnn_gate_rmsnorm_backward(B, T, N, V_, dtype, y, g, w, eps, dout, dy, dg, dw, workspace,
+                                           workspace_bytes, stream)
+
+
+def m2rnn_gate_rmsnorm_backward_workspace_bytes(B, T, N, V_=V):
+    return int(lib.m2rnn_gate_rmsnorm_backward_workspace_bytes(B, T, N, V_))
+
+
+def gate_rmsnorm_forward(y, g, w, eps=0.0, out=None, rstd=None):
+    """out = w * x * s with x = y * g and s = (mean over the N*V features of
+    x^2 + eps)^-1/2, per token.  y [B,T,N,V] float32; g like y and w [N,V]
+    (or [N*V]) in the input dtype.  Returns out [B,T,N,V] float32 (`out` may
+    be y itself); `rstd` [B,T] float32, if given, receives s."""
+    B, T, N, Vv = y.shape
+    if out is None:
+        out = torch.empty_like(y, dtype=torch.float32)
+    _check(lib.m2rnn_gate_rmsnorm_forward(B, T, N, Vv, _dtype_code(g), _ptr(y), _ptr(g), _ptr(w), float(eps),
+                                          _ptr(out), _ptr(rstd), _stream(y.device)))
+    return out
+
+
+def gate_rmsnorm_backward(y, g, w, dout, eps=0.0, out=None, workspace=None):
+    """Gradients of sum(out * dout) for gate_rmsnorm_forward: (dy [B,T,N,V],
+    dg [B,T,N,V], dw [N*V]) float32.  `out` may pass (dy, dg, dw)."""
+    B, T, N, Vv = y.shape
+    dev = y.device
+    if out is None:
+        out = (torch.empty_like(y, dtype=torch.float32), torch.empty_like(y, dtype=torch.float32),
+               torch.empty((N * Vv,), device=dev, dtype=torch.float32))
+    nbytes = int(lib.m2rnn_gate_rmsnorm_backward_workspace_bytes(B, T, N, Vv))
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty((nbytes,), device=dev, dtype=torch.uint8)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.m2rnn_gate_rmsnorm_backward(B, T, N, Vv, _dtype_code(g), _ptr(y), _ptr(g), _ptr(w), float(eps),
+                                           _ptr(dout), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(workspace),
+                                           wbytes, _stream(dev)))
+    return out

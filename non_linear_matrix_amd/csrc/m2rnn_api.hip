@@ -218,3 +218,79 @@ extern "C" int m2rnn_decode(int B, int N, int K, int V, int dtype, const void* q
   if ((long long)B * N > 0 && !H) return fail(M2RNN_ERR_INVALID_ARG, "H must not be NULL");
   return m2rnn_forward(B, 1, N, K, V, dtype, q, k, v, f, W, w_r, H, y, H, nullptr, 0, stream);
 }
+
+// ------------------------------------------------- output gate and RMSNorm
+namespace {
+
+int norm_check(int B, int T, int N, int V, int dtype, float eps, long long* ntok, int* d) {
+  if (B < 0 || T < 0 || N < 0 || V < 0)
+    return fail(M2RNN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d T=%d N=%d V=%d)", B, T, N, V);
+  if (dtype != M2RNN_F32 && dtype != M2RNN_BF16) return fail(M2RNN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(M2RNN_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  const long long dd = (long long)N * V;
+  if (dd % 4 != 0 || dd > m2rnn::kNormMaxD)
+    return fail(M2RNN_ERR_UNSUPPORTED, "N*V must be a multiple of 4 and at most %d (got %lld)", m2rnn::kNormMaxD, dd);
+  if ((long long)B * T * dd > kMaxElems) return fail(M2RNN_ERR_UNSUPPORTED, "problem too large");
+  *ntok = (long long)B * T;
+  *d = (int)dd;
+  return M2RNN_OK;
+}
+
+}  // namespace
+
+extern "C" int m2rnn_gate_rmsnorm_forward(int B, int T, int N, int V, int dtype, const float* y, const void* g,
+                                          const void* w, float eps, float* out, float* rstd, void* stream) {
+  g_err[0] = 0;
+  long long ntok;
+  int d, st;
+  if ((st = norm_check(B, T, N, V, dtype, eps, &ntok, &d))) return st;
+  const size_t es = dtype == M2RNN_F32 ? 4 : 2;
+  const long long n = ntok * d;
+  if ((st = need(y, "y", n, 16)) || (st = need(g, "g", n, 4 * es)) || (st = need(w, "w", n > 0 ? d : 0, 4 * es)) ||
+      (st = need(out, "out", n, 16)))
+    return st;
+  if (rstd && !aligned(rstd, 4)) return fail(M2RNN_ERR_INVALID_ARG, "rstd must be 4-byte aligned");
+  if (n == 0) return M2RNN_OK;
+  m2rnn::NormArgs a{};
+  a.y = y; a.g = g; a.w = w; a.out = out; a.rstd = rstd; a.ntok = ntok; a.d = d; a.eps = eps;
+  hipError_t e = m2rnn::launch_norm_forward(a, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "gate_rmsnorm forward launch: %s", hipGetErrorString(e));
+}
+
+extern "C" size_t m2rnn_gate_rmsnorm_backward_workspace_bytes(int B, int T, int N, int V) {
+  if (B < 0 || T < 0 || N < 0 || V < 0) return 0;
+  const long long ntok = (long long)B * T, d = (long long)N * V;
+  if (ntok == 0 || d == 0 || d % 4 != 0 || d > m2rnn::kNormMaxD) return 0;
+  return sizeof(float) * m2rnn::norm_backward_workspace_floats(ntok, (int)d);
+}
+
+extern "C" int m2rnn_gate_rmsnorm_backward(int B, int T, int N, int V, int dtype, const float* y, const void* g,
+                                           const void* w, float eps, const float* dout, float* dy, float* dg,
+                                           float* dw, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  long long ntok;
+  int d, st;
+  if ((st = norm_check(B, T, N, V, dtype, eps, &ntok, &d))) return st;
+  const size_t es = dtype == M2RNN_F32 ? 4 : 2;
+  const long long n = ntok * d;
+  if ((st = need(y, "y", n, 16)) || (st = need(g, "g", n, 4 * es)) || (st = need(w, "w", n > 0 ? d : 0, 4 * es)) ||
+      (st = need(dout, "dout", n, 16)) || (st = need(dy, "dy", n, 16)) || (st = need(dg, "dg", n, 16)) ||
+      (st = need(dw, "dw", d, 16)))
+    return st;
+  hipStream_t s = (hipStream_t)stream;
+  if (d == 0) return M2RNN_OK;
+  if (ntok == 0) {   // dw = 0
+    hipError_t e = m2rnn::launch_fill_zero(dw, (size_t)d, s);
+    return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "dw = 0: %s", hipGetErrorString(e));
+  }
+  const size_t need_bytes = m2rnn_gate_rmsnorm_backward_workspace_bytes(B, T, N, V);
+  if (!workspace || workspace_bytes < need_bytes)
+    return fail(M2RNN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(M2RNN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  m2rnn::NormArgs a{};
+  a.y = y; a.g = g; a.w = w; a.dout = dout; a.dy = dy; a.dg = dg; a.dw = dw; a.ws = (float*)workspace;
+  a.ntok = ntok; a.d = d; a.eps = eps;
+  hipError_t e = m2rnn::launch_norm_backward(a, dtype, s);
+  return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "gate_rmsnorm backward launch: %s", hipGetErrorString(e));
+}

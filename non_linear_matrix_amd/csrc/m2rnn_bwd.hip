@@ -560,45 +560,69 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   }
 }
 
-// Fixed-order sums over workgroups (dq, dk), batch rows and row tiles (dW),
-// and batch rows (dw_r).
-__global__ void m2rnn_bwd_reduce_kernel(BwdArgs a) {
+// Fixed-order sums over workgroups of the dq, dk partials.
+__global__ void m2rnn_bwd_reduce_qk_kernel(BwdArgs a) {
   const size_t nqk = (size_t)a.B * a.T * 32;   // float4 groups of dq and dk
-  const size_t nW = (size_t)a.N * 64;          // float4 groups of dW
-  const size_t nwr = (size_t)a.N * 4;
-  const size_t ngate = a.ga ? (size_t)a.N : 0;   // dalpha, dbeta of each head
-  const size_t total = nqk + nW + nwr + ngate;
-  for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (size_t)gridDim.x * blockDim.x) {
-    if (u < nqk) {
-      const size_t bt = u / 32;
-      const int e = (int)(u % 32) * 4;
-      const size_t b = bt / a.T, t = bt % a.T;
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int gp = 0; gp < a.ngroups; ++gp) acc += *(const f4*)(a.ws_dqk + ((b * a.ngroups + gp) * a.T + t) * 128 + e);
-      float* dst = e < 64 ? a.dq + bt * 64 + e : a.dk + bt * 64 + (e - 64);
-      *(f4*)dst = acc;
-    } else if (u < nqk + nW) {
-      const size_t v = u - nqk;
-      const size_t n = v / 64;
-      const int e = (int)(v % 64) * 4;
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int b = 0; b < a.B; ++b)
-        for (int jt = 0; jt < 4; ++jt) acc += *(const f4*)(a.ws_dW + (((size_t)b * a.N + n) * 4 + jt) * 256 + e);
-      *(f4*)(a.dW + n * 256 + e) = acc;
-    } else if (u < nqk + nW + nwr) {
-      const size_t v = u - nqk - nW;
-      const size_t n = v / 4;
-      const int e = (int)(v % 4) * 4;
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int b = 0; b < a.B; ++b) acc += *(const f4*)(a.ws_dwr + ((size_t)b * a.N + n) * 16 + e);
-      *(f4*)(a.dw_r + n * 16 + e) = acc;
-    } else {
-      const size_t n = u - nqk - nW - nwr;
-      f2 acc = {0.f, 0.f};
-      for (int b = 0; b < a.B; ++b) acc += *(const f2*)(a.ws_dgate + ((size_t)b * a.N + n) * 2);
-      a.dalpha[n] = acc[0];
-      a.dbeta[n] = acc[1];
+  for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < nqk; u += (size_t)gridDim.x * blockDim.x) {
+    const size_t bt = u / 32;
+    const int e = (int)(u % 32) * 4;
+    const size_t b = bt / a.T, t = bt % a.T;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int gp = 0; gp < a.ngroups; ++gp) acc += *(const f4*)(a.ws_dqk + ((b * a.ngroups + gp) * a.T + t) * 128 + e);
+    float* dst = e < 64 ? a.dq + bt * 64 + e : a.dk + bt * 64 + (e - 64);
+    *(f4*)dst = acc;
+  }
+}
+
+// Per-head sums over batch rows (and row tiles) of the dW, dw_r and gate
+// partials, one workgroup per head.  Thread (jt, c) of the first 256 sums the
+// dW partials of row tile jt, column group c over the batch rows (b
+// ascending, in four interleaved accumulators so that the loads overlap);
+// the four row tiles are then added in order.  dw_r and the gate sums use 16
+// interleaved lanes per value the same way.
+__global__ __launch_bounds__(256) void m2rnn_bwd_reduce_head_kernel(BwdArgs a) {
+  __shared__ f4 tiles[4][64];
+  __shared__ f4 wr[16][4];
+  __shared__ f2 gt[16];
+  const int n = blockIdx.x, tid = threadIdx.x;
+  {
+    const int jt = tid / 64, c = tid % 64;
+    f4 acc[4] = {};
+    int b = 0;
+    for (; b + 3 < a.B; b += 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        acc[q] += *(const f4*)(a.ws_dW + (((size_t)(b + q) * a.N + n) * 4 + jt) * 256 + c * 4);
     }
+    for (int q = 0; b < a.B; ++b, ++q) acc[q] += *(const f4*)(a.ws_dW + (((size_t)b * a.N + n) * 4 + jt) * 256 + c * 4);
+    tiles[jt][c] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  }
+  if (tid < 64) {
+    // dw_r: lane l (of 16) sums batch rows b = l, l + 16, ... of column group cg
+    const int l = tid / 4, cg = tid % 4;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int b = l; b < a.B; b += 16) acc += *(const f4*)(a.ws_dwr + ((size_t)b * a.N + n) * 16 + cg * 4);
+    wr[l][cg] = acc;
+  } else if (a.ga && tid < 80) {
+    const int l = tid - 64;
+    f2 acc = {0.f, 0.f};
+    for (int b = l; b < a.B; b += 16) acc += *(const f2*)(a.ws_dgate + ((size_t)b * a.N + n) * 2);
+    gt[l] = acc;
+  }
+  __syncthreads();
+  if (tid < 64) *(f4*)(a.dW + (size_t)n * 256 + tid * 4) = (tiles[0][tid] + tiles[1][tid]) + (tiles[2][tid] + tiles[3][tid]);
+  if (tid < 4) {
+    f4 acc = wr[0][tid];
+#pragma unroll
+    for (int l = 1; l < 16; ++l) acc += wr[l][tid];
+    *(f4*)(a.dw_r + (size_t)n * 16 + tid * 4) = acc;
+  }
+  if (a.ga && tid == 0) {
+    f2 acc = gt[0];
+#pragma unroll
+    for (int l = 1; l < 16; ++l) acc += gt[l];
+    a.dalpha[n] = acc[0];
+    a.dbeta[n] = acc[1];
   }
 }
 
@@ -634,10 +658,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((m2rnn_bwd_kernel<TIn, kBwdHPW, GATE>), grid, block, Cfg::kBytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const size_t total = (size_t)a.B * a.T * 32 + (size_t)a.N * (68 + (a.ga ? 1 : 0));
-  size_t blocks = (total + 255) / 256;
+  size_t blocks = ((size_t)a.B * a.T * 32 + 255) / 256;
   if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(m2rnn_bwd_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(m2rnn_bwd_reduce_qk_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(m2rnn_bwd_reduce_head_kernel, dim3((unsigned)a.N), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

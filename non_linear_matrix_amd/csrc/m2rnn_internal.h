@@ -48,6 +48,26 @@ int backward_sub_steps();
 // from the caller's checkpoints into the workspace) runs first.
 hipError_t launch_backward(const BwdArgs& a, const FwdArgs& replay, int dtype, hipStream_t stream);
 
+// Output gate and RMSNorm after the readout: per token row of d features,
+// x = y * g, s = ((1/d) sum x^2 + eps)^{-1/2}, out = w * x * s.
+struct NormArgs {
+  const float* y;
+  const void *g, *w;       // input dtype
+  const float* dout;       // backward
+  float *out, *rstd;       // forward (rstd may be nullptr)
+  float *dy, *dg, *dw;     // backward
+  float* ws;               // backward: dw partials [nwg][d], then [32][d]
+  long long ntok;
+  int d;
+  float eps;
+};
+constexpr int kNormMaxD = 2048;
+// Workgroups (and dw partial rows) of the backward, and its workspace.
+int norm_backward_groups(long long ntok, int d);
+size_t norm_backward_workspace_floats(long long ntok, int d);
+hipError_t launch_norm_forward(const NormArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_norm_backward(const NormArgs& a, int dtype, hipStream_t stream);
+
 // Zero `n` floats with a plain fill kernel (graph-capture friendly).
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
 // dst[i] = src[i] for `n` floats with a plain copy kernel; dst == src is allowed.

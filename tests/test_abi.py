@@ -25,7 +25,9 @@ def m2():
 
 def test_header_declares_the_entry_points():
     assert declared() == ["m2rnn_backward", "m2rnn_backward_gated", "m2rnn_backward_workspace_bytes",
-                          "m2rnn_decode", "m2rnn_forward", "m2rnn_forward_gated", "m2rnn_last_error"]
+                          "m2rnn_decode", "m2rnn_forward", "m2rnn_forward_gated", "m2rnn_gate_rmsnorm_backward",
+                          "m2rnn_gate_rmsnorm_backward_workspace_bytes", "m2rnn_gate_rmsnorm_forward",
+                          "m2rnn_last_error"]
 
 
 def test_library_exports_every_declared_symbol(m2):
@@ -99,3 +101,30 @@ def test_gated_argument_errors_without_launch(m2):
     assert "da must" in m2.m2rnn_last_error()
     assert bg(1, 4, 2, 64, 16, 0, *q3, dummy, dummy, dummy, dummy, dummy, dummy, 64, dummy, None, *g3, dummy,
               dummy, dummy, dummy, dummy, None, dummy, 16, None) == m2.M2RNN_ERR_WORKSPACE
+
+
+def test_gate_rmsnorm_argument_errors_without_launch(m2):
+    dummy = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    fwd = m2.lib.m2rnn_gate_rmsnorm_forward
+    # B, T, N, V, dtype, y, g, w, eps, out, rstd, stream
+    assert fwd(2, 3, 5, 16, 0, dummy, dummy, dummy, ctypes.c_float(-1.0), dummy, None, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert "eps" in m2.m2rnn_last_error()
+    assert fwd(2, 3, 129, 16, 0, dummy, dummy, dummy, 0.0, dummy, None, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert fwd(2, 3, 1, 3, 0, dummy, dummy, dummy, 0.0, dummy, None, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert fwd(2, 3, 5, 16, 2, dummy, dummy, dummy, 0.0, dummy, None, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert fwd(2, 3, 5, 16, 0, None, dummy, dummy, 0.0, dummy, None, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert fwd(2, 3, 5, 16, 1, dummy, ctypes.c_void_p(260), dummy, 0.0, dummy, None, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert "g must be 8-byte aligned" in m2.m2rnn_last_error()
+    assert fwd(2, 3, 5, 16, 0, dummy, dummy, dummy, 0.0, dummy, ctypes.c_void_p(258), None) == \
+        m2.M2RNN_ERR_INVALID_ARG
+    ws = m2.m2rnn_gate_rmsnorm_backward_workspace_bytes
+    # one dw partial row per workgroup of four token rows (at most 1024), then 32 second-level rows
+    assert ws(2, 3, 5, 16) == (2 + 32) * 80 * 4 and ws(2, 3, 5, 3) == 0 and ws(0, 3, 5, 16) == 0
+    assert ws(64, 4096, 64, 16) == (1024 + 32) * 1024 * 4 and ws(64, 4096, 8, 16) == (1024 + 32) * 128 * 4
+    bwd = m2.lib.m2rnn_gate_rmsnorm_backward
+    # ..., dout, dy, dg, dw, workspace, bytes, stream
+    assert bwd(2, 3, 5, 16, 0, dummy, dummy, dummy, 0.0, dummy, dummy, dummy, dummy, dummy, 16, None) == \
+        m2.M2RNN_ERR_WORKSPACE
+    assert bwd(2, 3, 5, 16, 0, dummy, dummy, dummy, 0.0, dummy, dummy, None, dummy, dummy, 1 << 20, None) == \
+        m2.M2RNN_ERR_INVALID_ARG
+    assert "dg" in m2.m2rnn_last_error()
