@@ -44,6 +44,12 @@ class Oracle:
         nf = self.lib.m2rnn_ref_gate_rmsnorm_forward
         nf.restype = ctypes.c_int
         nf.argtypes = [ctypes.c_int] * 2 + [_dbl_p] * 3 + [ctypes.c_double] + [_dbl_p] * 2
+        cf = self.lib.m2rnn_ref_conv_silu_forward
+        cf.restype = ctypes.c_int
+        cf.argtypes = [ctypes.c_int] * 3 + [_dbl_p] * 4
+        cb = self.lib.m2rnn_ref_conv_silu_backward
+        cb.restype = ctypes.c_int
+        cb.argtypes = [ctypes.c_int] * 3 + [_dbl_p] * 7
         nb = self.lib.m2rnn_ref_gate_rmsnorm_backward
         nb.restype = ctypes.c_int
         nb.argtypes = [ctypes.c_int] * 2 + [_dbl_p] * 3 + [ctypes.c_double] + [_dbl_p] * 4
@@ -119,6 +125,33 @@ class Oracle:
             raise RuntimeError(f"m2rnn_ref_gate_forward failed with status {st}")
         return f
 
+    def conv_silu_forward(self, u, w, bias=None):
+        """Causal depthwise Conv1D (width 4) and SiLU over time: u [B, T, C],
+        w [C, 4], bias [C] or None.  Returns z [B, T, C]."""
+        u = self._arr(u)
+        B, T, C = u.shape
+        w = self._arr(w, (C, 4))
+        bias = None if bias is None else self._arr(bias, (C,))
+        z = np.empty((B, T, C))
+        st = self.lib.m2rnn_ref_conv_silu_forward(B, T, C, self._p(u), self._p(w), self._p(bias), self._p(z))
+        if st != 0:
+            raise RuntimeError(f"m2rnn_ref_conv_silu_forward failed with status {st}")
+        return z
+
+    def conv_silu_backward(self, u, w, bias, dz):
+        """(du [B, T, C], dw [C, 4], dbias [C]) from dz [B, T, C]."""
+        u = self._arr(u)
+        B, T, C = u.shape
+        w = self._arr(w, (C, 4))
+        bias = None if bias is None else self._arr(bias, (C,))
+        dz = self._arr(dz, (B, T, C))
+        du, dw, db = np.empty((B, T, C)), np.empty((C, 4)), np.empty(C)
+        st = self.lib.m2rnn_ref_conv_silu_backward(B, T, C, self._p(u), self._p(w), self._p(bias), self._p(dz),
+                                                   self._p(du), self._p(dw), self._p(db))
+        if st != 0:
+            raise RuntimeError(f"m2rnn_ref_conv_silu_backward failed with status {st}")
+        return du, dw, db
+
     def gate_rmsnorm_forward(self, y, g, w, eps=0.0):
         """Output gate and RMSNorm over the last axis: y, g [..., d], w [d].
         Returns (o [..., d], rstd [...])."""
@@ -184,6 +217,14 @@ def forward(*args, **kw):
 
 def backward(*args, **kw):
     return get().backward(*args, **kw)
+
+
+def conv_silu_forward(*args, **kw):
+    return get().conv_silu_forward(*args, **kw)
+
+
+def conv_silu_backward(*args, **kw):
+    return get().conv_silu_backward(*args, **kw)
 
 
 def gate_rmsnorm_forward(*args, **kw):

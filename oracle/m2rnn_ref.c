@@ -425,3 +425,72 @@ int m2rnn_ref_gate_rmsnorm_backward(int ntok, int d, const double* y, const doub
   free(x);
   return 0;
 }
+
+/* -------------------------------------------------- causal Conv1D and SiLU
+ * Before the scan, q, k and v come out of a linear projection, a causal
+ * Conv1D of width 4 and a SiLU (slide "Most of the block can be computed
+ * before recurrence", paper Fig. 2).  Read as a depthwise convolution over
+ * time per channel c, with zero input before t = 0 and an optional bias,
+ * taps in the order of a cross-correlation (the last tap on the current step):
+ *     a[b][t][c] = bias[c] + sum_{j=0..3} w[c][j] u[b][t-3+j][c]
+ *     z = silu(a) = a / (1 + e^{-a})
+ * Backward from dz, with silu'(a) = s (1 + a (1 - s)), s = 1 / (1 + e^{-a}):
+ *     da = dz silu'(a)
+ *     du[b][t][c] = sum_j w[c][j] da[b][t+3-j][c]   (terms past T are zero)
+ *     dw[c][j] = sum_{b,t} da[b][t][c] u[b][t-3+j][c],   dbias[c] = sum_{b,t} da
+ * (sums over b ascending, then t ascending). */
+#define CONV_W 4
+
+static double conv_pre(int T, int C, const double* u, const double* w, const double* bias, int b, int t, int c) {
+  double a = bias ? bias[c] : 0.0;
+  for (int j = 0; j < CONV_W; ++j) {
+    const int ts = t - (CONV_W - 1) + j;
+    if (ts >= 0) a += w[c * CONV_W + j] * u[((size_t)b * T + ts) * C + c];
+  }
+  return a;
+}
+
+int m2rnn_ref_conv_silu_forward(int B, int T, int C, const double* u, const double* w, const double* bias,
+                                double* z) {
+  if (B < 0 || T < 0 || C < 1 || !u || !w || !z) return -1;
+  for (int b = 0; b < B; ++b)
+    for (int t = 0; t < T; ++t)
+      for (int c = 0; c < C; ++c) {
+        const double a = conv_pre(T, C, u, w, bias, b, t, c);
+        z[((size_t)b * T + t) * C + c] = a / (1.0 + exp(-a));
+      }
+  return 0;
+}
+
+int m2rnn_ref_conv_silu_backward(int B, int T, int C, const double* u, const double* w, const double* bias,
+                                 const double* dz, double* du, double* dw, double* dbias) {
+  if (B < 0 || T < 0 || C < 1 || !u || !w || !dz || !du || !dw) return -1;
+  double* da = (double*)malloc(sizeof(double) * ((size_t)T > 0 ? (size_t)T : 1));
+  if (!da) return -2;
+  for (int e = 0; e < C * CONV_W; ++e) dw[e] = 0.0;
+  if (dbias)
+    for (int c = 0; c < C; ++c) dbias[c] = 0.0;
+  for (int c = 0; c < C; ++c)
+    for (int b = 0; b < B; ++b) {
+      for (int t = 0; t < T; ++t) {
+        const double a = conv_pre(T, C, u, w, bias, b, t, c);
+        const double s = 1.0 / (1.0 + exp(-a));
+        da[t] = dz[((size_t)b * T + t) * C + c] * s * (1.0 + a * (1.0 - s));
+      }
+      for (int t = 0; t < T; ++t) {
+        double g = 0.0;
+        for (int j = 0; j < CONV_W; ++j) {
+          const int to = t + (CONV_W - 1) - j;
+          if (to < T) g += w[c * CONV_W + j] * da[to];
+        }
+        du[((size_t)b * T + t) * C + c] = g;
+        for (int j = 0; j < CONV_W; ++j) {
+          const int ts = t - (CONV_W - 1) + j;
+          if (ts >= 0) dw[c * CONV_W + j] += da[t] * u[((size_t)b * T + ts) * C + c];
+        }
+        if (dbias) dbias[c] += da[t];
+      }
+    }
+  free(da);
+  return 0;
+}

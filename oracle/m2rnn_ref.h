@@ -83,6 +83,18 @@ int m2rnn_ref_gate_rmsnorm_forward(int ntok, int d, const double* y, const doubl
 int m2rnn_ref_gate_rmsnorm_backward(int ntok, int d, const double* y, const double* g, const double* w,
                                     double eps, const double* dout, double* dy, double* dg, double* dw);
 
+/* Causal depthwise Conv1D of width 4 and SiLU before the scan (slide "Most of
+ * the block can be computed before recurrence", paper Fig. 2): for u, z
+ * [B][T][C], w [C][4], bias [C] (NULL: none),
+ *   z[b][t][c] = silu(bias[c] + sum_{j=0..3} w[c][j] u[b][t-3+j][c]),
+ * zero input before t = 0.  Backward from dz: du [B][T][C], dw [C][4] and
+ * dbias [C] (NULL: not wanted) summed over b and t.  Return 0, -1 on a bad
+ * argument, -2 when out of memory. */
+int m2rnn_ref_conv_silu_forward(int B, int T, int C, const double* u, const double* w, const double* bias,
+                                double* z);
+int m2rnn_ref_conv_silu_backward(int B, int T, int C, const double* u, const double* w, const double* bias,
+                                 const double* dz, double* du, double* dw, double* dbias);
+
 #ifdef __cplusplus
 }
 #endif

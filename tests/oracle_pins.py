@@ -20,6 +20,9 @@ Sources (M2RNN paper-discussion slides, reading of arXiv:2603.14360v2):
         [BW] for C ends.
   [GT]  slide "The gate preserves a direct path through time", paper Sec. 3.1,
         Eqs. (13), (17): f = exp(-alpha softplus(a + beta)), alpha >= 0.
+  [CNV] slide "Most of the block can be computed before recurrence", paper
+        Fig. 2: q, k, v pass a causal Conv1D of width 4 and a SiLU before the
+        scan (depthwise over time per channel, zero input before t = 0).
   [NRM] slide "Most of the block can be computed before recurrence", paper
         Fig. 2 (after the readout: times the output gate, then RMSNorm), with
         the statistic and backward of slide "Backup: RMSNormTP synchronizes
@@ -608,6 +611,98 @@ def pin_norm_finite_differences(o):
         _close(got, fd, 1e-7 * max(1.0, float(np.max(np.abs(fd)))), f"rmsnorm FD {['dy', 'dg', 'dw'][idx]}")
 
 
+def _conv_inputs(rng, B, T, C):
+    u = rng.standard_normal((B, T, C)) * 1.5
+    w = rng.standard_normal((C, 4)) * 0.6
+    bias = rng.standard_normal(C) * 0.5
+    return u, w, bias
+
+
+def pin_conv_torch_conv1d(o):
+    """[CNV] against torch.nn.functional.conv1d (groups = C, padding 3, the
+    first T outputs) and torch.nn.functional.silu in float64, forward and,
+    through torch autograd, du, dw and dbias; with and without a bias."""
+    rng = np.random.default_rng(RNG_SEED + 50)
+    B, T, C = 2, 11, 5
+    u, w, bias = _conv_inputs(rng, B, T, C)
+    dz = rng.standard_normal((B, T, C))
+    for use_bias in (True, False):
+        b = bias if use_bias else None
+        tu = torch.tensor(u, requires_grad=True)
+        tw = torch.tensor(w, requires_grad=True)
+        tb = torch.tensor(bias, requires_grad=True) if use_bias else None
+        a = torch.nn.functional.conv1d(tu.transpose(1, 2), tw.unsqueeze(1), tb, padding=3, groups=C)[..., :T]
+        ref = torch.nn.functional.silu(a).transpose(1, 2)
+        (ref * torch.tensor(dz)).sum().backward()
+        _close(o.conv_silu_forward(u, w, b), ref.detach().numpy(), 1e-13, f"conv silu bias={use_bias}")
+        du, dw, db = o.conv_silu_backward(u, w, b, dz)
+        _close(du, tu.grad.numpy(), 1e-12, f"conv du bias={use_bias}")
+        _close(dw, tw.grad.numpy(), 1e-12, f"conv dw bias={use_bias}")
+        if use_bias:
+            _close(db, tb.grad.numpy(), 1e-12, "conv dbias")
+
+
+def pin_conv_impulse_and_causality(o):
+    """[CNV] a unit impulse at (t0, c) gives a = bias + w[c][3 - (t - t0)] for
+    t0 <= t <= t0 + 3 and a = bias elsewhere (closed form, silu written out
+    with numpy); a change of u at t0 leaves every z before t0 unchanged."""
+    rng = np.random.default_rng(RNG_SEED + 51)
+    B, T, C, t0, c = 1, 12, 3, 5, 1
+    _, w, bias = _conv_inputs(rng, B, T, C)
+    u = np.zeros((B, T, C))
+    u[0, t0, c] = 1.0
+    a = np.tile(bias, (B, T, 1))
+    for t in range(t0, min(T, t0 + 4)):
+        a[0, t, c] += w[c, 3 - (t - t0)]
+    _close(o.conv_silu_forward(u, w, bias), a / (1.0 + np.exp(-a)), 1e-15, "conv impulse")
+    u2, _, _ = _conv_inputs(rng, 2, T, C)
+    z1 = o.conv_silu_forward(u2, w, bias)
+    u3 = u2.copy()
+    u3[:, t0:] += rng.standard_normal((2, T - t0, C))
+    z2 = o.conv_silu_forward(u3, w, bias)
+    assert np.array_equal(z1[:, :t0], z2[:, :t0]), "conv is not causal"
+    assert not np.allclose(z1[:, t0:], z2[:, t0:])
+
+
+def pin_conv_identity_taps(o):
+    """[CNV] taps (0, 0, 0, 1) and no bias make z = silu(u) exactly, and the
+    gradient du = dz silu'(u) with silu'(x) = s (1 + x (1 - s))."""
+    rng = np.random.default_rng(RNG_SEED + 52)
+    u, _, _ = _conv_inputs(rng, 2, 7, 4)
+    w = np.zeros((4, 4))
+    w[:, 3] = 1.0
+    s = 1.0 / (1.0 + np.exp(-u))
+    _close(o.conv_silu_forward(u, w), u * s, 1e-15, "conv identity taps")
+    dz = rng.standard_normal(u.shape)
+    du, _, _ = o.conv_silu_backward(u, w, None, dz)
+    _close(du, dz * s * (1.0 + u * (1.0 - s)), 1e-14, "conv identity du")
+
+
+def pin_conv_finite_differences(o):
+    """[CNV] backward against central differences of L = sum(z * dz) over every
+    element of u, w and bias."""
+    rng = np.random.default_rng(RNG_SEED + 53)
+    u, w, bias = _conv_inputs(rng, 2, 6, 3)
+    dz = rng.standard_normal(u.shape)
+    du, dw, db = o.conv_silu_backward(u, w, bias, dz)
+    ins = [u, w, bias]
+    h = 1e-6
+    for idx, got in enumerate([du, dw, db]):
+        x = ins[idx]
+        fd = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            mi = it.multi_index
+            orig = x[mi]
+            x[mi] = orig + h
+            lp = float(np.sum(o.conv_silu_forward(*ins) * dz))
+            x[mi] = orig - h
+            lm = float(np.sum(o.conv_silu_forward(*ins) * dz))
+            x[mi] = orig
+            fd[mi] = (lp - lm) / (2 * h)
+        _close(got, fd, 1e-7 * max(1.0, float(np.max(np.abs(fd)))), f"conv FD {['du', 'dw', 'dbias'][idx]}")
+
+
 FORWARD_PINS = [pin_t1_closed_form, pin_f_one_forward, pin_zero_w_zero_f_forward, pin_readout_linear_in_q,
                 pin_checkpoints, pin_convex_bound, pin_permutations, pin_rnn_embedding_forward_backward]
 BACKWARD_PINS = [pin_f_one_backward, pin_zero_w_zero_f_backward, pin_finite_differences_small,
@@ -617,4 +712,7 @@ INITIAL_STATE_PINS = [pin_initial_state_f_one, pin_initial_state_forgotten, pin_
 GATE_PINS = [pin_gate_sigmoid_identity, pin_gate_alpha_zero, pin_gate_power_law_and_range,
              pin_gate_large_arguments, pin_gate_finite_differences]
 NORM_PINS = [pin_norm_torch_rms_norm, pin_norm_invariances, pin_norm_constant_token, pin_norm_finite_differences]
-ALL_PINS = FORWARD_PINS + BACKWARD_PINS + INITIAL_STATE_PINS + GATE_PINS + NORM_PINS + [pin_thread_invariance]
+CONV_PINS = [pin_conv_torch_conv1d, pin_conv_impulse_and_causality, pin_conv_identity_taps,
+             pin_conv_finite_differences]
+ALL_PINS = (FORWARD_PINS + BACKWARD_PINS + INITIAL_STATE_PINS + GATE_PINS + NORM_PINS + CONV_PINS
+            + [pin_thread_invariance])

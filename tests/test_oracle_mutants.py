@@ -78,6 +78,19 @@ MUTANTS = [
     ("norm_dg_uses_g", "dg[(size_t)t * d + j] = dx * yt[j];", "dg[(size_t)t * d + j] = dx * gt[j];"),
     ("norm_dw_drops_s", "dw[j] += dt[j] * x[j] * s;", "dw[j] += dt[j] * x[j];"),
     ("norm_dw_uses_y", "dw[j] += dt[j] * x[j] * s;", "dw[j] += dt[j] * yt[j] * s;"),
+    ("conv_taps_reversed", "if (ts >= 0) a += w[c * CONV_W + j] * u[((size_t)b * T + ts) * C + c];",
+     "if (ts >= 0) a += w[c * CONV_W + (CONV_W - 1 - j)] * u[((size_t)b * T + ts) * C + c];"),
+    ("conv_not_causal", "    const int ts = t - (CONV_W - 1) + j;\n    if (ts >= 0) a +=",
+     "    const int ts = t + j;\n    if (ts < T) a +="),
+    ("conv_drops_bias", "double a = bias ? bias[c] : 0.0;", "double a = 0.0;"),
+    ("conv_sigmoid_for_silu", "z[((size_t)b * T + t) * C + c] = a / (1.0 + exp(-a));",
+     "z[((size_t)b * T + t) * C + c] = 1.0 / (1.0 + exp(-a));"),
+    ("conv_silu_derivative_is_sigmoid", "da[t] = dz[((size_t)b * T + t) * C + c] * s * (1.0 + a * (1.0 - s));",
+     "da[t] = dz[((size_t)b * T + t) * C + c] * s;"),
+    ("conv_du_forward_taps", "const int to = t + (CONV_W - 1) - j;", "const int to = t + j;"),
+    ("conv_dw_wrong_shift", "          const int ts = t - (CONV_W - 1) + j;\n          if (ts >= 0) dw[",
+     "          const int ts = t - j;\n          if (ts >= 0) dw["),
+    ("conv_dbias_is_dz", "if (dbias) dbias[c] += da[t];", "if (dbias) dbias[c] += dz[((size_t)b * T + t) * C + c];"),
 ]
 
 
