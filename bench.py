@@ -33,8 +33,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--pass", dest="which", choices=["fwdbwd", "fwd", "epilogue"], default="fwdbwd",
-                    help="epilogue: the output gate and RMSNorm after the readout, forward + backward")
+    ap.add_argument("--pass", dest="which", choices=["fwdbwd", "fwd", "epilogue", "prologue"], default="fwdbwd",
+                    help="epilogue: the output gate and RMSNorm after the readout; prologue: the causal Conv1D "
+                         "and SiLU of q, k and v; each forward + backward")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
@@ -213,10 +214,113 @@ def bench_epilogue(args):
     return 0
 
 
+def bench_prologue(args):
+    """Causal Conv1D (width 4) and SiLU of q, k (C = 64 each) and v (C = N V
+    = 1024) at B=32, T=4096, N=64, bf16: the three forward calls, then the
+    three backward calls, per step.  HBM-bound: the roofline object prices the
+    v backward launch's algorithmic bytes (u and dz read, du written) against
+    MI355X's 8 TB/s."""
+    import torch
+    import m2rnn_inputs
+    import non_linear_matrix_amd as m2
+    B, T, N, dtype = 32, 4096, 64, "bf16"
+    name = f"conv_silu_{dtype}_B{B}_T{T}_N{N}"
+    chans = {"q": K_DIM, "k": K_DIM, "v": N * V_DIM}
+    xs = {n: {k: t.cuda() for k, t in m2rnn_inputs.make_conv(B, T, C, dtype, seed=args.seed + i).items()}
+          for i, (n, C) in enumerate(chans.items())}
+    dev = xs["q"]["u"].device
+    zs = {n: torch.empty_like(x["u"]) for n, x in xs.items()}
+    gs = {n: (torch.empty(x["u"].shape, device=dev), torch.empty((chans[n], 4), device=dev),
+              torch.empty((chans[n],), device=dev)) for n, x in xs.items()}
+    wss = {n: torch.empty((max(1, m2.m2rnn_conv_silu_backward_workspace_bytes(B, T, chans[n])),), device=dev,
+                          dtype=torch.uint8) for n in xs}
+    stream = torch.cuda.current_stream(dev)
+    if args.copy_calibration_bytes > 0:
+        src = torch.empty(args.copy_calibration_bytes // 4, device=dev, dtype=torch.float32).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        for n, x in xs.items():
+            m2.conv_silu_forward(x["u"], x["w"], x["bias"], out=zs[n])
+        if ev is not None:
+            ev[1].record(stream)
+        for n in ("q", "k"):
+            x = xs[n]
+            m2.conv_silu_backward(x["u"], x["w"], x["bias"], x["dz"], out=gs[n], workspace=wss[n])
+        if ev is not None:
+            ev[2].record(stream)
+        x = xs["v"]
+        m2.conv_silu_backward(x["u"], x["w"], x["bias"], x["dz"], out=gs["v"], workspace=wss["v"])
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        step(events[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
+    bwd_qk_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps
+    bwd_v_ms = sum(e[2].elapsed_time(e[3]) for e in events) / args.steps
+    es = 2 if dtype == "bf16" else 4
+    elems = B * T * sum(chans.values())
+    fwd_bytes = elems * 2 * es                                  # u read, z written
+    v_elems = B * T * chans["v"]
+    bwd_v_bytes = v_elems * (es + 4 + 4)                        # u, dz read; du written
+    achieved = bwd_v_bytes / (bwd_v_ms * 1e-3) / 1e9
+    htok = B * T * N
+    res = {
+        "metric": "M2RNN causal Conv1D(4) + SiLU of q, k, v head-tokens/s fwd & bwd; % of HBM roofline",
+        "value": htok * args.steps / (total_ms * 1e-3),
+        "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": total_ms / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; u = N(0,1), w and bias U(-1/2,1/2), dz = N(0,1))",
+        "config": {"workload": name, "pass": "forward+backward", "B": B, "T": T, "N": N,
+                   "channels": chans, "input_dtype": dtype},
+        "copy_calibration_bytes": args.copy_calibration_bytes,
+        "fwd_ms": fwd_ms, "bwd_qk_ms": bwd_qk_ms, "bwd_v_ms": bwd_v_ms,
+        "fwd_GBs": fwd_bytes / (fwd_ms * 1e-3) / 1e9,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": profiled_traffic(name, "bwd"),
+                     "kernel": "m2rnn_conv_silu_backward of v (conv_bwd_kernel + two column-sum launches)",
+                     "kernel_ms": bwd_v_ms,
+                     "algorithmic": f"{es + 8} B/element x {v_elems} elements per launch"},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        x = m2rnn_inputs.make_conv(B, T, chans["v"], dtype, seed=args.seed + 2)
+        rows = max(1, min(B, int(args.cpu_seconds / 1.5)))       # batch rows of v, about 1.5 s each
+        c0 = time.perf_counter()
+        u = x["u"][:rows].double().numpy()
+        w, bb = x["w"].double().numpy(), x["bias"].double().numpy()
+        oracle.conv_silu_forward(u, w, bb)
+        oracle.conv_silu_backward(u, w, bb, x["dz"][:rows].double().numpy())
+        dt = time.perf_counter() - c0
+        res["cpu_baseline"] = {"value": rows * T * N / dt, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
+                               "sample": f"forward+backward of the fp64 oracle on v's channels (C = {chans['v']}) "
+                                         f"for the first {rows} batch rows, {dt:.1f} s on 1 thread"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     if args.which == "epilogue" and args.gpus == 1:
         return bench_epilogue(args)
+    if args.which == "prologue" and args.gpus == 1:
+        return bench_prologue(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the scan shards over batch rows/heads with no communication, "

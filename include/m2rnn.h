@@ -164,6 +164,45 @@ int m2rnn_backward_gated(int B, int T, int N, int K, int V, int dtype,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Causal Conv1D of width 4 and SiLU that q, k and v pass before the scan
+ * (slide "Most of the block can be computed before recurrence", paper Fig. 2),
+ * read as a depthwise convolution over time per channel with zero input
+ * before t = 0 and taps in cross-correlation order (torch conv1d's):
+ *       z[b][t][c] = silu(bias[c] + sum_{j=0..3} w[c][j] u[b][t-3+j][c])
+ *   u     [B][T][C]  input (dtype `dtype`), e.g. a projected q, k or v with
+ *                    C = 64, 64 or N V; 4-element aligned
+ *   w     [C][4]     taps (dtype `dtype`), 4-element aligned
+ *   bias  [C]        (dtype `dtype`) or NULL for none
+ *   z     [B][T][C]  out, dtype `dtype` (bf16: rounded to nearest even from
+ *                    the float32 result); must not overlap u
+ * C must be a multiple of 4 (else M2RNN_ERR_UNSUPPORTED).
+ */
+int m2rnn_conv_silu_forward(int B, int T, int C, int dtype, const void* u, const void* w,
+                            const void* bias, void* z, void* stream);
+
+/* Bytes of device workspace m2rnn_conv_silu_backward needs (0 if none). */
+size_t m2rnn_conv_silu_backward_workspace_bytes(int B, int T, int C);
+
+/*
+ * Backward of m2rnn_conv_silu_forward by the chain rule: with
+ * a = bias + sum_j w[c][j] u[t-3+j] and silu'(a) = s (1 + a (1 - s)),
+ * s = 1 / (1 + e^{-a}), da = dz silu'(a) and
+ *       du[b][t][c] = sum_j w[c][j] da[b][t+3-j][c]      (zero past T)
+ *       dw[c][j] = sum_{b,t} da[b][t][c] u[b][t-3+j][c],  dbias[c] = sum_{b,t} da
+ *   u, w, bias     the forward's inputs
+ *   dz    [B][T][C] float32, 16-byte aligned
+ *   du    [B][T][C] float32 out; must not overlap dz
+ *   dw    [C][4] float32 out; dbias [C] float32 out or NULL (not wanted);
+ *                  both summed over b and t in a fixed order
+ *   workspace      m2rnn_conv_silu_backward_workspace_bytes(...) bytes,
+ *                  16-byte aligned; contents on entry are ignored
+ * B T == 0 sets dw (and dbias) to 0.
+ */
+int m2rnn_conv_silu_backward(int B, int T, int C, int dtype, const void* u, const void* w,
+                             const void* bias, const float* dz, float* du, float* dw, float* dbias,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Output gate and RMSNorm after the readout (slide "Most of the block can be
  * computed before recurrence", paper Fig. 2), with the per-token statistic of
  * slide "Backup: RMSNormTP synchronizes per-token statistics" (paper App. C,

@@ -31,6 +31,15 @@ its own generator, in this order:
     w    = 1 + N(0, 1/100)         [N, V]        RMSNorm weight
     dout = N(0, 1)                 [B, T, N, V]  float32
 
+For the causal Conv1D and SiLU before the scan, make_conv draws, from its own
+generator, in this order (the taps and bias as a width-4 conv layer's default
+initialisation, U(-1/2, 1/2)):
+
+    u    = N(0, 1)                 [B, T, C]   projected q, k or v
+    w    = U(-1/2, 1/2)            [C, 4]
+    bias = U(-1/2, 1/2)            [C]
+    dz   = N(0, 1)                 [B, T, C]   float32
+
 Draw order is fixed (q, k, v, f, W, w_r, dy) from one CPU torch.Generator
 seeded with `seed`; every tensor is drawn in float32 and, for bfloat16
 workloads, rounded to bfloat16 with round-to-nearest-even.  dy stays float32.
@@ -139,3 +148,17 @@ def make_epilogue(B, T, N, dtype="f32", seed=0, V=V_DIM):
     w = 1.0 + 0.1 * torch.randn(N, V, generator=g, dtype=torch.float32)
     dout = torch.randn(B, T, N, V, generator=g, dtype=torch.float32)
     return {"y": y.contiguous(), "g": gate.to(td).contiguous(), "w": w.to(td).contiguous(), "dout": dout.contiguous()}
+
+
+def make_conv(B, T, C, dtype="f32", seed=0):
+    """Seeded inputs of the causal Conv1D and SiLU: dict of CPU tensors u, w,
+    bias in `dtype` and dz in float32."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(int(seed) + 1299709)
+    td = torch_dtype(dtype)
+    u = torch.randn(B, T, C, generator=g, dtype=torch.float32)
+    w = torch.rand(C, 4, generator=g, dtype=torch.float32) - 0.5
+    bias = torch.rand(C, generator=g, dtype=torch.float32) - 0.5
+    dz = torch.randn(B, T, C, generator=g, dtype=torch.float32)
+    return {"u": u.to(td).contiguous(), "w": w.to(td).contiguous(), "bias": bias.to(td).contiguous(),
+            "dz": dz.contiguous()}

@@ -13,6 +13,7 @@ is no CPU fallback.
     y_t = m2.decode(q_t, k_t, v_t, f_t, W, w_r, H)              # one token, H updated
     y, H_T = m2.forward_gated(q, k, v, a, alpha, beta, W, w_r)  # f from the gate
     grads = m2.backward_gated(q, k, v, a, alpha, beta, W, w_r, H_ckpt, 64, dy)
+    q = m2.conv_silu_forward(q_proj, w_cq, b_cq)                # SiLU(causal conv4(q_proj))
     o = m2.gate_rmsnorm_forward(y, g, w_o)                      # RMSNorm(y * g) * w_o
     dy, dg, dw_o = m2.gate_rmsnorm_backward(y, g, w_o, do)
 
@@ -56,6 +57,12 @@ lib.m2rnn_forward_gated.argtypes = [_i] * 6 + [_p] * 9 + [_p, _p, _p, _i, _p]
 lib.m2rnn_backward_gated.restype = _i
 lib.m2rnn_backward_gated.argtypes = ([_i] * 6 + [_p] * 8 + [_p, _i] + [_p, _p] + [_p] * 9
                                      + [_p, ctypes.c_size_t, _p])
+lib.m2rnn_conv_silu_forward.restype = _i
+lib.m2rnn_conv_silu_forward.argtypes = [_i] * 4 + [_p] * 4 + [_p]
+lib.m2rnn_conv_silu_backward_workspace_bytes.restype = ctypes.c_size_t
+lib.m2rnn_conv_silu_backward_workspace_bytes.argtypes = [_i] * 3
+lib.m2rnn_conv_silu_backward.restype = _i
+lib.m2rnn_conv_silu_backward.argtypes = [_i] * 4 + [_p] * 7 + [_p, ctypes.c_size_t, _p]
 lib.m2rnn_gate_rmsnorm_forward.restype = _i
 lib.m2rnn_gate_rmsnorm_forward.argtypes = [_i] * 5 + [_p] * 3 + [ctypes.c_float] + [_p, _p, _p]
 lib.m2rnn_gate_rmsnorm_backward_workspace_bytes.restype = ctypes.c_size_t
@@ -287,4 +294,57 @@ def gate_rmsnorm_backward(y, g, w, dout, eps=0.0, out=None, workspace=None):
     _check(lib.m2rnn_gate_rmsnorm_backward(B, T, N, Vv, _dtype_code(g), _ptr(y), _ptr(g), _ptr(w), float(eps),
                                            _ptr(dout), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(workspace),
                                            wbytes, _stream(dev)))
+    return out
+
+
+def m2rnn_conv_silu_forward(B, T, C, dtype, u, w, bias, z, stream):
+    """Raw C-ABI call with ctypes pointers; returns the status code."""
+    return lib.m2rnn_conv_silu_forward(B, T, C, dtype, u, w, bias, z, stream)
+
+
+def m2rnn_conv_silu_backward(B, T, C, dtype, u, w, bias, dz, du, dw, dbias, workspace, workspace_bytes, stream):
+    """Raw C-ABI call with ctypes pointers; returns the status code."""
+    return lib.m2rnn_conv_silu_backward(B, T, C, dtype, u, w, bias, dz, du, dw, dbias, workspace, workspace_bytes,
+                                        stream)
+
+
+def m2rnn_conv_silu_backward_workspace_bytes(B, T, C):
+    return int(lib.m2rnn_conv_silu_backward_workspace_bytes(B, T, C))
+
+
+def _conv_shape(u):
+    """u [B, T, C] or [B, T, N, V] (treated as C = N V)."""
+    C = 1
+    for s in u.shape[2:]:
+        C *= s
+    return u.shape[0], u.shape[1], C
+
+
+def conv_silu_forward(u, w, bias=None, out=None):
+    """z = SiLU(bias + causal depthwise conv of width 4 over time) with taps
+    w [C, 4] in torch conv1d order (the last tap on the current step).  u is
+    [B, T, C] or [B, T, N, V]; z has u's shape and dtype."""
+    B, T, C = _conv_shape(u)
+    if out is None:
+        out = torch.empty_like(u)
+    _check(lib.m2rnn_conv_silu_forward(B, T, C, _dtype_code(u), _ptr(u), _ptr(w), _ptr(bias), _ptr(out),
+                                       _stream(u.device)))
+    return out
+
+
+def conv_silu_backward(u, w, bias, dz, out=None, workspace=None, want_dbias=True):
+    """Gradients of sum(z * dz) for conv_silu_forward: (du like u in float32,
+    dw [C, 4], dbias [C] or None) float32.  `out` may pass (du, dw, dbias)."""
+    B, T, C = _conv_shape(u)
+    dev = u.device
+    if out is None:
+        out = (torch.empty(u.shape, device=dev, dtype=torch.float32), torch.empty((C, 4), device=dev),
+               torch.empty((C,), device=dev) if want_dbias else None)
+    nbytes = int(lib.m2rnn_conv_silu_backward_workspace_bytes(B, T, C))
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty((nbytes,), device=dev, dtype=torch.uint8)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.m2rnn_conv_silu_backward(B, T, C, _dtype_code(u), _ptr(u), _ptr(w), _ptr(bias), _ptr(dz),
+                                        _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(workspace), wbytes,
+                                        _stream(dev)))
     return out

@@ -294,3 +294,71 @@ extern "C" int m2rnn_gate_rmsnorm_backward(int B, int T, int N, int V, int dtype
   hipError_t e = m2rnn::launch_norm_backward(a, dtype, s);
   return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "gate_rmsnorm backward launch: %s", hipGetErrorString(e));
 }
+
+// ------------------------------------------------ causal Conv1D and SiLU
+namespace {
+
+int conv_check(int B, int T, int C, int dtype) {
+  if (B < 0 || T < 0 || C < 0) return fail(M2RNN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d T=%d C=%d)", B, T, C);
+  if (dtype != M2RNN_F32 && dtype != M2RNN_BF16) return fail(M2RNN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
+  if (C % 4 != 0 || C > (1 << 20)) return fail(M2RNN_ERR_UNSUPPORTED, "C must be a multiple of 4, at most 2^20 (got %d)", C);
+  if ((long long)B * T * C > kMaxElems) return fail(M2RNN_ERR_UNSUPPORTED, "problem too large");
+  return M2RNN_OK;
+}
+
+}  // namespace
+
+extern "C" int m2rnn_conv_silu_forward(int B, int T, int C, int dtype, const void* u, const void* w,
+                                       const void* bias, void* z, void* stream) {
+  g_err[0] = 0;
+  int st = conv_check(B, T, C, dtype);
+  if (st) return st;
+  const size_t es = dtype == M2RNN_F32 ? 4 : 2;
+  const long long n = (long long)B * T * C;
+  if ((st = need(u, "u", n, 4 * es)) || (st = need(w, "w", n > 0 ? (long long)C * 4 : 0, 4 * es)) ||
+      (st = need(z, "z", n, 4 * es)))
+    return st;
+  if (bias && !aligned(bias, 4 * es)) return fail(M2RNN_ERR_INVALID_ARG, "bias must be %zu-byte aligned", 4 * es);
+  if (n == 0) return M2RNN_OK;
+  m2rnn::ConvArgs a{};
+  a.u = u; a.w = w; a.bias = bias; a.z = z; a.B = B; a.T = T; a.C = C;
+  hipError_t e = m2rnn::launch_conv_forward(a, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "conv_silu forward launch: %s", hipGetErrorString(e));
+}
+
+extern "C" size_t m2rnn_conv_silu_backward_workspace_bytes(int B, int T, int C) {
+  if (B <= 0 || T <= 0 || C <= 0 || C % 4 != 0 || C > (1 << 20)) return 0;
+  return sizeof(float) * m2rnn::conv_backward_workspace_floats(B, T, C);
+}
+
+extern "C" int m2rnn_conv_silu_backward(int B, int T, int C, int dtype, const void* u, const void* w,
+                                        const void* bias, const float* dz, float* du, float* dw, float* dbias,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  int st = conv_check(B, T, C, dtype);
+  if (st) return st;
+  const size_t es = dtype == M2RNN_F32 ? 4 : 2;
+  const long long n = (long long)B * T * C;
+  if ((st = need(u, "u", n, 4 * es)) || (st = need(w, "w", n > 0 ? (long long)C * 4 : 0, 4 * es)) ||
+      (st = need(dz, "dz", n, 16)) || (st = need(du, "du", n, 16)) || (st = need(dw, "dw", (long long)C * 4, 16)))
+    return st;
+  if (bias && !aligned(bias, 4 * es)) return fail(M2RNN_ERR_INVALID_ARG, "bias must be %zu-byte aligned", 4 * es);
+  if (dbias && !aligned(dbias, 16)) return fail(M2RNN_ERR_INVALID_ARG, "dbias must be 16-byte aligned");
+  hipStream_t s = (hipStream_t)stream;
+  if (C == 0) return M2RNN_OK;
+  if (n == 0) {   // dw = dbias = 0
+    hipError_t e = m2rnn::launch_fill_zero(dw, (size_t)C * 4, s);
+    if (e == hipSuccess && dbias) e = m2rnn::launch_fill_zero(dbias, (size_t)C, s);
+    return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "dw = 0: %s", hipGetErrorString(e));
+  }
+  const size_t need_bytes = m2rnn_conv_silu_backward_workspace_bytes(B, T, C);
+  if (!workspace || workspace_bytes < need_bytes)
+    return fail(M2RNN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need_bytes,
+                workspace ? workspace_bytes : (size_t)0);
+  if (!aligned(workspace, 16)) return fail(M2RNN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  m2rnn::ConvArgs a{};
+  a.u = u; a.w = w; a.bias = bias; a.dz = dz; a.du = du; a.dw = dw; a.dbias = dbias; a.ws = (float*)workspace;
+  a.B = B; a.T = T; a.C = C; a.R = m2rnn::conv_backward_workers(B, T, C);
+  hipError_t e = m2rnn::launch_conv_backward(a, dtype, s);
+  return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "conv_silu backward launch: %s", hipGetErrorString(e));
+}

@@ -68,6 +68,33 @@ size_t norm_backward_workspace_floats(long long ntok, int d);
 hipError_t launch_norm_forward(const NormArgs& a, int dtype, hipStream_t stream);
 hipError_t launch_norm_backward(const NormArgs& a, int dtype, hipStream_t stream);
 
+// Causal depthwise Conv1D (width 4) and SiLU over time, per channel:
+// z[b][t][c] = silu(bias[c] + sum_j w[c][j] u[b][t-3+j][c]).
+struct ConvArgs {
+  const void *u, *w, *bias;   // input dtype; bias may be nullptr
+  void* z;                    // forward output, input dtype
+  const float* dz;            // backward
+  float *du, *dw, *dbias;     // backward (dbias may be nullptr)
+  float* ws;                  // backward: partials [R][C*5], then [kColsumRowBlocks][C*5]
+  int B, T, C;
+  int R;                      // backward: workers per channel group
+};
+constexpr int kConvTaps = 4;
+constexpr int kConvStrip = 16;   // time steps per thread (forward)
+constexpr int kConvStripBwd = 8; // time steps per thread (backward)
+int conv_backward_workers(int B, int T, int C);
+size_t conv_backward_workspace_floats(int B, int T, int C);
+hipError_t launch_conv_forward(const ConvArgs& a, int dtype, hipStream_t stream);
+hipError_t launch_conv_backward(const ConvArgs& a, int dtype, hipStream_t stream);
+
+// out[col] = sum over rows of in[row][col] for cols columns (a multiple of 4),
+// rows summed in a fixed order (two levels; ws2 holds kColsumRowBlocks rows
+// of cols floats).  Columns below cols_a go to out_a[col], the rest to
+// out_b[col - cols_a].
+constexpr int kColsumRowBlocks = 32;
+hipError_t launch_colsum(const float* in, int rows, int cols, float* ws2, float* out_a, int cols_a, float* out_b,
+                         hipStream_t stream);
+
 // Zero `n` floats with a plain fill kernel (graph-capture friendly).
 hipError_t launch_fill_zero(float* p, size_t n, hipStream_t stream);
 // dst[i] = src[i] for `n` floats with a plain copy kernel; dst == src is allowed.

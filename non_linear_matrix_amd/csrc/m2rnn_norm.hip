@@ -136,44 +136,6 @@ __global__ __launch_bounds__(64 * kWaves) void norm_bwd_kernel(NormArgs a) {
   }
 }
 
-// dw = sum over the nwg partial rows ws[row][d], in two fixed-order levels
-// so that many loads are in flight: block (cx, ry) of kRowBlocks row blocks
-// has 64 f4 columns x 4 row lanes; lane r sums rows ry 4 + r + k 4 kRowBlocks
-// (k ascending), the 4 lanes are added in order and written to ws2[ry][d];
-// then each column adds its kRowBlocks values in order.
-constexpr int kRowBlocks = 32;
-
-__global__ __launch_bounds__(256) void norm_dw_partial_kernel(const float* ws, int nwg, int d, float* ws2) {
-  __shared__ f4 lanes[4][64];
-  const int col = blockIdx.x * 64 + threadIdx.x % 64, r = threadIdx.x / 64, ry = blockIdx.y;
-  const int d4 = d / 4;
-  f4 acc[4] = {};
-  if (col < d4) {
-    const int stride = 4 * kRowBlocks;
-    int row = ry * 4 + r, k = 0;
-    for (; row + 3 * stride < nwg; row += 4 * stride, k += 4) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] += *(const f4*)(ws + (size_t)(row + q * stride) * d + col * 4);
-    }
-    for (int q = 0; row < nwg; row += stride, ++q) acc[q] += *(const f4*)(ws + (size_t)row * d + col * 4);
-  }
-  lanes[r][threadIdx.x % 64] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-  __syncthreads();
-  if (r == 0 && col < d4) {
-    const int c = threadIdx.x % 64;
-    *(f4*)(ws2 + (size_t)ry * d + col * 4) = ((lanes[0][c] + lanes[1][c]) + (lanes[2][c] + lanes[3][c]));
-  }
-}
-
-__global__ __launch_bounds__(256) void norm_dw_final_kernel(const float* ws2, int d, float* dw) {
-  const int col = blockIdx.x * 256 + threadIdx.x;
-  if (col >= d / 4) return;
-  f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int ry = 0; ry < kRowBlocks; ++ry) acc += *(const f4*)(ws2 + (size_t)ry * d + col * 4);
-  *(f4*)(dw + col * 4) = acc;
-}
-
 int chunks_for(int d) {
   const int c = (d + 255) / 256;
   return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : 8;
@@ -205,14 +167,7 @@ hipError_t norm_bwd_t(const NormArgs& a, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  float* ws2 = a.ws + (size_t)nwg * a.d;
-  const dim3 pgrid((unsigned)((a.d / 4 + 63) / 64), (unsigned)kRowBlocks);
-  hipLaunchKernelGGL(norm_dw_partial_kernel, pgrid, dim3(256), 0, stream, a.ws, nwg, a.d, ws2);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(norm_dw_final_kernel, dim3((unsigned)((a.d / 4 + 255) / 256)), dim3(256), 0, stream, ws2, a.d,
-                     a.dw);
-  return hipGetLastError();
+  return launch_colsum(a.ws, nwg, a.d, a.ws + (size_t)nwg * a.d, a.dw, a.d, nullptr, stream);
 }
 
 }  // namespace
@@ -225,7 +180,7 @@ int norm_backward_groups(long long ntok, int d) {
 }
 
 size_t norm_backward_workspace_floats(long long ntok, int d) {
-  return ((size_t)norm_backward_groups(ntok, d) + kRowBlocks) * (size_t)d;
+  return ((size_t)norm_backward_groups(ntok, d) + kColsumRowBlocks) * (size_t)d;
 }
 
 hipError_t launch_norm_forward(const NormArgs& a, int dtype, hipStream_t stream) {

@@ -25,9 +25,10 @@ def m2():
 
 def test_header_declares_the_entry_points():
     assert declared() == ["m2rnn_backward", "m2rnn_backward_gated", "m2rnn_backward_workspace_bytes",
-                          "m2rnn_decode", "m2rnn_forward", "m2rnn_forward_gated", "m2rnn_gate_rmsnorm_backward",
-                          "m2rnn_gate_rmsnorm_backward_workspace_bytes", "m2rnn_gate_rmsnorm_forward",
-                          "m2rnn_last_error"]
+                          "m2rnn_conv_silu_backward", "m2rnn_conv_silu_backward_workspace_bytes",
+                          "m2rnn_conv_silu_forward", "m2rnn_decode", "m2rnn_forward", "m2rnn_forward_gated",
+                          "m2rnn_gate_rmsnorm_backward", "m2rnn_gate_rmsnorm_backward_workspace_bytes",
+                          "m2rnn_gate_rmsnorm_forward", "m2rnn_last_error"]
 
 
 def test_library_exports_every_declared_symbol(m2):
@@ -128,3 +129,28 @@ def test_gate_rmsnorm_argument_errors_without_launch(m2):
     assert bwd(2, 3, 5, 16, 0, dummy, dummy, dummy, 0.0, dummy, dummy, None, dummy, dummy, 1 << 20, None) == \
         m2.M2RNN_ERR_INVALID_ARG
     assert "dg" in m2.m2rnn_last_error()
+
+
+def test_conv_silu_argument_errors_without_launch(m2):
+    dummy = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    fwd = m2.lib.m2rnn_conv_silu_forward
+    # B, T, C, dtype, u, w, bias, z, stream
+    assert fwd(2, 3, 6, 0, dummy, dummy, None, dummy, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert fwd(2, 3, 8, 3, dummy, dummy, None, dummy, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert fwd(-1, 3, 8, 0, dummy, dummy, None, dummy, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert fwd(2, 3, 8, 0, None, dummy, None, dummy, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert fwd(2, 3, 8, 1, dummy, dummy, ctypes.c_void_p(260), dummy, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert "bias" in m2.m2rnn_last_error()
+    assert fwd(2, 3, 8, 0, dummy, dummy, None, ctypes.c_void_p(264), None) == m2.M2RNN_ERR_INVALID_ARG
+    ws = m2.m2rnn_conv_silu_backward_workspace_bytes
+    # R = max(1, min(262144 / (C/4), B * ceil(T/8) / 4)) worker rows, then 32 second-level rows, of 5 C floats
+    assert ws(2, 3, 8) == (1 + 32) * 40 * 4 and ws(2, 3, 6) == 0 and ws(0, 3, 8) == 0
+    assert ws(32, 4096, 1024) == (1024 + 32) * 5120 * 4 and ws(32, 4096, 64) == (4096 + 32) * 320 * 4
+    bwd = m2.lib.m2rnn_conv_silu_backward
+    # ..., dz, du, dw, dbias, workspace, bytes, stream
+    assert bwd(2, 3, 8, 0, dummy, dummy, None, dummy, dummy, dummy, None, dummy, 16, None) == m2.M2RNN_ERR_WORKSPACE
+    assert bwd(2, 3, 8, 0, dummy, dummy, None, dummy, None, dummy, None, dummy, 1 << 20, None) == \
+        m2.M2RNN_ERR_INVALID_ARG
+    assert "du" in m2.m2rnn_last_error()
+    assert bwd(2, 3, 8, 0, dummy, dummy, None, dummy, dummy, dummy, ctypes.c_void_p(260), dummy, 1 << 20, None) == \
+        m2.M2RNN_ERR_INVALID_ARG
