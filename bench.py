@@ -58,14 +58,29 @@ def algorithmic_bytes_fwd(w):
     return ins + outs + ck
 
 
-def kernel_source_sha256():
-    import glob
+# the sources each profiled workload's kernels are built from
+KERNEL_SOURCES = {
+    "scan": ("m2rnn_fwd.hip", "m2rnn_bwd.hip"),
+    "gate_rmsnorm": ("m2rnn_norm.hip", "m2rnn_colsum.hip"),
+    "conv_silu": ("m2rnn_conv.hip", "m2rnn_colsum.hip"),
+}
+
+
+def kernel_source_sha256(kind):
+    """sha256 over the kernel sources of `kind` and the shared device headers."""
     import hashlib
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "non_linear_matrix_amd", "csrc", "*"))):
-        with open(p, "rb") as fh:
+    for name in (*KERNEL_SOURCES[kind], "m2rnn_device.h", "m2rnn_internal.h"):
+        with open(os.path.join(ROOT, "non_linear_matrix_amd", "csrc", name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+def workload_kind(workload):
+    for kind in ("gate_rmsnorm", "conv_silu"):
+        if workload.startswith(kind):
+            return kind
+    return "scan"
 
 
 def profiled_traffic(workload, which):
@@ -83,7 +98,7 @@ def profiled_traffic(workload, which):
                                                        "traffic_bytes_per_launch_forward", "source_sha256"):
                 k, v = line.split(":", 1)
                 vals[k] = v.strip()
-    if vals.get("source_sha256") != kernel_source_sha256():
+    if vals.get("source_sha256") != kernel_source_sha256(workload_kind(workload)):
         return None
     key = "traffic_bytes_per_launch_backward" if which == "bwd" else "traffic_bytes_per_launch_forward"
     return float(vals[key]) if key in vals else None
