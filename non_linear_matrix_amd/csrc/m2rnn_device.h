@@ -154,9 +154,11 @@ template <> struct WOperand<float> {
 };
 
 // ------------------------------------------------------ cross-lane reductions
+// (every control used here reads a lane of the same row, so bound_ctrl never
+// applies; setting it lets the compiler fold the move into the add)
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
 }
 // Sum over the 16 lanes of each row (lanes 16g .. 16g+15); every lane of the
 // row ends with the row sum.
@@ -164,8 +166,23 @@ __device__ __forceinline__ float row_sum16(float x) {
   x += dpp<0xB1>(x);  // quad_perm [1,0,3,2]
   x += dpp<0x4E>(x);  // quad_perm [2,3,0,1]
   x += dpp<0x141>(x); // row_half_mirror
-  x += dpp<0x140>(x); // row_mirror
+  x += dpp<0x128>(x); // row_ror:8 (lane m adds lane m +- 8)
   return x;
+}
+// Row sums of four values per lane at once (each 16-lane row reduces its own
+// x[0..3]).  Returns, in lane m of the row, the row sum of x[c] with
+// c = 2 (m & 1) + ((m >> 1) & 1): two halving exchanges (each lane keeps half
+// of its values and adds the partner's matching half: lanes m ^ 1, then
+// m ^ 2), then two rotations within the row add the four quads.
+__device__ __forceinline__ float row_sum16x4(f4 x, int m) {
+  const bool b0 = (m & 1) != 0, b1 = (m & 2) != 0;
+  const float k0 = b0 ? x[2] : x[0], k1 = b0 ? x[3] : x[1];
+  const float s0 = b0 ? x[0] : x[2], s1 = b0 ? x[1] : x[3];
+  const float y0 = k0 + dpp<0xB1>(s0), y1 = k1 + dpp<0xB1>(s1);   // quad_perm [1,0,3,2]
+  float z = (b1 ? y1 : y0) + dpp<0x4E>(b1 ? y0 : y1);              // quad_perm [2,3,0,1]
+  z += dpp<0x124>(z);                                               // row_ror:4
+  z += dpp<0x128>(z);                                               // row_ror:8
+  return z;
 }
 
 }  // namespace m2rnn

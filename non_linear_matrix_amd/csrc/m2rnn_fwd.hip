@@ -282,9 +282,10 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
             p[i] = fmaf(P[j][i], qq.v[j], p[i]);
           }
         if constexpr (!DENSE) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[i] = row_sum16(p[i]);
-          if (m == 0) *(f4*)(ystage + ((tt * HPW + hw) * WPH + ts) * 16 + 4 * g) = p;
+          // lane m ends with the sum for value channel 4 g + c(m); every lane
+          // stores it (the four lanes of each c write the same value)
+          const float ys = row_sum16x4(p, m);
+          ystage[((tt * HPW + hw) * WPH + ts) * 16 + 4 * g + ((m & 1) << 1) + ((m >> 1) & 1)] = ys;
         }
       }
     }
