@@ -25,7 +25,6 @@
 #include "m2rnn_device.h"
 #include "m2rnn_internal.h"
 
-#include <stdlib.h>
 
 namespace m2rnn {
 
@@ -327,22 +326,26 @@ static hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tiles per wave: four (one head per wave) by default; the M2RNN_FWD_TPW
-// environment variable (1, 2 or 4) overrides it for tuning.
-static int fwd_tiles_per_wave() {
-  const char* e = getenv("M2RNN_FWD_TPW");
-  int v = e ? atoi(e) : 4;
-  return (v == 1 || v == 2) ? v : 4;
+// Workgroup shape by the number of (batch row, head) chains.  Every head
+// needs four tile-steps per time step, and the waves of a workgroup share one
+// CU.  Many chains: four heads per workgroup, one head per wave, which issues
+// the fewest instructions per head-step.  Few chains would then leave most
+// CUs idle, so each head gets its own workgroup with one tile per wave (its
+// four waves on the four SIMDs of a CU, the readout partials summed through
+// LDS once per chunk); in between, two heads of two waves each.
+constexpr long long kFewChains = 512, kMidChains = 1536;
+
+template <typename TIn, bool GATE>
+static hipError_t dispatch_fwd_shape(const FwdArgs& a, hipStream_t stream) {
+  const long long chains = (long long)a.B * a.N;
+  if (chains <= kFewChains) return launch_fwd<TIn, 1, 1, 32, false, GATE>(a, stream);
+  if (chains <= kMidChains) return launch_fwd<TIn, 2, 2, 32, false, GATE>(a, stream);
+  return launch_fwd<TIn, 4, 4, 32, false, GATE>(a, stream);
 }
 
 template <typename TIn>
 static hipError_t dispatch_fwd(const FwdArgs& a, hipStream_t stream) {
-  if (a.ga) return launch_fwd<TIn, 4, 4, 32, false, true>(a, stream);
-  switch (fwd_tiles_per_wave()) {
-    case 4: return launch_fwd<TIn, 4, 4, 32>(a, stream);
-    case 2: return launch_fwd<TIn, 4, 2, 16>(a, stream);
-    default: return launch_fwd<TIn, 4, 1, 16>(a, stream);
-  }
+  return a.ga ? dispatch_fwd_shape<TIn, true>(a, stream) : dispatch_fwd_shape<TIn, false>(a, stream);
 }
 
 __global__ void fill_zero_kernel(float* p, size_t n) {

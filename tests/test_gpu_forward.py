@@ -32,6 +32,21 @@ def test_forward_parity_small(dtype, B, T, N):
     assert ey <= TOL[dtype] and eh <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,N", [(1, 70, 512), (3, 40, 201), (2, 20, 801), (1, 45, 1600)])
+def test_forward_parity_launch_shapes(dtype, B, T, N):
+    """Chain counts B*N in each launch shape the forward picks: at most 512
+    (one head per workgroup, one tile per wave), up to 1536 (two heads of two
+    waves each, with a head count that leaves the last workgroup half empty)
+    and above (four heads, one per wave, the last group partly empty)."""
+    x = make(B, T, N, dtype, seed=B * 7 + T + N)
+    y, HT = run(x)
+    yr, HTr = oracle_forward(x)
+    ey, eh = max_abs(y, yr), max_abs(HT, HTr)
+    print(f"{dtype} B{B} T{T} N{N} (B*N={B * N}): max|dy|={ey:.3e} max|dH_T|={eh:.3e}")
+    assert ey <= TOL[dtype] and eh <= TOL[dtype]
+
+
 def test_forward_config_fp32_B1_T256_N4():
     """The float32 workload B=1, T=256, N=4 (seed 0), element by element."""
     w = m2rnn_inputs.WORKLOADS["fwd_f32_B1_T256_N4"]

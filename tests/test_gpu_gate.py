@@ -76,7 +76,8 @@ def check(gg, gr, tol, label):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("B,T,N", [(1, 256, 4), (2, 100, 5), (3, 37, 1), (2, 70, 9), (3, 1, 2)])
+@pytest.mark.parametrize("B,T,N", [(1, 256, 4), (2, 100, 5), (3, 37, 1), (2, 70, 9), (3, 1, 2), (3, 30, 201),
+                                   (2, 20, 801)])
 def test_gated_forward_parity(dtype, B, T, N):
     """Ragged lengths and head counts that leave part of a workgroup idle,
     from a given initial state, with checkpoints."""
