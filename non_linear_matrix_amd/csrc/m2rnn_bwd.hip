@@ -43,20 +43,29 @@ namespace m2rnn {
 
 constexpr int kSub = 4;  // steps between restart states; their H_{t-1}, Z_t stay in registers
 
+// The df role's layout: pair p = s HPW + h of a sub-chunk goes to df wave
+// p / 4 as its value o = p % 4, which sum4_over_lanes leaves in lane row
+// r = 2 (o & 1) + (o >> 1) (the map is its own inverse).  gate_slot is the
+// (wave, row) slot of (step s, head h).
+template <int HPW>
+__device__ __forceinline__ int gate_slot(int s, int h) {
+  const int p = s * HPW + h, o = p & 3;
+  return (p >> 2) * 4 + 2 * (o & 1) + (o >> 1);
+}
+
 template <int HPW, bool GATE>
 struct BwdCfg {
   // the reduction pass gives each wave a fixed role (lane = (step, 16 values))
-  static_assert((HPW == 2 || HPW == 4) && kSub == 4, "backward workgroup shape");
-  // pass roles: dq, dk; one dv wave per head; one df wave per two heads and
-  // two steps
+  static_assert((HPW == 1 || HPW == 2 || HPW == 4) && kSub == 4, "backward workgroup shape");
+  // pass roles: dq, dk; one dv wave per head; df waves, wave d for the four
+  // (step, head) pairs p = 4 d .. 4 d + 3 of the sub-chunk, p = step HPW + head
   static constexpr int kDvWave = 2, kDfWave = 2 + HPW, kRoleWaves = 2 + HPW + HPW;
   static constexpr int NWAVES = HPW * 4;
   static constexpr int NT = 64 * NWAVES;
   // per staged step: K_s[64] (c k), Q_s[64] (q), V_s[HPW][16], F_s[HPW][4],
   // U_s[HPW][16], Kp_s[64] (c k permuted: [tile][g][r] = row 16 tile + 4 r + g),
   // and with the gate G_s[HPW][2] (df -> da and df -> dalpha factors, in the
-  // df waves' row order: (s, h) at df wave (s >> 1) + 2 (h >> 1), row
-  // (s & 1) + 2 (h & 1))
+  // df waves' row order, slot gate_slot(s, h))
   static constexpr int kStep = 192 + HPW * (GATE ? 38 : 36);
   static constexpr int kBuf = kSub * kStep;
   // per wave, two slots of {H_{t-1} tile, D tile}; a tile is stored as
@@ -202,7 +211,7 @@ struct BwdStage {
       }
       const float gg = 1.0f - ff;
       *(f4*)(F_s + u * 4) = f4{ff, kScale * gg, -2.0f * kScale * gg, gg};
-      if (GATE) *(f2*)(G_s + (((ft >> 1) + 2 * (fh >> 1)) * 4 + (ft & 1) + 2 * (fh & 1)) * 2) = gf;
+      if (GATE) *(f2*)(G_s + gate_slot<HPW>(ft, fh) * 2) = gf;
     }
   }
 };
@@ -344,8 +353,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   const bool dv_wave = w >= Cfg::kDvWave && w < Cfg::kDvWave + HPW;
   float wr_e = 0.f, dwr = 0.f;
   // the gate parameters of the group's heads, read by the threads that stage
-  // f; the df waves' dalpha, dbeta sums (row r of df wave d: step parity r & 1
-  // and head 2 (d >> 1) + (r >> 1))
+  // f; the df waves' dalpha, dbeta sums (slot gate_slot(s, h): row r of df
+  // wave d accumulates its (step, head) pair over the sub-chunks)
   float* gpar = dfbuf + Cfg::kDF;
   float* gacc = gpar + 2 * HPW;
   if (GATE) {
@@ -502,16 +511,16 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       if (s < len && n0 + hh < a.N)
         dst[(unsigned)((s * a.N + hh) * 16 + e)] = fmaf(wr_e, uu, ((p[0] + p[1]) + (p[2] + p[3])) * kInvScale);
     } else if (w < Cfg::kRoleWaves) {
-      // df[b][t][n]: each wave two steps of two heads
-      const int d = w - Cfg::kDfWave, s0 = 2 * (d & 1), h0 = 2 * (d >> 1);
+      // df[b][t][n]: wave d sums the pairs p = 4 d + o (p = step HPW + head)
+      const int d = w - Cfg::kDfWave;
       float x[4];
 #pragma unroll
       for (int o = 0; o < 4; ++o) {
-        const f4 p = *(const f4*)(dfbuf + ((s0 + o / 2) * HPW + h0 + o % 2) * 256 + lane * 4);
+        const f4 p = *(const f4*)(dfbuf + (4 * d + o) * 256 + lane * 4);
         x[o] = (p[0] + p[1]) + (p[2] + p[3]);
       }
-      const float tot = sum4_over_lanes(x[0], x[1], x[2], x[3]);
-      const int s = s0 + (g & 1), hh = h0 + (g >> 1);
+      const float tot = sum4_over_lanes(x[0], x[1], x[2], x[3]);   // row g: x[2 (g & 1) + (g >> 1)]
+      const int pg = 4 * d + 2 * (g & 1) + (g >> 1), s = pg / HPW, hh = pg % HPW;
       float out = tot;
       if (gate) {
         // chain rule through f = exp(-alpha softplus(a + beta)): da, and the
@@ -550,12 +559,10 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     if (n0 + hh < a.N) a.ws_dwr[((size_t)b * a.N + n0 + hh) * 16 + e] = acc;
   }
   if (gate && w == 1 && lane < HPW && n0 + lane < a.N) {
-    const int hh = lane, d0 = 2 * (hh >> 1), r0 = 2 * (hh & 1);
+    const int hh = lane;
     f2 acc = {0.f, 0.f};
 #pragma unroll
-    for (int dd = 0; dd < 2; ++dd)
-#pragma unroll
-      for (int rr = 0; rr < 2; ++rr) acc += *(const f2*)(gacc + ((d0 + dd) * 4 + r0 + rr) * 2);
+    for (int s = 0; s < kSub; ++s) acc += *(const f2*)(gacc + gate_slot<HPW>(s, hh) * 2);
     *(f2*)(a.ws_dgate + ((size_t)b * a.N + n0 + hh) * 2) = acc;
   }
 }
@@ -626,11 +633,20 @@ __global__ __launch_bounds__(256) void m2rnn_bwd_reduce_head_kernel(BwdArgs a) {
   }
 }
 
-constexpr int kBwdHPW = 4;
+// Heads per workgroup of the sweep by the number of (batch row, head)
+// chains: four heads (16 waves, one workgroup per CU) issue the fewest
+// instructions per head-step, but need B N / 4 >= 256 workgroups to fill
+// the GPU; with fewer chains, two heads or one head per workgroup put each
+// chain's four waves on more CUs.
+static int bwd_heads_per_group(int B, int N) {
+  const long long chains = (long long)B * N;
+  return chains >= 1024 ? 4 : chains >= 512 ? 2 : 1;
+}
 
 size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* off_dense, size_t* off_dqk,
                                  size_t* off_dW, size_t* off_dwr, size_t* off_dgate, int* ngroups) {
-  const int ng = (N + kBwdHPW - 1) / kBwdHPW;
+  const int hpw = bwd_heads_per_group(B, N);
+  const int ng = (N + hpw - 1) / hpw;
   auto up = [](size_t x) { return (x + 63) & ~(size_t)63; };   // 256-byte aligned regions
   size_t o = 0;
   *off_dense = o;
@@ -643,19 +659,19 @@ size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* of
   return o;
 }
 
-template <typename TIn, bool GATE>
+template <typename TIn, int HPW, bool GATE>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  typedef BwdCfg<kBwdHPW, GATE> Cfg;
+  typedef BwdCfg<HPW, GATE> Cfg;
   static_assert(Cfg::kBytes <= 160 * 1024, "backward LDS budget");
   static bool attr_set = false;   // per process; the attribute is per kernel
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)m2rnn_bwd_kernel<TIn, kBwdHPW, GATE>,
+    hipError_t e = hipFuncSetAttribute((const void*)m2rnn_bwd_kernel<TIn, HPW, GATE>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   dim3 grid((unsigned)(a.B * a.ngroups)), block(Cfg::NT);
-  hipLaunchKernelGGL((m2rnn_bwd_kernel<TIn, kBwdHPW, GATE>), grid, block, Cfg::kBytes, stream, a);
+  hipLaunchKernelGGL((m2rnn_bwd_kernel<TIn, HPW, GATE>), grid, block, Cfg::kBytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   size_t blocks = ((size_t)a.B * a.T * 32 + 255) / 256;
@@ -665,6 +681,15 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(m2rnn_bwd_reduce_head_kernel, dim3((unsigned)a.N), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <typename TIn, bool GATE>
+static hipError_t launch_bwd_shape(const BwdArgs& a, hipStream_t stream) {
+  switch (bwd_heads_per_group(a.B, a.N)) {
+    case 4: return launch_bwd_t<TIn, 4, GATE>(a, stream);
+    case 2: return launch_bwd_t<TIn, 2, GATE>(a, stream);
+    default: return launch_bwd_t<TIn, 1, GATE>(a, stream);
+  }
 }
 
 hipError_t launch_backward(const BwdArgs& a0, const FwdArgs& replay, int dtype, hipStream_t stream) {
@@ -677,8 +702,8 @@ hipError_t launch_backward(const BwdArgs& a0, const FwdArgs& replay, int dtype, 
     a.ckpt_every = kSub;
     a.nck = (a.T + kSub - 1) / kSub;
   }
-  if (a.ga) return dtype == 0 ? launch_bwd_t<float, true>(a, stream) : launch_bwd_t<bf16_t, true>(a, stream);
-  return dtype == 0 ? launch_bwd_t<float, false>(a, stream) : launch_bwd_t<bf16_t, false>(a, stream);
+  if (a.ga) return dtype == 0 ? launch_bwd_shape<float, true>(a, stream) : launch_bwd_shape<bf16_t, true>(a, stream);
+  return dtype == 0 ? launch_bwd_shape<float, false>(a, stream) : launch_bwd_shape<bf16_t, false>(a, stream);
 }
 
 int backward_sub_steps() { return kSub; }

@@ -55,6 +55,17 @@ def test_backward_parity_small(dtype, B, T, N, ck):
     check(gpu_grads(x, ck, dHT), ref_grads(x, dHT), TOL[dtype], f"{dtype} B{B} T{T} N{N} ck{ck}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,T,N,ck", [(1, 45, 300, 16), (2, 30, 301, 64), (2, 20, 520, 8), (1, 13, 1031, 4)])
+def test_backward_parity_launch_shapes(dtype, B, T, N, ck):
+    """Chain counts B*N in each sweep shape: under 512 (one head per
+    workgroup; the small cases above), 512 to 1023 (two heads per workgroup,
+    one case with the last workgroup half empty) and 1024 and more (four
+    heads, the last group partly empty)."""
+    x = make(B, T, N, dtype, seed=B * 11 + T + N + ck, with_dy=True)
+    check(gpu_grads(x, ck), ref_grads(x), TOL[dtype], f"{dtype} B{B} T{T} N{N} ck{ck} (B*N={B * N})")
+
+
 def test_backward_config_bf16_B8_T2048_N16():
     """The forward + backward workload B=8, T=2048, N=16 (bf16 inputs, fp32
     state, checkpoints every 64 steps), every gradient element by element."""

@@ -124,7 +124,8 @@ def test_gated_forward_saturated_gate(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("B,T,N,ck", [(2, 37, 3, 1), (1, 70, 5, 16), (2, 150, 6, 64), (1, 45, 9, 8), (1, 3, 2, 64)])
+@pytest.mark.parametrize("B,T,N,ck", [(2, 37, 3, 1), (1, 70, 5, 16), (2, 150, 6, 64), (1, 45, 9, 8), (1, 3, 2, 64),
+                                      (2, 20, 301, 16), (1, 13, 1031, 4)])
 def test_gated_backward_parity(dtype, B, T, N, ck):
     """From a given initial state with dH_T; checkpoint intervals below, at
     and above the replay window; head counts that do not fill a workgroup."""
