@@ -109,9 +109,9 @@ extern "C" int m2rnn_forward_gated(int B, int T, int N, int K, int V, int dtype,
 
 extern "C" size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckpt_every) {
   if (B <= 0 || T <= 0 || N <= 0 || K != 64 || V != 16 || ckpt_every < 1) return 0;
-  size_t o1, o2, o3, o4, o5;
+  size_t o1, o2, o3, o4, o5, o6;
   int ng;
-  return sizeof(float) * m2rnn::backward_workspace_floats(B, T, N, ckpt_every, &o1, &o2, &o3, &o4, &o5, &ng);
+  return sizeof(float) * m2rnn::backward_workspace_floats(B, T, N, ckpt_every, &o1, &o2, &o3, &o4, &o5, &o6, &ng);
 }
 
 // f is given (df out) or computed from the gate (da in the df slot, dalpha and
@@ -161,10 +161,10 @@ static int backward_impl(bool gated, int B, int T, int N, int K, int V, int dtyp
     }
     return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "zero fill: %s", hipGetErrorString(e));
   }
-  size_t o_dense, o_dqk, o_dW, o_dwr, o_dgate;
+  size_t o_dense, o_dqk, o_dW, o_dwr, o_dgate, o_amax;
   int ng;
   const size_t need_bytes = sizeof(float) * m2rnn::backward_workspace_floats(B, T, N, ckpt_every, &o_dense, &o_dqk,
-                                                                              &o_dW, &o_dwr, &o_dgate, &ng);
+                                                                              &o_dW, &o_dwr, &o_dgate, &o_amax, &ng);
   if (!workspace || workspace_bytes < need_bytes)
     return fail(M2RNN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need_bytes,
                 workspace ? workspace_bytes : (size_t)0);
@@ -175,6 +175,7 @@ static int backward_impl(bool gated, int B, int T, int N, int K, int V, int dtyp
   a.H_ckpt = H_ckpt; a.dy = dy; a.dH_T = dH_T;
   a.dq = dq; a.dk = dk; a.dv = dv; a.df = df; a.dW = dW; a.dw_r = dw_r; a.dH_0 = dH_0;
   a.ws_dqk = ws + o_dqk; a.ws_dW = ws + o_dW; a.ws_dwr = ws + o_dwr; a.ws_dgate = ws + o_dgate;
+  a.ws_amax = ws + o_amax;
   if (gated) { a.ga = ga; a.galpha = galpha; a.gbeta = gbeta; a.dalpha = dalpha; a.dbeta = dbeta; }
   a.B = B; a.T = T; a.N = N;
   a.ckpt_every = ckpt_every; a.nck = nck; a.ngroups = ng;

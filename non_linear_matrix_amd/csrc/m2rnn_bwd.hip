@@ -24,10 +24,16 @@
 //    waves of one workgroup and a workgroup holds HPW heads of a batch row;
 //    per kSub-step sub-chunk, latest first, the wave replays the steps keeping
 //    H_{t-1} and Z_t in registers, then walks them back;
-//  * C_{t-1}^T = f R^T + W D^T is one v_mfma_f32_16x16x32_bf16 per step (W in
-//    the A operand, hi/lo split of D^T in B, f R^T as the accumulator input;
-//    four exact fp32 MFMAs for fp32 inputs), in the same transposed frame as
-//    the forward, so C stays in registers;
+//  * C_{t-1}^T = f R^T + W D^T is one v_mfma_f32_16x16x16_f16 per step (W in
+//    the A operand, D^T rounded once to fp16 in B, f R^T as the accumulator
+//    input; four exact fp32 MFMAs for fp32 inputs), in the same transposed
+//    frame as the forward, so C stays in registers.  For the fp16 rounding,
+//    dy and dH_T enter scaled by a power of two that puts their largest
+//    magnitude in [1/4, 1/2) (every gradient is linear in them; the outputs
+//    are scaled back exactly), so D sits well inside fp16's range whatever
+//    the scale of the caller's gradients;
+//  * the sweep's few-step replays run one fp16 pass per step
+//    (m2rnn_device.h) from states that hold the forward's precision;
 //  * dW needs a contraction over the rows, which live on lanes: each step the
 //    wave writes its H_{t-1} and D tiles to LDS and reads them back in MFMA
 //    operand layout one step later (one bf16 MFMA on rounded factors for
@@ -42,6 +48,26 @@
 namespace m2rnn {
 
 constexpr int kSub = 4;  // steps between restart states; their H_{t-1}, Z_t stay in registers
+constexpr int kAmaxParts = 1024;   // partial maxima of |dy|, |dH_T| (one per workgroup of the max pass)
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+// The power of two sig = 2^-e that puts mx sig in [1/4, 1/2), and 1 / sig;
+// 1 when mx is zero or not finite.
+__device__ __forceinline__ void grad_scale(float mx, float& sig, float& isig) {
+  sig = isig = 1.0f;
+  if (mx > 0.0f && mx <= 3.4028235e38f) {
+    int e;
+    frexpf(mx, &e);                          // mx in [2^(e-1), 2^e)
+    e = min(max(e + 1, -120), 120);
+    sig = ldexpf(1.0f, -e);
+    isig = ldexpf(1.0f, e);
+  }
+}
 
 // The df role's layout: pair p = s HPW + h of a sub-chunk goes to df wave
 // p / 4 as its value o = p % 4, which sum4_over_lanes leaves in lane row
@@ -146,7 +172,8 @@ struct BwdStage {
   }
 
   // gpar: alpha, beta of the HPW heads, [h][2] (with the gate)
-  __device__ void store(float* buf, int w, int lane, int n0, int len, int N, const float* gpar) const {
+  // dy is staged multiplied by sig (the gradients' scale)
+  __device__ void store(float* buf, int w, int lane, int n0, int len, int N, const float* gpar, float sig) const {
     if (w < NWAVES - NL) return;
     float* K_s = buf;
     float* Q_s = K_s + kSub * 64;
@@ -192,7 +219,7 @@ struct BwdStage {
 #pragma unroll
       for (int i = 0; i < EPC; i += 4) *(f4*)(V_s + t * HPW * 16 + e0 + i) = f4{x[i], x[i + 1], x[i + 2], x[i + 3]};
     } else if (kind == 3) {
-      *(f4*)(U_s + t * HPW * 16 + e0) = f4{x[0], x[1], x[2], x[3]};
+      *(f4*)(U_s + t * HPW * 16 + e0) = f4{x[0], x[1], x[2], x[3]} * sig;
     }
     (void)n;
     if (u < kSub * HPW) {
@@ -218,19 +245,18 @@ struct BwdStage {
 
 // Accumulator-input variant of the contraction used by the C update:
 // returns (W D^T)^T + cin in the transposed frame, i.e. A = W (not W^T).
+// bf16 inputs: W (exact in fp16, see m2rnn_device.h) and D rounded once to
+// fp16, with D normalised through the scale of dy; each product is then off
+// by at most 2^-11 relative, against 2^-8 for a bf16 rounding, which the
+// recursion for C amplified past the bf16-input bar.
 template <typename TIn> struct WBackOperand;
 template <> struct WBackOperand<bf16_t> {
-  bf16x8 a;
+  h4 a;
   __device__ void load(const bf16_t* Wn, int g, int m) {
-    float w[8];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      float x = Wn ? to_f32(Wn[m * 16 + 4 * g + s]) : 0.0f;   // W[v = m][v' = 4g + s]
-      w[s] = w[s + 4] = x;
-    }
-    a = pack8(w);
+    for (int s = 0; s < 4; ++s) a[s] = (_Float16)(Wn ? to_f32(Wn[m * 16 + 4 * g + s]) : 0.0f);   // W[m][4g + s]
   }
-  __device__ f4 apply(f4 d, f4 cin) const { return mfma_bf16(a, split_operand(d), cin); }
+  __device__ f4 apply(f4 d, f4 cin) const { return mfma_f16(a, to_half4(d), cin); }
 };
 template <> struct WBackOperand<float> {
   float a[4];
@@ -273,8 +299,8 @@ __device__ __forceinline__ f4 dw_update(f4 a, f4 b, f4 acc) {
 
 // One forward step of one tile (no readout): returns r = (1 - tanh)/2 and
 // updates P in place.
-template <typename TIn>
-__device__ __forceinline__ f4 fwd_tile_step(const WOperand<TIn>& Aw, f4& P, float ck, f4 vv, f4 fc) {
+template <typename Op>
+__device__ __forceinline__ f4 fwd_tile_step(const Op& Aw, f4& P, float ck, f4 vv, f4 fc) {
   f4 x = Aw.times_state(P);
   f4 r, hg;
 #pragma unroll
@@ -339,14 +365,24 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   const int dv_slot = hw * 320 + m * 20 + ((j + 4 * g + m) & 15);
   const int df_slot = w * 64 + lane;
 
-  WOperand<TIn> Af;
+  typename ReplayOperand<TIn>::type Af;
   Af.load(live ? (const TIn*)a.W + (size_t)n * 256 : nullptr, g, m);
   WBackOperand<TIn> Ab;
   Ab.load(live ? (const TIn*)a.W + (size_t)n * 256 : nullptr, g, m);
 
+  // the gradients' scale: dy and dH_T enter multiplied by sig, every output
+  // leaves multiplied by isig (each wave reduces the partial maxima itself)
+  float sig = 1.0f, isig = 1.0f;
+  if (a.ws_amax) {
+    float mx = 0.0f;
+    for (int i = lane; i < kAmaxParts; i += 64) mx = fmaxf(mx, a.ws_amax[i]);
+    grad_scale(wave_max(mx), sig, isig);
+    sig = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sig)));   // uniform
+    isig = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, isig)));
+  }
   // C in the transposed frame: lane (g, m), register i = C[kk][4g + i]
   f4 C = {0.f, 0.f, 0.f, 0.f};
-  if (live && a.dH_T) C = *(const f4*)(a.dH_T + head * 1024 + kk * 16 + 4 * g);
+  if (live && a.dH_T) C = *(const f4*)(a.dH_T + head * 1024 + kk * 16 + 4 * g) * sig;
   f4 dW = {0.f, 0.f, 0.f, 0.f};   // lane (g, m), register i: c * dW[4g + i][m] partial
   // dv waves (one per head): w_r of their (head, v') and the dw_r partial of
   // their step slot
@@ -381,7 +417,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     BwdStage<TIn, HPW, Cfg::NWAVES, GATE> st;
     const int t0 = (ns - 1) * L, len0 = min(L, a.T - t0);
     st.load(a, w, lane, b, n0, t0, len0);
-    st.store(smem, w, lane, n0, len0, a.N, gpar);
+    st.store(smem, w, lane, n0, len0, a.N, gpar, sig);
   }
   // the next restart state, prefetched one sub-chunk ahead and scaled by c
   // only when it is used (so nothing waits on the load early)
@@ -423,7 +459,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
           const f4 fc = *(const f4*)(F_s + (s * HPW + hw) * 4);
           const f4 uu = *(const f4*)(U_s + (s * HPW + hw) * 16 + 4 * g);
           Pp[s] = P;
-          const f4 r = fwd_tile_step<TIn>(Af, P, K_s[s * 64 + kk], vv, fc);
+          const f4 r = fwd_tile_step(Af, P, K_s[s * 64 + kk], vv, fc);
 #pragma unroll
           for (int i = 0; i < 4; ++i) Z[s][i] = fmaf(-2.0f, r[i], 1.0f);
           // dq_t[kk] (this head) = sum_v H_t[kk][v] u_t[v] = (1/c) sum_v P u
@@ -497,7 +533,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) acc += *(const f4*)(src + hh * 256 + gg * 64 + (((r4 + 4 * gg) & 15) << 2));
-      if (w == 0) acc *= kInvScale;
+      acc *= w == 0 ? kInvScale * isig : isig;
       float* dst = a.ws_dqk + (((size_t)b * ngroups + grp) * a.T + t0) * 128;   // uniform
       if (s < len) *(f4*)(dst + (unsigned)(s * 128 + w * 64 + 4 * r4)) = acc;
     } else if (dv_wave) {
@@ -509,7 +545,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       dwr = fmaf(uu, V_s[(s * HPW + hh) * 16 + e], dwr);
       float* dst = a.dv + (((size_t)b * a.T + t0) * a.N + n0) * 16;   // uniform
       if (s < len && n0 + hh < a.N)
-        dst[(unsigned)((s * a.N + hh) * 16 + e)] = fmaf(wr_e, uu, ((p[0] + p[1]) + (p[2] + p[3])) * kInvScale);
+        dst[(unsigned)((s * a.N + hh) * 16 + e)] = fmaf(wr_e, uu, ((p[0] + p[1]) + (p[2] + p[3])) * kInvScale) * isig;
     } else if (w < Cfg::kRoleWaves) {
       // df[b][t][n]: wave d sums the pairs p = 4 d + o (p = step HPW + head)
       const int d = w - Cfg::kDfWave;
@@ -519,7 +555,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
         const f4 p = *(const f4*)(dfbuf + (4 * d + o) * 256 + lane * 4);
         x[o] = (p[0] + p[1]) + (p[2] + p[3]);
       }
-      const float tot = sum4_over_lanes(x[0], x[1], x[2], x[3]);   // row g: x[2 (g & 1) + (g >> 1)]
+      const float tot = sum4_over_lanes(x[0], x[1], x[2], x[3]) * isig;   // row g: x[2 (g & 1) + (g >> 1)]
       const int pg = 4 * d + 2 * (g & 1) + (g >> 1), s = pg / HPW, hh = pg % HPW;
       float out = tot;
       if (gate) {
@@ -536,16 +572,16 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       if (GATE) dst = sgpr_ptr(dst);
       if (m == 0 && s < len && n0 + hh < a.N) dst[(unsigned)(s * a.N + hh)] = out;
     }
-    st.store(smem + ((it + 1) & 1) * Cfg::kBuf, w, lane, n0, lenn, a.N, gpar);
+    st.store(smem + ((it + 1) & 1) * Cfg::kBuf, w, lane, n0, lenn, a.N, gpar, sig);
     __syncthreads();
   }
 
   if (live) {
     float* dst = a.ws_dW + (head * 4 + j) * 256;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[(4 * g + i) * 16 + m] = dW[i] * kInvScale;
+    for (int i = 0; i < 4; ++i) dst[(4 * g + i) * 16 + m] = dW[i] * (kInvScale * isig);
     // the recursion for C ends at C_0 = dL/dH_0
-    if (a.dH_0) *(f4*)(a.dH_0 + head * 1024 + kk * 16 + 4 * g) = C;
+    if (a.dH_0) *(f4*)(a.dH_0 + head * 1024 + kk * 16 + 4 * g) = C * isig;
   }
   // dw_r: the dv waves hold one partial per (step slot, head, v'); sum the
   // step slots in a fixed order
@@ -556,7 +592,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     float acc = 0.f;
 #pragma unroll
     for (int s = 0; s < kSub; ++s) acc += dfbuf[hh * 64 + s * 16 + e];
-    if (n0 + hh < a.N) a.ws_dwr[((size_t)b * a.N + n0 + hh) * 16 + e] = acc;
+    if (n0 + hh < a.N) a.ws_dwr[((size_t)b * a.N + n0 + hh) * 16 + e] = acc * isig;
   }
   if (gate && w == 1 && lane < HPW && n0 + lane < a.N) {
     const int hh = lane;
@@ -565,6 +601,37 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     for (int s = 0; s < kSub; ++s) acc += *(const f2*)(gacc + gate_slot<HPW>(s, hh) * 2);
     *(f2*)(a.ws_dgate + ((size_t)b * a.N + n0 + hh) * 2) = acc;
   }
+}
+
+// Largest magnitude of dy and dH_T, the gradients that enter the sweep, as
+// kAmaxParts per-workgroup partial maxima (grid = kAmaxParts workgroups);
+// every sweep workgroup reduces them to the same scale.  NaNs are skipped.
+__device__ __forceinline__ float absmax4(f4 v) {
+  return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+}
+
+__global__ __launch_bounds__(256) void m2rnn_bwd_absmax_kernel(const float* dy, size_t ndy4, const float* dH,
+                                                              size_t ndh4, float* part) {
+  __shared__ float wm[4];
+  const size_t stride = (size_t)gridDim.x * 256;
+  const f4* p = (const f4*)dy;
+  float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < ndy4; i += 4 * stride) {   // four loads in flight
+    m0 = fmaxf(m0, absmax4(p[i]));
+    m1 = fmaxf(m1, absmax4(p[i + stride]));
+    m2 = fmaxf(m2, absmax4(p[i + 2 * stride]));
+    m3 = fmaxf(m3, absmax4(p[i + 3 * stride]));
+  }
+  for (; i < ndy4; i += stride) m0 = fmaxf(m0, absmax4(p[i]));
+  if (dH) {
+    const f4* h = (const f4*)dH;
+    for (size_t k = (size_t)blockIdx.x * 256 + threadIdx.x; k < ndh4; k += stride) m1 = fmaxf(m1, absmax4(h[k]));
+  }
+  const float mx = wave_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
+  if (threadIdx.x % 64 == 0) wm[threadIdx.x / 64] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
 }
 
 // Fixed-order sums over workgroups of the dq, dk partials.
@@ -644,7 +711,8 @@ static int bwd_heads_per_group(int B, int N) {
 }
 
 size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* off_dense, size_t* off_dqk,
-                                 size_t* off_dW, size_t* off_dwr, size_t* off_dgate, int* ngroups) {
+                                 size_t* off_dW, size_t* off_dwr, size_t* off_dgate, size_t* off_amax,
+                                 int* ngroups) {
   const int hpw = bwd_heads_per_group(B, N);
   const int ng = (N + hpw - 1) / hpw;
   auto up = [](size_t x) { return (x + 63) & ~(size_t)63; };   // 256-byte aligned regions
@@ -655,6 +723,7 @@ size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* of
   *off_dW = o;   o += up((size_t)B * N * 4 * 256);
   *off_dwr = o;  o += up((size_t)B * N * 16);
   *off_dgate = o; o += up((size_t)B * N * 2);
+  *off_amax = o; o += up(kAmaxParts);
   *ngroups = ng;
   return o;
 }
@@ -701,6 +770,14 @@ hipError_t launch_backward(const BwdArgs& a0, const FwdArgs& replay, int dtype, 
     a.H_ckpt = replay.H_ckpt;
     a.ckpt_every = kSub;
     a.nck = (a.T + kSub - 1) / kSub;
+  }
+  if (dtype == 0) {
+    a.ws_amax = nullptr;   // exact fp32 contractions: no scale needed
+  } else {
+    hipLaunchKernelGGL(m2rnn_bwd_absmax_kernel, dim3(kAmaxParts), dim3(256), 0, stream, a.dy,
+                       (size_t)a.B * a.T * a.N * 4, a.dH_T, a.dH_T ? (size_t)a.B * a.N * 256 : (size_t)0, a.ws_amax);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   if (a.ga) return dtype == 0 ? launch_bwd_shape<float, true>(a, stream) : launch_bwd_shape<bf16_t, true>(a, stream);
   return dtype == 0 ? launch_bwd_shape<float, false>(a, stream) : launch_bwd_shape<bf16_t, false>(a, stream);

@@ -22,6 +22,8 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 
 constexpr float kScale = 2.8853900817779268f;     // 2 / ln 2
 constexpr float kInvScale = 0.34657359027997264f; // ln 2 / 2
@@ -152,6 +154,43 @@ template <> struct WOperand<float> {
     return d;
   }
 };
+
+// ------------------------- one fp16 pass, for the sweep's short replays only
+// The backward's reverse sweep replays a few steps at a time from states of
+// full precision, so the rounding of a single fp16 pass acts over those few
+// steps only and stays well inside the backward's bf16-input bar.  (Over a
+// whole 64-step checkpoint chunk it does not: with a gate close to 1 the
+// rounding errors of the state accumulate across the chunk, so the chunk
+// replay keeps the split.)  Both factors are rounded once to fp16
+// (v_cvt_pk_f16_f32: round to nearest even, subnormals kept; 11 significant
+// bits, 8 times finer than bf16): P = c H is bounded by c, and a bf16 W is
+// exact in fp16 for 2^-14 <= |W| <= 65504.  One v_mfma_f32_16x16x16_f16 per
+// tile instead of the split.
+__device__ __forceinline__ h4 to_half4(f4 x) {
+  const h2 a = __builtin_convertvector((f2{x[0], x[1]}), h2);
+  const h2 b = __builtin_convertvector((f2{x[2], x[3]}), h2);
+  return h4{a[0], a[1], b[0], b[1]};
+}
+
+__device__ __forceinline__ f4 mfma_f16(h4 a, h4 b, f4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// The step's contraction in one fp16 pass: A = W^T (lane 16g+m holds
+// W[4g+s][m], s = 0..3), B = the accumulator tile as is.
+struct WOperandF16 {
+  h4 a;
+  __device__ void load(const bf16_t* Wn, int g, int m) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[s] = (_Float16)(Wn ? to_f32(Wn[(4 * g + s) * 16 + m]) : 0.0f);
+  }
+  __device__ f4 times_state(f4 p) const { return mfma_f16(a, to_half4(p), f4{0.f, 0.f, 0.f, 0.f}); }
+};
+
+// The operand of the sweep's replay: one fp16 pass for bf16 inputs, the exact
+// fp32 MFMAs for fp32 inputs (whose bar is 50 times tighter).
+template <typename TIn> struct ReplayOperand { typedef WOperand<TIn> type; };
+template <> struct ReplayOperand<bf16_t> { typedef WOperandF16 type; };
 
 // ------------------------------------------------------ cross-lane reductions
 // (every control used here reads a lane of the same row, so bound_ctrl never

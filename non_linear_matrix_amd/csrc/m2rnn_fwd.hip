@@ -10,11 +10,11 @@
 // tiles do not remove the sequential dependency", paper Sec. 4.1); this
 // kernel does the same with an MI355X-specific register layout:
 //
-//  * one wave64 owns one (b, n) head for the whole sequence; its 64 x 16 state
-//    sits in four MFMA accumulators (see m2rnn_device.h);
+//  * a (b, n) head's 64 x 16 state sits in four MFMA accumulators (see
+//    m2rnn_device.h), held by one, two or four waves for the whole sequence;
 //  * H_{t-1} W is one v_mfma_f32_16x16x32_bf16 per row tile: W^T in the A
 //    operand (resident), hi/lo bf16 split of the fp32 state in the B operand
-//    (fp32 inputs add a second MFMA for the low half of W);
+//    (fp32 inputs: four exact v_mfma_f32_16x16x4_f32);
 //  * k v^T, tanh, the gate and the readout products are fused per lane;
 //    the readout sum over the 64 rows is an in-register sum over the four
 //    tiles plus a 16-lane DPP reduction;
@@ -24,7 +24,6 @@
 //    staged in LDS and written back as contiguous NW*16-float rows.
 #include "m2rnn_device.h"
 #include "m2rnn_internal.h"
-
 
 namespace m2rnn {
 

@@ -35,13 +35,15 @@ struct BwdArgs {
   float *dalpha = nullptr, *dbeta = nullptr;   // gate parameters' gradients
   float *ws_dqk, *ws_dW, *ws_dwr;   // workspace regions
   float* ws_dgate = nullptr;        // [B][N][2] per-row dalpha, dbeta partials
+  float* ws_amax = nullptr;         // partial maxima of |dy|, |dH_T| (bf16 inputs)
   int B, T, N;
   int ckpt_every, nck, ngroups;
 };
 
 // Workspace layout (in floats) for the backward; returns the total.
 size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* off_dense, size_t* off_dqk,
-                                 size_t* off_dW, size_t* off_dwr, size_t* off_dgate, int* ngroups);
+                                 size_t* off_dW, size_t* off_dwr, size_t* off_dgate, size_t* off_amax,
+                                 int* ngroups);
 // Steps between the states the reverse sweep restarts from.
 int backward_sub_steps();
 // When a.ckpt_every exceeds the sub-step count, `replay` (a densify launch

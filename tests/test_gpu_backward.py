@@ -87,6 +87,45 @@ def test_backward_f_one_closed_form(dtype):
     assert np.max(np.abs(gg["df"] - gr["df"])) <= TOL[dtype] * max(1.0, np.max(np.abs(gr["df"])))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [-40, 40])
+@pytest.mark.parametrize("gated", [False, True])
+def test_backward_gradient_scale_equivariant(dtype, k, gated):
+    """Every gradient is linear in (dy, dH_T).  Scaling both by 2^k must scale
+    every output, dH_0 included, by exactly 2^k, bit for bit, also where the
+    scaled values fall far outside fp16's range (2^-40 is the order of the
+    gradients of a loss averaged over many tokens).  For bf16 inputs this
+    pins the power-of-two normalisation the sweep applies before it rounds D
+    to fp16: without it, D * 2^-40 would round to zero."""
+    B, T, N, ck = 2, 70, 5, 16
+    x = make(B, T, N, dtype, seed=31, with_dy=True)
+    dHT = torch.randn(B, N, 64, 16, generator=torch.Generator().manual_seed(3))
+    if gated:
+        gt = m2rnn_inputs.make_gate(B, T, N, dtype, seed=31)
+        g = {n: t.cuda() for n, t in gt.items()}
+    gx = to_gpu(x)
+
+    def run(scale):
+        dy = gx["dy"] * scale
+        dh = (dHT * scale).cuda()
+        if gated:
+            _, _, Hck = m2.forward_gated(gx["q"], gx["k"], gx["v"], g["a"], g["alpha"], g["beta"], gx["W"], gx["wr"],
+                                         ckpt_every=ck)
+            out = m2.backward_gated(gx["q"], gx["k"], gx["v"], g["a"], g["alpha"], g["beta"], gx["W"], gx["wr"], Hck,
+                                    ck, dy, dH_T=dh, want_dH_0=True)
+        else:
+            _, _, Hck = m2.forward(gx["q"], gx["k"], gx["v"], gx["f"], gx["W"], gx["wr"], ckpt_every=ck)
+            out = m2.backward(gx["q"], gx["k"], gx["v"], gx["f"], gx["W"], gx["wr"], Hck, ck, dy, dH_T=dh,
+                              want_dH_0=True)
+        torch.cuda.synchronize()
+        return {n: t.cpu() for n, t in out.items()}
+
+    base, other = run(1.0), run(2.0 ** k)
+    for name, t in base.items():
+        assert bool(torch.isfinite(t).all()), name
+        assert torch.equal(other[name], t * 2.0 ** k), (name, k)
+
+
 def test_backward_checkpoint_interval_invariance():
     x = make(2, 130, 3, "f32", seed=21, with_dy=True)
     base = gpu_grads(x, 1)
