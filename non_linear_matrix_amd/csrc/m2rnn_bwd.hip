@@ -206,15 +206,24 @@ struct BwdStage {
 #pragma unroll
       for (int i = 0; i < EPC; i += 4) *(f4*)(Q_s + t * 64 + e0 + i) = f4{x[i], x[i + 1], x[i + 2], x[i + 3]};
     } else if (kind == 1) {
+      // row e = 16 tile + 4 r + g goes to [tile][g][r] of Kp_s; a chunk starts
+      // at a multiple of 4, so element i sits at base + (i % 4) * 4 + i / 4
+      if constexpr (sizeof(TIn) == 2) {
+        // k itself in fp16 (exact for bf16 values in fp16's normal range); a
+        // chunk is 8 rows, r0 and r0 + 1 of each g, which sit side by side
+        uint32_t* kp = (uint32_t*)((_Float16*)Kp_s + t * 64 + (e0 / 16) * 16 + (e0 % 16) / 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kp[i * 2] = __builtin_bit_cast(uint32_t, (h2{(_Float16)x[i], (_Float16)x[i + 4]}));
+      }
 #pragma unroll
       for (int i = 0; i < EPC; ++i) x[i] *= kScale;
 #pragma unroll
       for (int i = 0; i < EPC; i += 4) *(f4*)(K_s + t * 64 + e0 + i) = f4{x[i], x[i + 1], x[i + 2], x[i + 3]};
-      // row e = 16 tile + 4 r + g goes to [tile][g][r]; a chunk starts at a
-      // multiple of 4, so element i sits at base + (i % 4) * 4 + i / 4
-      float* kp = Kp_s + t * 64 + (e0 / 16) * 16 + (e0 % 16) / 4;
+      if constexpr (sizeof(TIn) == 4) {
+        float* kp = Kp_s + t * 64 + (e0 / 16) * 16 + (e0 % 16) / 4;   // c k
 #pragma unroll
-      for (int i = 0; i < EPC; ++i) kp[(i % 4) * 4 + i / 4] = x[i];
+        for (int i = 0; i < EPC; ++i) kp[(i % 4) * 4 + i / 4] = x[i];
+      }
     } else if (kind == 2) {
 #pragma unroll
       for (int i = 0; i < EPC; i += 4) *(f4*)(V_s + t * HPW * 16 + e0 + i) = f4{x[i], x[i + 1], x[i + 2], x[i + 3]};
@@ -256,7 +265,8 @@ template <> struct WBackOperand<bf16_t> {
 #pragma unroll
     for (int s = 0; s < 4; ++s) a[s] = (_Float16)(Wn ? to_f32(Wn[m * 16 + 4 * g + s]) : 0.0f);   // W[m][4g + s]
   }
-  __device__ f4 apply(f4 d, f4 cin) const { return mfma_f16(a, to_half4(d), cin); }
+  __device__ f4 apply(f4 d, f4 cin) const { return apply_half(to_half4(d), cin); }
+  __device__ f4 apply_half(h4 dh, f4 cin) const { return mfma_f16(a, dh, cin); }
 };
 template <> struct WBackOperand<float> {
   float a[4];
@@ -272,36 +282,19 @@ template <> struct WBackOperand<float> {
 };
 
 // dW[v][v'] += sum over 16 rows kk of A[kk][v] B[kk][v'], with lane (g, m)
-// holding A, B at rows 4r + g (r = 0..3) and column m.  fp32 inputs: four
-// exact v_mfma_f32_16x16x4_f32.  bf16 inputs: one v_mfma_f32_16x16x16_bf16 on
-// the RNE bf16 roundings of both factors.  Each product is off by at most
-// ~2^-8 relative; over a whole sequence the errors are independent and the
-// sum over time and rows stays within ~6e-4 of max|dW| (bf16 inputs carry a
-// 5e-3 bar), for a quarter of the VALU work of the hi/lo products.
-template <typename TIn>
+// holding A, B at rows 4r + g (r = 0..3) and column m: four exact
+// v_mfma_f32_16x16x4_f32 (fp32 inputs; bf16 inputs contract the fp16 tiles
+// in one v_mfma_f32_16x16x16_f16, each product then off by at most 2^-10
+// relative, independently over rows and time).
 __device__ __forceinline__ f4 dw_update(f4 a, f4 b, f4 acc) {
-  if constexpr (sizeof(TIn) == 4) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], acc, 0, 0, 0);
-    return acc;
-  } else {
-    typedef short s4 __attribute__((ext_vector_type(4)));
-    const bf16x2 a01 = __builtin_convertvector((f2{a[0], a[1]}), bf16x2);
-    const bf16x2 a23 = __builtin_convertvector((f2{a[2], a[3]}), bf16x2);
-    const bf16x2 b01 = __builtin_convertvector((f2{b[0], b[1]}), bf16x2);
-    const bf16x2 b23 = __builtin_convertvector((f2{b[2], b[3]}), bf16x2);
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-    const u32x2 au = {__builtin_bit_cast(uint32_t, a01), __builtin_bit_cast(uint32_t, a23)};
-    const u32x2 bu = {__builtin_bit_cast(uint32_t, b01), __builtin_bit_cast(uint32_t, b23)};
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, au), __builtin_bit_cast(s4, bu), acc, 0, 0, 0);
-  }
+  for (int r = 0; r < 4; ++r) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], b[r], acc, 0, 0, 0);
+  return acc;
 }
 
-// One forward step of one tile (no readout): returns r = (1 - tanh)/2 and
-// updates P in place.
-template <typename Op>
-__device__ __forceinline__ f4 fwd_tile_step(const Op& Aw, f4& P, float ck, f4 vv, f4 fc) {
-  f4 x = Aw.times_state(P);
+// The rest of one forward step of one tile (no readout) once x = c (H W)^T
+// is known: returns r = (1 - tanh)/2 and updates P in place.
+__device__ __forceinline__ f4 fwd_tile_finish(f4 x, f4& P, float ck, f4 vv, f4 fc) {
   f4 r, hg;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -337,6 +330,10 @@ __device__ __forceinline__ float sum4_over_lanes(float x0, float x1, float x2, f
 template <typename TIn, int HPW, bool GATE>
 __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) void m2rnn_bwd_kernel(BwdArgs a) {
   typedef BwdCfg<HPW, GATE> Cfg;
+  // bf16 inputs: fp16 LDS transposes, dv partials from k itself; fp32
+  // inputs: fp32 transposes, dv partials from c k
+  constexpr bool kHalf = sizeof(TIn) == 2;
+  constexpr float kDvScale = kHalf ? 1.0f : kInvScale;
   extern __shared__ float smem[];
   float* xpose = smem + 2 * Cfg::kBuf;
   float* qkbuf = xpose + Cfg::kXpose;
@@ -442,12 +439,14 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     const float* V_s = Q_s + kSub * 64;
     const float* F_s = V_s + kSub * HPW * 16;
     const float* U_s = F_s + kSub * HPW * 4;
-    const float* Kp_s = U_s + kSub * HPW * 16;     // c k permuted, [s][tile][g][r]
+    const float* Kp_s = U_s + kSub * HPW * 16;     // k permuted, [s][tile][g][r] (c k in fp32, k in fp16)
     const float* G_s = Kp_s + kSub * 64;            // gate factors, [df wave][row][2]
 
     if (live) {
-      // replay the sub-chunk keeping H_{t-1} and Z_t on chip
+      // replay the sub-chunk keeping H_{t-1} and Z_t on chip (and, for bf16
+      // inputs, the fp16 rounding of H_{t-1} its contraction used)
       f4 Pp[kSub], Z[kSub];
+      h4 Ph[kSub];
 #pragma unroll
       // Steps s >= len of a short last sub-chunk are staged as f = 1 with
       // q = k = v = u = 0: an exact identity for C and a zero contribution to
@@ -459,7 +458,14 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
           const f4 fc = *(const f4*)(F_s + (s * HPW + hw) * 4);
           const f4 uu = *(const f4*)(U_s + (s * HPW + hw) * 16 + 4 * g);
           Pp[s] = P;
-          const f4 r = fwd_tile_step(Af, P, K_s[s * 64 + kk], vv, fc);
+          f4 x;
+          if constexpr (kHalf) {
+            Ph[s] = to_half4(P);
+            x = Af.times_half(Ph[s]);
+          } else {
+            x = Af.times_state(P);
+          }
+          const f4 r = fwd_tile_finish(x, P, K_s[s * 64 + kk], vv, fc);
 #pragma unroll
           for (int i = 0; i < 4; ++i) Z[s][i] = fmaf(-2.0f, r[i], 1.0f);
           // dq_t[kk] (this head) = sum_v H_t[kk][v] u_t[v] = (1/c) sum_v P u
@@ -475,20 +481,48 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       // they run one step behind the sweep so that the LDS round trip
       // overlaps the next step's arithmetic (LDS requests of a wave complete
       // in issue order, so no wait is needed between the write and the read).
+      //
+      // bf16 inputs: the fp16 tiles the contractions already rounded go to
+      // LDS as 8-byte chunks (lane (g, m): row m, columns 4g..4g+3) and come
+      // back with ds_read_b64_tr_b16, which hands lane i of each 16-lane
+      // group, as element s, element i % 4 of the chunk that lane
+      // 4 s + i / 4 of the group addressed (checked on the GPU).  Lane (g, m)
+      // addresses the chunk (row 4 (m / 4) + g, columns 4 (m % 4) ..), so it
+      // receives X[4 s + g][m], s = 0..3: the operand layout.  Chunk (row,
+      // block) of a tile sits at 16 (row / 4) + 4 ((row % 4) ^ block) +
+      // (block ^ row / 4), which spreads the 16 chunks of every 16-lane
+      // write and every 16-lane transposed read over distinct banks.
+      const int xw = 16 * (m >> 2) + 4 * ((m & 3) ^ g) + (g ^ (m >> 2));            // chunk this lane writes
+      const int xr = 16 * (m >> 2) + 4 * (g ^ (m & 3)) + ((m & 3) ^ (m >> 2));        // chunk it reads
+      h4* xh = (h4*)xp;   // [slot][H | D][64 chunks]
       auto drain = [&](int ps) {
-        const float* xs = xp + (ps & 1) * 2 * Cfg::kTile;
-        const f4 ckp = *(const f4*)(Kp_s + ps * 64 + j * 16 + g * 4);   // c k[16j+4r+g], r = 0..3
-        float dvp = 0.f;
-        f4 av, bv;
+        if constexpr (kHalf) {
+          typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+          const h4 ah = __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (lds_i16x4*)(xh + (ps & 1) * 128 + xr)));   // c H_{t-1}[16j+4s+g][m]
+          const h4 bh = __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                                   (lds_i16x4*)(xh + (ps & 1) * 128 + 64 + xr)));   // D[16j+4s+g][m]
+          const h4 kh = *(const h4*)((const _Float16*)Kp_s + ps * 64 + j * 16 + g * 4);   // k[16j+4s+g]
+          const float dvp = __builtin_amdgcn_fdot2(h2{bh[0], bh[1]}, h2{kh[0], kh[1]},
+                                                   __builtin_amdgcn_fdot2(h2{bh[2], bh[3]}, h2{kh[2], kh[3]}, 0.0f, false),
+                                                   false);
+          dW = mfma_f16(ah, bh, dW);
+          dvbuf[ps * HPW * 320 + dv_slot] = dvp;            // partial of dv[v' = m] over rows 4s+g
+        } else {
+          const float* xs = xp + (ps & 1) * 2 * Cfg::kTile;
+          const f4 ckp = *(const f4*)(Kp_s + ps * 64 + j * 16 + g * 4);   // c k[16j+4r+g], r = 0..3
+          float dvp = 0.f;
+          f4 av, bv;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int at = (m / 4) * Cfg::kXs + (4 * r + g) * 4 + m % 4;
-          av[r] = xs[at];                                   // c H_{t-1}[16j+4r+g][v = m]
-          bv[r] = xs[Cfg::kTile + at];                      // D[16j+4r+g][v' = m]
-          dvp = fmaf(bv[r], ckp[r], dvp);
+          for (int r = 0; r < 4; ++r) {
+            const int at = (m / 4) * Cfg::kXs + (4 * r + g) * 4 + m % 4;
+            av[r] = xs[at];                                   // c H_{t-1}[16j+4r+g][v = m]
+            bv[r] = xs[Cfg::kTile + at];                      // D[16j+4r+g][v' = m]
+            dvp = fmaf(bv[r], ckp[r], dvp);
+          }
+          dW = dw_update(av, bv, dW);
+          dvbuf[ps * HPW * 320 + dv_slot] = dvp;              // partial of dv[v' = m] over rows 4r+g
         }
-        dW = dw_update<TIn>(av, bv, dW);
-        dvbuf[ps * HPW * 320 + dv_slot] = dvp;              // partial of dv[v' = m] over rows 4r+g
       };
 #pragma unroll
       for (int s = kSub - 1; s >= 0; --s) {
@@ -508,13 +542,21 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
             fR[i] = fc[0] * R[i];
             dk = fmaf(D[i], vv[i], dk);
           }
-          C = Ab.apply(D, fR);                                       // C_{t-1} = f R + D W^T
           // per-lane partials of dk_t[kk] (over v' = 4g..4g+3) and df_t
           qkbuf[(2 * s + 1) * HPW * 256 + qk_slot] = dk;
           dfbuf[s * HPW * 256 + df_slot] = dfp;
-          // stage H_{t-1} and D of this step, finish the previous step
-          *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + g * Cfg::kXs + m * 4) = Pp[s];
-          *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + Cfg::kTile + g * Cfg::kXs + m * 4) = D;
+          // C_{t-1} = f R + D W^T; stage H_{t-1} and D of this step, finish
+          // the previous step
+          if constexpr (kHalf) {
+            const h4 Dh = to_half4(D);
+            C = Ab.apply_half(Dh, fR);
+            xh[(s & 1) * 128 + xw] = Ph[s];
+            xh[(s & 1) * 128 + 64 + xw] = Dh;
+          } else {
+            C = Ab.apply(D, fR);
+            *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + g * Cfg::kXs + m * 4) = Pp[s];
+            *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + Cfg::kTile + g * Cfg::kXs + m * 4) = D;
+          }
           if (s < kSub - 1) drain(s + 1);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -545,7 +587,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       dwr = fmaf(uu, V_s[(s * HPW + hh) * 16 + e], dwr);
       float* dst = a.dv + (((size_t)b * a.T + t0) * a.N + n0) * 16;   // uniform
       if (s < len && n0 + hh < a.N)
-        dst[(unsigned)((s * a.N + hh) * 16 + e)] = fmaf(wr_e, uu, ((p[0] + p[1]) + (p[2] + p[3])) * kInvScale) * isig;
+        dst[(unsigned)((s * a.N + hh) * 16 + e)] = fmaf(wr_e, uu, ((p[0] + p[1]) + (p[2] + p[3])) * kDvScale) * isig;
     } else if (w < Cfg::kRoleWaves) {
       // df[b][t][n]: wave d sums the pairs p = 4 d + o (p = step HPW + head)
       const int d = w - Cfg::kDfWave;
@@ -617,11 +659,14 @@ __global__ __launch_bounds__(256) void m2rnn_bwd_absmax_kernel(const float* dy, 
   const f4* p = (const f4*)dy;
   float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
   size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 3 * stride < ndy4; i += 4 * stride) {   // four loads in flight
-    m0 = fmaxf(m0, absmax4(p[i]));
-    m1 = fmaxf(m1, absmax4(p[i + stride]));
-    m2 = fmaxf(m2, absmax4(p[i + 2 * stride]));
-    m3 = fmaxf(m3, absmax4(p[i + 3 * stride]));
+  for (; i + 7 * stride < ndy4; i += 8 * stride) {   // eight loads in flight
+    f4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[i + u * stride];
+    m0 = fmaxf(m0, fmaxf(absmax4(v[0]), absmax4(v[1])));
+    m1 = fmaxf(m1, fmaxf(absmax4(v[2]), absmax4(v[3])));
+    m2 = fmaxf(m2, fmaxf(absmax4(v[4]), absmax4(v[5])));
+    m3 = fmaxf(m3, fmaxf(absmax4(v[6]), absmax4(v[7])));
   }
   for (; i < ndy4; i += stride) m0 = fmaxf(m0, absmax4(p[i]));
   if (dH) {

@@ -24,6 +24,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kScale = 2.8853900817779268f;     // 2 / ln 2
 constexpr float kInvScale = 0.34657359027997264f; // ln 2 / 2
@@ -184,7 +185,9 @@ struct WOperandF16 {
 #pragma unroll
     for (int s = 0; s < 4; ++s) a[s] = (_Float16)(Wn ? to_f32(Wn[(4 * g + s) * 16 + m]) : 0.0f);
   }
-  __device__ f4 times_state(f4 p) const { return mfma_f16(a, to_half4(p), f4{0.f, 0.f, 0.f, 0.f}); }
+  __device__ f4 times_state(f4 p) const { return times_half(to_half4(p)); }
+  // the same from a tile already rounded to fp16
+  __device__ f4 times_half(h4 ph) const { return mfma_f16(a, ph, f4{0.f, 0.f, 0.f, 0.f}); }
 };
 
 // The operand of the sweep's replay: one fp16 pass for bf16 inputs, the exact
