@@ -119,8 +119,9 @@ struct BwdCfg {
 };
 
 // Staging of one sub-chunk (kSub steps from t0, the first len of them real)
-// through registers into an LDS buffer.  The last NL waves load: thread u of
-// them fetches one 16-byte chunk of q, k, v or u = dy, and one f value.  The
+// through registers into an LDS buffer.  The waves of the last NL roles load:
+// thread u of them fetches one 16-byte chunk of q, k, v or u = dy, and one f
+// value.  The
 // load path is the same straight line for every loading thread (addresses of
 // steps past len, of a missing head, and of idle threads are clamped to valid
 // data), so no register of an in-flight load is ever merged or copied and
@@ -148,9 +149,10 @@ struct BwdStage {
     else { kind = 4; t = 0; e0 = 0; }
   }
 
-  __device__ void load(const BwdArgs& a, int w, int lane, int b, int n0, int t0, int len) {
-    if (w < NWAVES - NL) return;
-    const int u = (w - (NWAVES - NL)) * 64 + lane;
+  // rw: the wave's role (role_wave); the last NL roles load
+  __device__ void load(const BwdArgs& a, int rw, int lane, int b, int n0, int t0, int len) {
+    if (rw < NWAVES - NL) return;
+    const int u = (rw - (NWAVES - NL)) * 64 + lane;
     int kind, t, e0;
     decode(u, kind, t, e0);
     const bool ok = t < len && (kind < 2 || n0 + e0 / 16 < a.N);
@@ -173,8 +175,8 @@ struct BwdStage {
 
   // gpar: alpha, beta of the HPW heads, [h][2] (with the gate)
   // dy is staged multiplied by sig (the gradients' scale)
-  __device__ void store(float* buf, int w, int lane, int n0, int len, int N, const float* gpar, float sig) const {
-    if (w < NWAVES - NL) return;
+  __device__ void store(float* buf, int rw, int lane, int n0, int len, int N, const float* gpar, float sig) const {
+    if (rw < NWAVES - NL) return;
     float* K_s = buf;
     float* Q_s = K_s + kSub * 64;
     float* V_s = Q_s + kSub * 64;
@@ -182,7 +184,7 @@ struct BwdStage {
     float* U_s = F_s + kSub * HPW * 4;
     float* Kp_s = U_s + kSub * HPW * 16;
     float* G_s = Kp_s + kSub * 64;
-    const int u = (w - (NWAVES - NL)) * 64 + lane;
+    const int u = (rw - (NWAVES - NL)) * 64 + lane;
     int kind, t, e0;
     decode(u, kind, t, e0);
     const bool ok = t < len && (kind < 2 || n0 + e0 / 16 < N);
@@ -251,6 +253,18 @@ struct BwdStage {
     }
   }
 };
+
+// Role of wave w in the reduction pass and in the staging (roles: 0 dq, 1 dk,
+// then one dv wave per head, one df wave per four (step, head) pairs, and
+// the last NL loaders).  Waves w, w + 4, w + 8 and w + 12 of a workgroup share
+// one SIMD (checked on the GPU), and the pass ends at a barrier, so with four
+// heads and three loaders the roles are dealt out to even the SIMDs: dq, dk
+// and the last head's dv and df on one; a loader, a dv and a df on each other.
+template <int HPW, int NL>
+__device__ __forceinline__ int role_wave(int w) {
+  if constexpr (HPW == 4 && NL == 3) return w == 0 ? 0 : w <= 3 ? 12 + w : w - 3;
+  return w;
+}
 
 // Accumulator-input variant of the contraction used by the C update:
 // returns (W D^T)^T + cin in the transposed frame, i.e. A = W (not W^T).
@@ -345,6 +359,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   const int w = __builtin_amdgcn_readfirstlane(tid / 64);
   const int lane = tid % 64, g = lane / 16, m = lane % 16;
   const int hw = w / 4, j = w % 4;               // head in group, row tile
+  typedef BwdStage<TIn, HPW, Cfg::NWAVES, GATE> Stage;
+  const int rw = role_wave<HPW, Stage::NL>(w);   // role in the pass and the staging
   const int ngroups = (a.N + HPW - 1) / HPW;
   const int b = blockIdx.x / ngroups;
   const int grp = blockIdx.x % ngroups;
@@ -383,7 +399,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   f4 dW = {0.f, 0.f, 0.f, 0.f};   // lane (g, m), register i: c * dW[4g + i][m] partial
   // dv waves (one per head): w_r of their (head, v') and the dw_r partial of
   // their step slot
-  const bool dv_wave = w >= Cfg::kDvWave && w < Cfg::kDvWave + HPW;
+  const bool dv_wave = rw >= Cfg::kDvWave && rw < Cfg::kDvWave + HPW;
   float wr_e = 0.f, dwr = 0.f;
   // the gate parameters of the group's heads, read by the threads that stage
   // f; the df waves' dalpha, dbeta sums (slot gate_slot(s, h): row r of df
@@ -401,7 +417,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   }
   constexpr bool gate = GATE;
   if (dv_wave) {
-    const int hh = w - Cfg::kDvWave;
+    const int hh = rw - Cfg::kDvWave;
     if (n0 + hh < a.N) wr_e = to_f32(((const TIn*)a.wr)[(size_t)(n0 + hh) * 16 + m]);
   }
   if (!live) {
@@ -411,10 +427,10 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   }
 
   {
-    BwdStage<TIn, HPW, Cfg::NWAVES, GATE> st;
+    Stage st;
     const int t0 = (ns - 1) * L, len0 = min(L, a.T - t0);
-    st.load(a, w, lane, b, n0, t0, len0);
-    st.store(smem, w, lane, n0, len0, a.N, gpar, sig);
+    st.load(a, rw, lane, b, n0, t0, len0);
+    st.store(smem, rw, lane, n0, len0, a.N, gpar, sig);
   }
   // the next restart state, prefetched one sub-chunk ahead and scaled by c
   // only when it is used (so nothing waits on the load early)
@@ -429,9 +445,9 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     // The last iteration fetches sub-chunk 0 again and stages it into the
     // buffer no one reads: no branch, so nothing in flight gets copied.
     const int sn = sb > 0 ? sb - 1 : 0;
-    BwdStage<TIn, HPW, Cfg::NWAVES, GATE> st;
+    Stage st;
     const int lenn = min(L, a.T - sn * L);
-    st.load(a, w, lane, b, n0, sn * L, lenn);
+    st.load(a, rw, lane, b, n0, sn * L, lenn);
     if (live) Hnext = *(const f4*)(Hs + (size_t)sn * 1024);
     const float* buf = smem + (it & 1) * Cfg::kBuf;
     const float* K_s = buf;
@@ -565,22 +581,22 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     }
     __syncthreads();
     // ---- pass: reduce this sub-chunk's partials; each wave has one role.
-    if (w < 2) {
+    if (rw < 2) {
       // dq (wave 0), dk (wave 1): lane (s, 4-row quad r4) sums the HPW heads
       // and four lane groups -> workspace [b][grp][t][dq | dk][64]
       const int s = lane / 16, r4 = lane % 16;
-      const float* src = qkbuf + (2 * s + w) * HPW * 256;
+      const float* src = qkbuf + (2 * s + rw) * HPW * 256;
       f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh)
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) acc += *(const f4*)(src + hh * 256 + gg * 64 + (((r4 + 4 * gg) & 15) << 2));
-      acc *= w == 0 ? kInvScale * isig : isig;
+      acc *= rw == 0 ? kInvScale * isig : isig;
       float* dst = a.ws_dqk + (((size_t)b * ngroups + grp) * a.T + t0) * 128;   // uniform
-      if (s < len) *(f4*)(dst + (unsigned)(s * 128 + w * 64 + 4 * r4)) = acc;
+      if (s < len) *(f4*)(dst + (unsigned)(s * 128 + rw * 64 + 4 * r4)) = acc;
     } else if (dv_wave) {
       // dv[b][t][n][v'] = (1/c) (sum of the 16 (tile, g) partials) + w_r u; dw_r
-      const int hh = w - Cfg::kDvWave, s = lane / 16, e = lane % 16;
+      const int hh = rw - Cfg::kDvWave, s = lane / 16, e = lane % 16;
       const float* d = dvbuf + (s * HPW + hh) * 320 + e * 20;
       const f4 p = (*(const f4*)d + *(const f4*)(d + 4)) + (*(const f4*)(d + 8) + *(const f4*)(d + 12));
       const float uu = U_s[(s * HPW + hh) * 16 + e];
@@ -588,9 +604,9 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       float* dst = a.dv + (((size_t)b * a.T + t0) * a.N + n0) * 16;   // uniform
       if (s < len && n0 + hh < a.N)
         dst[(unsigned)((s * a.N + hh) * 16 + e)] = fmaf(wr_e, uu, ((p[0] + p[1]) + (p[2] + p[3])) * kDvScale) * isig;
-    } else if (w < Cfg::kRoleWaves) {
+    } else if (rw < Cfg::kRoleWaves) {
       // df[b][t][n]: wave d sums the pairs p = 4 d + o (p = step HPW + head)
-      const int d = w - Cfg::kDfWave;
+      const int d = rw - Cfg::kDfWave;
       float x[4];
 #pragma unroll
       for (int o = 0; o < 4; ++o) {
@@ -614,7 +630,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       if (GATE) dst = sgpr_ptr(dst);
       if (m == 0 && s < len && n0 + hh < a.N) dst[(unsigned)(s * a.N + hh)] = out;
     }
-    st.store(smem + ((it + 1) & 1) * Cfg::kBuf, w, lane, n0, lenn, a.N, gpar, sig);
+    st.store(smem + ((it + 1) & 1) * Cfg::kBuf, rw, lane, n0, lenn, a.N, gpar, sig);
     __syncthreads();
   }
 
@@ -627,7 +643,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   }
   // dw_r: the dv waves hold one partial per (step slot, head, v'); sum the
   // step slots in a fixed order
-  if (dv_wave) dfbuf[(w - Cfg::kDvWave) * 64 + lane] = dwr;
+  if (dv_wave) dfbuf[(rw - Cfg::kDvWave) * 64 + lane] = dwr;
   __syncthreads();
   if (w == 0 && lane < HPW * 16) {
     const int hh = lane / 16, e = lane % 16;
@@ -655,23 +671,26 @@ __device__ __forceinline__ float absmax4(f4 v) {
 __global__ __launch_bounds__(256) void m2rnn_bwd_absmax_kernel(const float* dy, size_t ndy4, const float* dH,
                                                               size_t ndh4, float* part) {
   __shared__ float wm[4];
-  const size_t stride = (size_t)gridDim.x * 256;
+  // workgroup w streams its own contiguous slice of dy, 8 x 4 KB at a time
+  const size_t per = (ndy4 + gridDim.x - 1) / gridDim.x;
+  const size_t lo = min(ndy4, (size_t)blockIdx.x * per), hi = min(ndy4, lo + per);
   const f4* p = (const f4*)dy;
   float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
-  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
-  for (; i + 7 * stride < ndy4; i += 8 * stride) {   // eight loads in flight
+  size_t i = lo + threadIdx.x;
+  for (; i + 7 * 256 < hi; i += 8 * 256) {   // eight loads in flight
     f4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[i + u * stride];
+    for (int u = 0; u < 8; ++u) v[u] = p[i + u * 256];
     m0 = fmaxf(m0, fmaxf(absmax4(v[0]), absmax4(v[1])));
     m1 = fmaxf(m1, fmaxf(absmax4(v[2]), absmax4(v[3])));
     m2 = fmaxf(m2, fmaxf(absmax4(v[4]), absmax4(v[5])));
     m3 = fmaxf(m3, fmaxf(absmax4(v[6]), absmax4(v[7])));
   }
-  for (; i < ndy4; i += stride) m0 = fmaxf(m0, absmax4(p[i]));
+  for (; i < hi; i += 256) m0 = fmaxf(m0, absmax4(p[i]));
   if (dH) {
     const f4* h = (const f4*)dH;
-    for (size_t k = (size_t)blockIdx.x * 256 + threadIdx.x; k < ndh4; k += stride) m1 = fmaxf(m1, absmax4(h[k]));
+    for (size_t k = (size_t)blockIdx.x * 256 + threadIdx.x; k < ndh4; k += (size_t)gridDim.x * 256)
+      m1 = fmaxf(m1, absmax4(h[k]));
   }
   const float mx = wave_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
   if (threadIdx.x % 64 == 0) wm[threadIdx.x / 64] = mx;
@@ -808,14 +827,8 @@ static hipError_t launch_bwd_shape(const BwdArgs& a, hipStream_t stream) {
 
 hipError_t launch_backward(const BwdArgs& a0, const FwdArgs& replay, int dtype, hipStream_t stream) {
   BwdArgs a = a0;
-  if (a.ckpt_every > kSub) {
-    // states every kSub steps, replayed from the caller's checkpoints
-    hipError_t e = launch_densify(replay, dtype, stream);
-    if (e != hipSuccess) return e;
-    a.H_ckpt = replay.H_ckpt;
-    a.ckpt_every = kSub;
-    a.nck = (a.T + kSub - 1) / kSub;
-  }
+  // the gradients' scale first: the read-only pass over dy then does not
+  // meet the replay's freshly written states in the caches
   if (dtype == 0) {
     a.ws_amax = nullptr;   // exact fp32 contractions: no scale needed
   } else {
@@ -823,6 +836,14 @@ hipError_t launch_backward(const BwdArgs& a0, const FwdArgs& replay, int dtype, 
                        (size_t)a.B * a.T * a.N * 4, a.dH_T, a.dH_T ? (size_t)a.B * a.N * 256 : (size_t)0, a.ws_amax);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (a.ckpt_every > kSub) {
+    // states every kSub steps, replayed from the caller's checkpoints
+    hipError_t e = launch_densify(replay, dtype, stream);
+    if (e != hipSuccess) return e;
+    a.H_ckpt = replay.H_ckpt;
+    a.ckpt_every = kSub;
+    a.nck = (a.T + kSub - 1) / kSub;
   }
   if (a.ga) return dtype == 0 ? launch_bwd_shape<float, true>(a, stream) : launch_bwd_shape<bf16_t, true>(a, stream);
   return dtype == 0 ? launch_bwd_shape<float, false>(a, stream) : launch_bwd_shape<bf16_t, false>(a, stream);
