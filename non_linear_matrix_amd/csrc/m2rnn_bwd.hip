@@ -90,9 +90,11 @@ struct BwdCfg {
   static constexpr int NT = 64 * NWAVES;
   // per staged step: K_s[64] (c k), Q_s[64] (q), V_s[HPW][16], F_s[HPW][4],
   // U_s[HPW][16], Kp_s[64] (c k permuted: [tile][g][r] = row 16 tile + 4 r + g),
-  // and with the gate G_s[HPW][2] (df -> da and df -> dalpha factors, in the
-  // df waves' row order, slot gate_slot(s, h))
-  static constexpr int kStep = 192 + HPW * (GATE ? 38 : 36);
+  // with the gate G_s[HPW][2] (df -> da and df -> dalpha factors, in the df
+  // waves' row order, slot gate_slot(s, h)), and for bf16 inputs the fp16
+  // rows Hu_s[HPW][16] (u) and Hv_s[HPW][16] (v) that the dq and dk
+  // contractions take as their A operand
+  static constexpr int kStep = 192 + HPW * (GATE ? 54 : 52);
   static constexpr int kBuf = kSub * kStep;
   // per wave, two slots of {H_{t-1} tile, D tile}; a tile is stored as
   // [v / 4][kk][v % 4] with a 72-float stride between the v / 4 blocks, which
@@ -103,11 +105,15 @@ struct BwdCfg {
   static constexpr int kTile = 3 * kXs + 64;
   static constexpr int kXpose = NWAVES * 4 * kTile;
   // per-lane partials of one sub-chunk, each a 256-float block per (step, head):
-  //   qk: [s][dq | dk][h] x [g][64 rows], the 4-row quads of lane group g
-  //       rotated by 4 g quads (conflict-free writes, 16-byte reads);
+  //   qk: [s][dq | dk][h] x [g][64 rows]; fp32 inputs: partials over the four
+  //       values of lane group g, the 4-row quads of group g rotated by 4 g
+  //       quads (conflict-free writes, 16-byte reads); bf16 inputs: every
+  //       group holds the whole sum (an MFMA), and the pass reads group 0;
   //   dv: [s][h] x [v'][20], the 16 (tile, g) partials of row v' at column
   //       (tile + 4 g + v') mod 16;
-  //   df: [s][h] x [tile][lane].
+  //   df: [s][h] x 256 lane partials, at the same offsets within the block
+  //       as the qk partials (the pass sums the whole block, in any order),
+  //       so that a step's dk and df partials leave in one ds_write2st64.
   static constexpr int kQK = kSub * 2 * HPW * 256;
   static constexpr int kDV = kSub * HPW * 320;
   static constexpr int kDF = kSub * HPW * 256;
@@ -184,6 +190,8 @@ struct BwdStage {
     float* U_s = F_s + kSub * HPW * 4;
     float* Kp_s = U_s + kSub * HPW * 16;
     float* G_s = Kp_s + kSub * 64;
+    _Float16* Hu_s = (_Float16*)(G_s + (GATE ? kSub * HPW * 2 : 0));   // [s][h][16] fp16
+    _Float16* Hv_s = Hu_s + kSub * HPW * 16;
     const int u = (rw - (NWAVES - NL)) * 64 + lane;
     int kind, t, e0;
     decode(u, kind, t, e0);
@@ -229,8 +237,13 @@ struct BwdStage {
     } else if (kind == 2) {
 #pragma unroll
       for (int i = 0; i < EPC; i += 4) *(f4*)(V_s + t * HPW * 16 + e0 + i) = f4{x[i], x[i + 1], x[i + 2], x[i + 3]};
+      if constexpr (sizeof(TIn) == 2)   // v exact in fp16 (normal range)
+        *(u32x4*)(Hv_s + t * HPW * 16 + e0) = __builtin_bit_cast(u32x4, (h8{(_Float16)x[0], (_Float16)x[1],
+            (_Float16)x[2], (_Float16)x[3], (_Float16)x[4], (_Float16)x[5], (_Float16)x[6], (_Float16)x[7]}));
     } else if (kind == 3) {
-      *(f4*)(U_s + t * HPW * 16 + e0) = f4{x[0], x[1], x[2], x[3]} * sig;
+      const f4 us = f4{x[0], x[1], x[2], x[3]} * sig;
+      *(f4*)(U_s + t * HPW * 16 + e0) = us;
+      if constexpr (sizeof(TIn) == 2) *(h4*)(Hu_s + t * HPW * 16 + e0) = to_half4(us);
     }
     (void)n;
     if (u < kSub * HPW) {
@@ -351,8 +364,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   extern __shared__ float smem[];
   float* xpose = smem + 2 * Cfg::kBuf;
   float* qkbuf = xpose + Cfg::kXpose;
-  float* dvbuf = qkbuf + Cfg::kQK;
-  float* dfbuf = dvbuf + Cfg::kDV;
+  float* dfbuf = qkbuf + Cfg::kQK;   // right after qkbuf: a step's dk and df share one write
+  float* dvbuf = dfbuf + Cfg::kDF;
 
   const int tid = threadIdx.x;
   // wave-uniform indices live in scalar registers
@@ -374,9 +387,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   const int L = a.ckpt_every, ns = a.nck;
   const float* Hs = a.H_ckpt + head * (size_t)ns * 1024 + kk * 16 + 4 * g;
   // this lane's slots in the partials blocks (see BwdCfg)
-  const int qk_slot = hw * 256 + g * 64 + (((4 * j + m / 4 + 4 * g) & 15) << 2) + (m & 3);
+  const int qk_slot = hw * 256 + g * 64 + (kHalf ? kk : (((4 * j + m / 4 + 4 * g) & 15) << 2) + (m & 3));
   const int dv_slot = hw * 320 + m * 20 + ((j + 4 * g + m) & 15);
-  const int df_slot = w * 64 + lane;
 
   typename ReplayOperand<TIn>::type Af;
   Af.load(live ? (const TIn*)a.W + (size_t)n * 256 : nullptr, g, m);
@@ -404,7 +416,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   // the gate parameters of the group's heads, read by the threads that stage
   // f; the df waves' dalpha, dbeta sums (slot gate_slot(s, h): row r of df
   // wave d accumulates its (step, head) pair over the sub-chunks)
-  float* gpar = dfbuf + Cfg::kDF;
+  float* gpar = dvbuf + Cfg::kDV;
   float* gacc = gpar + 2 * HPW;
   if (GATE) {
     if (tid < HPW) {
@@ -457,41 +469,54 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     const float* U_s = F_s + kSub * HPW * 4;
     const float* Kp_s = U_s + kSub * HPW * 16;     // k permuted, [s][tile][g][r] (c k in fp32, k in fp16)
     const float* G_s = Kp_s + kSub * 64;            // gate factors, [df wave][row][2]
+    const _Float16* Hu_s = (const _Float16*)(G_s + (GATE ? kSub * HPW * 2 : 0));   // fp16 rows of u, v
+    const _Float16* Hv_s = Hu_s + kSub * HPW * 16;
 
     if (live) {
       // replay the sub-chunk keeping H_{t-1} and Z_t on chip (and, for bf16
       // inputs, the fp16 rounding of H_{t-1} its contraction used)
       f4 Pp[kSub], Z[kSub];
       h4 Ph[kSub];
-#pragma unroll
+      // dq_t[kk] (this head) = sum_v H_t[kk][v] u_t[v] = (1/c) sum_v P u:
+      // fp32 inputs, per-lane partials over the lane's four v; bf16 inputs,
+      // one MFMA with u in every row of A and the fp16 state tile (the next
+      // step's operand) in B, the whole sum in every lane group
+      auto dq_half = [&](int s, h4 ph) {
+        const h4 hu = *(const h4*)(Hu_s + (s * HPW + hw) * 16 + 4 * g);
+        qkbuf[(2 * s) * HPW * 256 + qk_slot] = mfma_f16(hu, ph, f4{0.f, 0.f, 0.f, 0.f})[0];
+      };
       // Steps s >= len of a short last sub-chunk are staged as f = 1 with
       // q = k = v = u = 0: an exact identity for C and a zero contribution to
       // dq, dk, dv, dW and dw_r (df of such steps is not stored), so all kSub
       // steps run unguarded.
+#pragma unroll
       for (int s = 0; s < kSub; ++s) {
         {
           const f4 vv = *(const f4*)(V_s + (s * HPW + hw) * 16 + 4 * g);
           const f4 fc = *(const f4*)(F_s + (s * HPW + hw) * 4);
-          const f4 uu = *(const f4*)(U_s + (s * HPW + hw) * 16 + 4 * g);
           Pp[s] = P;
           f4 x;
           if constexpr (kHalf) {
             Ph[s] = to_half4(P);
             x = Af.times_half(Ph[s]);
+            if (s > 0) dq_half(s - 1, Ph[s]);
           } else {
             x = Af.times_state(P);
           }
           const f4 r = fwd_tile_finish(x, P, K_s[s * 64 + kk], vv, fc);
 #pragma unroll
           for (int i = 0; i < 4; ++i) Z[s][i] = fmaf(-2.0f, r[i], 1.0f);
-          // dq_t[kk] (this head) = sum_v H_t[kk][v] u_t[v] = (1/c) sum_v P u
-          float dq = 0.f;
+          if constexpr (!kHalf) {
+            const f4 uu = *(const f4*)(U_s + (s * HPW + hw) * 16 + 4 * g);
+            float dq = 0.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) dq = fmaf(P[i], uu[i], dq);
-          qkbuf[(2 * s) * HPW * 256 + qk_slot] = dq;
+            for (int i = 0; i < 4; ++i) dq = fmaf(P[i], uu[i], dq);
+            qkbuf[(2 * s) * HPW * 256 + qk_slot] = dq;
+          }
         }
         __builtin_amdgcn_sched_barrier(0);   // keep each step's loads in its step
       }
+      if constexpr (kHalf) dq_half(kSub - 1, to_half4(P));
       // reverse sweep over the sub-chunk.  The dW / dv contractions over the
       // tile's rows read H_{t-1} and D back from LDS in MFMA operand layout;
       // they run one step behind the sweep so that the LDS round trip
@@ -543,12 +568,11 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
 #pragma unroll
       for (int s = kSub - 1; s >= 0; --s) {
         {
-          const f4 vv = *(const f4*)(V_s + (s * HPW + hw) * 16 + 4 * g);
           const f4 fc = *(const f4*)(F_s + (s * HPW + hw) * 4);   // f, c(1-f), -2c(1-f), 1-f
           const f4 uu = *(const f4*)(U_s + (s * HPW + hw) * 16 + 4 * g);
           const float qv = Q_s[s * 64 + kk];
           f4 R, D, fR;
-          float dfp = 0.f, dk = 0.f;
+          float dfp = 0.f;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             R[i] = fmaf(qv, uu[i], C[i]);                            // R = C + q u^T
@@ -556,19 +580,28 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
             D[i] = R[i] * fmaf(-gz, Z[s][i], fc[3]);                 // (1-f) R (1 - Z^2)
             dfp = fmaf(R[i], fmaf(Pp[s][i], kInvScale, -Z[s][i]), dfp);   // <R, H_{t-1} - Z>
             fR[i] = fc[0] * R[i];
-            dk = fmaf(D[i], vv[i], dk);
           }
-          // per-lane partials of dk_t[kk] (over v' = 4g..4g+3) and df_t
-          qkbuf[(2 * s + 1) * HPW * 256 + qk_slot] = dk;
-          dfbuf[s * HPW * 256 + df_slot] = dfp;
+          // dk_t[kk] (this head) = sum_v' D[kk][v'] v_t[v'] (as dq above) and
+          // the per-lane partial of df_t, which sits at the same offset of its
+          // block
+          float* pq = qkbuf + qk_slot;
           // C_{t-1} = f R + D W^T; stage H_{t-1} and D of this step, finish
           // the previous step
           if constexpr (kHalf) {
             const h4 Dh = to_half4(D);
+            const h4 hv = *(const h4*)(Hv_s + (s * HPW + hw) * 16 + 4 * g);
             C = Ab.apply_half(Dh, fR);
+            pq[(2 * s + 1) * HPW * 256] = mfma_f16(hv, Dh, f4{0.f, 0.f, 0.f, 0.f})[0];
+            pq[Cfg::kQK + s * HPW * 256] = dfp;
             xh[(s & 1) * 128 + xw] = Ph[s];
             xh[(s & 1) * 128 + 64 + xw] = Dh;
           } else {
+            const f4 vv = *(const f4*)(V_s + (s * HPW + hw) * 16 + 4 * g);
+            float dk = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dk = fmaf(D[i], vv[i], dk);
+            pq[(2 * s + 1) * HPW * 256] = dk;
+            pq[Cfg::kQK + s * HPW * 256] = dfp;
             C = Ab.apply(D, fR);
             *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + g * Cfg::kXs + m * 4) = Pp[s];
             *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + Cfg::kTile + g * Cfg::kXs + m * 4) = D;
@@ -588,9 +621,14 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       const float* src = qkbuf + (2 * s + rw) * HPW * 256;
       f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh)
+      for (int hh = 0; hh < HPW; ++hh) {
+        if constexpr (kHalf) {
+          acc += *(const f4*)(src + hh * 256 + 4 * r4);   // lane group 0's copy of the whole sum
+        } else {
 #pragma unroll
-        for (int gg = 0; gg < 4; ++gg) acc += *(const f4*)(src + hh * 256 + gg * 64 + (((r4 + 4 * gg) & 15) << 2));
+          for (int gg = 0; gg < 4; ++gg) acc += *(const f4*)(src + hh * 256 + gg * 64 + (((r4 + 4 * gg) & 15) << 2));
+        }
+      }
       acc *= rw == 0 ? kInvScale * isig : isig;
       float* dst = a.ws_dqk + (((size_t)b * ngroups + grp) * a.T + t0) * 128;   // uniform
       if (s < len) *(f4*)(dst + (unsigned)(s * 128 + rw * 64 + 4 * r4)) = acc;
