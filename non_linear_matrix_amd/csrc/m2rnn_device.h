@@ -20,7 +20,6 @@ namespace m2rnn {
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -86,37 +85,37 @@ __device__ __forceinline__ GateVal gate_value(float a, float alpha, float beta) 
   return g;
 }
 
-// ------------------------------------------------------- bf16 hi/lo splitting
-// x = hi + lo + O(2^-17 |x|) with hi = bf16(x), lo = bf16(x - hi), both
-// round-to-nearest-even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
-  bf16x2 h = __builtin_convertvector((f2{x0, x1}), bf16x2);
-  hi = __builtin_bit_cast(uint32_t, h);
-  float l0 = x0 - __uint_as_float(hi << 16);
-  float l1 = x1 - __uint_as_float(hi & 0xffff0000u);
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{l0, l1}), bf16x2));
+// ------------------------------------------------------- fp16 hi/lo splitting
+// x = hi + lo with hi = fp16(x) and lo = fp16(x - hi), both round-to-nearest-
+// even (v_cvt_pk_f16_f32).  x - hi is exact in fp32 and comes from one
+// v_fma_mix_f32 that reads hi as the fp16 half of the packed register it
+// already sits in.  For |x| <= c (every state element) the pair carries x to
+// within 2^-22 |x| + 2^-25 (fp16 subnormals are kept), which is finer than a
+// bf16 pair (2^-17 |x|) at the same cost in MFMA work and 4 fewer VALU
+// instructions per four elements.
+__device__ __forceinline__ float minus_half_lo(uint32_t hpk, float x) {   // x - (float)(low fp16 of hpk)
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hpk), "v"(x));
+  return r;
+}
+__device__ __forceinline__ float minus_half_hi(uint32_t hpk, float x) {   // x - (float)(high fp16 of hpk)
+  float r;
+  asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hpk), "v"(x));
+  return r;
+}
+__device__ __forceinline__ void split2h(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{x0, x1}), h2));
+  const float l0 = minus_half_lo(hi, x0), l1 = minus_half_hi(hi, x1);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{l0, l1}), h2));
 }
 
-// B operand of v_mfma_f32_16x16x32_bf16 from an accumulator tile: k-slots
+// B operand of v_mfma_f32_16x16x32_f16 from an accumulator tile: k-slots
 // 0..3 of lane group g carry hi(x[0..3]), slots 4..7 carry lo(x[0..3]).
-__device__ __forceinline__ bf16x8 split_operand(f4 x) {
+__device__ __forceinline__ h8 split_operand(f4 x) {
   uint32_t h01, l01, h23, l23;
-  split2(x[0], x[1], h01, l01);
-  split2(x[2], x[3], h23, l23);
-  return __builtin_bit_cast(bf16x8, (u32x4{h01, h23, l01, l23}));
-}
-
-__device__ __forceinline__ f4 mfma_bf16(bf16x8 a, bf16x8 b, f4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// Pack eight floats (already representable, or rounded RNE) into a bf16x8.
-__device__ __forceinline__ bf16x8 pack8(const float* w) {
-  u32x4 u;
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-    u[s] = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2{w[2 * s], w[2 * s + 1]}), bf16x2));
-  return __builtin_bit_cast(bf16x8, u);
+  split2h(x[0], x[1], h01, l01);
+  split2h(x[2], x[3], h23, l23);
+  return __builtin_bit_cast(h8, (u32x4{h01, h23, l01, l23}));
 }
 
 // ------------------------------------------- the per-step contraction W^T P
@@ -125,20 +124,21 @@ __device__ __forceinline__ bf16x8 pack8(const float* w) {
 // sum_v W[v][v'] P^T[v][m], i.e. the transposed tile of P W.
 template <typename TIn> struct WOperand;
 
-// bfloat16 inputs: W is exact in bf16; the fp32 state is split hi + lo and
-// both halves ride in one v_mfma_f32_16x16x32_bf16 (A = [W^T | W^T]).
+// bfloat16 inputs: W is exact in fp16 (for 2^-14 <= |W| <= 65504; smaller
+// values round to within 2^-25); the fp32 state is split hi + lo and both
+// halves ride in one v_mfma_f32_16x16x32_f16 (A = [W^T | W^T]).
 template <> struct WOperand<bf16_t> {
-  bf16x8 a;
+  h8 a;
   __device__ void load(const bf16_t* Wn, int g, int m) {
-    float w[8];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      float x = Wn ? to_f32(Wn[(4 * g + s) * 16 + m]) : 0.0f;
-      w[s] = w[s + 4] = x;
+      const _Float16 x = (_Float16)(Wn ? to_f32(Wn[(4 * g + s) * 16 + m]) : 0.0f);
+      a[s] = a[s + 4] = x;
     }
-    a = pack8(w);
   }
-  __device__ f4 times_state(f4 p) const { return mfma_bf16(a, split_operand(p), f4{0.f, 0.f, 0.f, 0.f}); }
+  __device__ f4 times_state(f4 p) const {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, split_operand(p), f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  }
 };
 
 // float32 inputs: four exact v_mfma_f32_16x16x4_f32; accumulator register r

@@ -12,8 +12,8 @@
 //
 //  * a (b, n) head's 64 x 16 state sits in four MFMA accumulators (see
 //    m2rnn_device.h), held by one, two or four waves for the whole sequence;
-//  * H_{t-1} W is one v_mfma_f32_16x16x32_bf16 per row tile: W^T in the A
-//    operand (resident), hi/lo bf16 split of the fp32 state in the B operand
+//  * H_{t-1} W is one v_mfma_f32_16x16x32_f16 per row tile: W^T in the A
+//    operand (resident), hi/lo fp16 split of the fp32 state in the B operand
 //    (fp32 inputs: four exact v_mfma_f32_16x16x4_f32);
 //  * k v^T, tanh, the gate and the readout products are fused per lane;
 //    the readout sum over the 64 rows is an in-register sum over the four
