@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
 
   for (int sb = ns - 1, it = 0; sb >= 0; --sb, ++it) {
     const int t0 = sb * L, len = min(L, a.T - t0);
-    f4 P = Hnext * kScale;
+    f4 P = Hnext * a.ck_scale;
     // prefetch the next sub-chunk (registers live for this iteration only).
     // The last iteration fetches sub-chunk 0 again and stages it into the
     // buffer no one reads: no branch, so nothing in flight gets copied.
@@ -880,6 +880,7 @@ hipError_t launch_backward(const BwdArgs& a0, const FwdArgs& replay, int dtype, 
     hipError_t e = launch_densify(replay, dtype, stream);
     if (e != hipSuccess) return e;
     a.H_ckpt = replay.H_ckpt;
+    a.ck_scale = 1.0f;   // the replay stores c H
     a.ckpt_every = kSub;
     a.nck = (a.T + kSub - 1) / kSub;
   }

@@ -244,7 +244,8 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
           next_ck += a.ckpt_every;
           ++ck_idx;
 #pragma unroll
-          for (int j = 0; j < TPW; ++j) *(f4*)(dst + (16 * (j0 + j) + m) * 16 + 4 * g) = P[j] * kInvScale;
+          for (int j = 0; j < TPW; ++j)   // the replay's states stay scaled by c (only the sweep reads them)
+            *(f4*)(dst + (16 * (j0 + j) + m) * 16 + 4 * g) = DENSE ? P[j] : P[j] * kInvScale;
         }
         const TileVals<TPW> kq = load_tiles<TPW>(K_s + tt * 64 + m * 4 + j0);   // c k[16j+m]
         const TileVals<TPW> qq = load_tiles<TPW>(Q_s + tt * 64 + m * 4 + j0);   // q[16j+m] / c

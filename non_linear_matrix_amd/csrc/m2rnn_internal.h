@@ -36,6 +36,7 @@ struct BwdArgs {
   float *ws_dqk, *ws_dW, *ws_dwr;   // workspace regions
   float* ws_dgate = nullptr;        // [B][N][2] per-row dalpha, dbeta partials
   float* ws_amax = nullptr;         // partial maxima of |dy|, |dH_T| (bf16 inputs)
+  float ck_scale = 2.8853900817779268f;   // H_ckpt holds H (c = 2 / ln 2) or, from the replay, c H (1)
   int B, T, N;
   int ckpt_every, nck, ngroups;
 };
