@@ -108,7 +108,8 @@ struct BwdCfg {
   //   qk: [s][dq | dk][h] x [g][64 rows]; fp32 inputs: partials over the four
   //       values of lane group g, the 4-row quads of group g rotated by 4 g
   //       quads (conflict-free writes, 16-byte reads); bf16 inputs: every
-  //       group holds the whole sum (an MFMA), and the pass reads group 0;
+  //       group holds the whole sum (an MFMA), groups 1 and 3 rotated by 16
+  //       rows, and the pass reads group 0;
   //   dv: [s][h] x [v'][20], the 16 (tile, g) partials of row v' at column
   //       (tile + 4 g + v') mod 16;
   //   df: [s][h] x 256 lane partials, at the same offsets within the block
@@ -387,7 +388,11 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   const int L = a.ckpt_every, ns = a.nck;
   const float* Hs = a.H_ckpt + head * (size_t)ns * 1024 + kk * 16 + 4 * g;
   // this lane's slots in the partials blocks (see BwdCfg)
-  const int qk_slot = hw * 256 + g * 64 + (kHalf ? kk : (((4 * j + m / 4 + 4 * g) & 15) << 2) + (m & 3));
+  // (bf16 inputs: lane group g writes its copy rotated by 16 (g & 1) rows, so
+  // the two groups that share a write cycle hit different banks; the pass
+  // reads group 0's copy, which is not rotated)
+  const int qk_slot = hw * 256 + g * 64 +
+                      (kHalf ? ((kk + 16 * (g & 1)) & 63) : (((4 * j + m / 4 + 4 * g) & 15) << 2) + (m & 3));
   const int dv_slot = hw * 320 + m * 20 + ((j + 4 * g + m) & 15);
 
   typename ReplayOperand<TIn>::type Af;
