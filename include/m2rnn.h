@@ -40,6 +40,13 @@
  *     (zero when dH_T is NULL).  This build supports K == 64 and
  *     V == 16 only (other values return M2RNN_ERR_UNSUPPORTED).
  *   - f is used as given (not clamped); the method expects f in [0, 1].
+ *   - Precision with bf16 inputs: the forward keeps the fp32 state to an
+ *     fp16 hi/lo pair (2^-22 relative) in its H W contraction, and the
+ *     backward's reverse sweep rounds its factors once to fp16 (see
+ *     m2rnn_backward), so W must lie within fp16's range, |W| <= 65504
+ *     (entries below 2^-14 in magnitude round to within 2^-25; entries
+ *     beyond the range make the results non-finite).  fp32 inputs use exact
+ *     fp32 products throughout.
  *   - Errors are reported before anything is launched: a negative status is
  *     returned and m2rnn_last_error() describes it.  A failed kernel launch
  *     returns M2RNN_ERR_HIP.
@@ -130,7 +137,13 @@ size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckp
  *                        C), or NULL when not wanted
  *   workspace            device buffer of at least
  *                        m2rnn_backward_workspace_bytes(...) bytes,
- *                        16-byte aligned; contents on entry are ignored
+ *                        256-byte aligned; contents on entry are ignored
+ * With bf16 inputs the reverse sweep rounds its factors once to fp16 and
+ * first scales dy and dH_T by the power of two that puts their largest
+ * magnitude in [1/4, 1/2), scaling every output back exactly: the results
+ * do not depend on the scale of the caller's gradients (dy, dH_T times 2^k
+ * give every output times 2^k, bit for bit).  NaNs in dy are left out of
+ * that scale and reach the outputs as usual.
  */
 int m2rnn_backward(int B, int T, int N, int K, int V, int dtype,
                    const void* q, const void* k, const void* v, const void* f,

@@ -201,3 +201,15 @@ def test_backward_full_size_sampled(chains):
             scale = max(1.0, float(np.max(np.abs(ref))))
             print(f"chain ({b},{n}) {name}: max err {err:.3e} (scale {scale:.2f})")
             assert err <= 5e-3 * scale
+
+
+def test_backward_bf16_weight_range():
+    """bf16 inputs with W of order 1e-5 and entries down to 5e-7, below
+    fp16's normal range, where the fp16 operands round: every gradient still
+    meets the bf16 bar against the oracle."""
+    B, T, N, ck = 2, 70, 5, 16
+    x = make(B, T, N, "bf16", seed=41, with_dy=True)
+    W = x["W"].float() * 1e-5
+    W[0, 0, :4] = torch.tensor([1e-6, -3e-6, 5e-7, 2e-5])   # below 2^-14
+    x["W"] = W.to(torch.bfloat16)
+    check(gpu_grads(x, ck), ref_grads(x), TOL["bf16"], "bf16 small W")

@@ -47,6 +47,23 @@ def test_forward_parity_launch_shapes(dtype, B, T, N):
     assert ey <= TOL[dtype] and eh <= TOL[dtype]
 
 
+def test_forward_bf16_weight_range():
+    """bf16 W of order 1e-5 with entries down to 5e-7, below fp16's normal
+    range, where the fp16 A operand rounds to within 2^-25: y and H_T still
+    meet the bf16 bar.  (Large W is no test of precision: the saturated
+    recurrence then amplifies any rounding difference, the oracle's own
+    included.)"""
+    x = make(2, 100, 5, "bf16", seed=43)
+    W = x["W"].float() * 1e-5
+    W[0, 0, :4] = torch.tensor([1e-6, -3e-6, 5e-7, 2e-5])   # below 2^-14
+    x["W"] = W.to(torch.bfloat16)
+    y, HT = run(x)
+    yr, HTr = oracle_forward(x)
+    ey, eh = max_abs(y, yr), max_abs(HT, HTr)
+    print(f"bf16 small W: max|dy|={ey:.3e} max|dH_T|={eh:.3e}")
+    assert ey <= TOL["bf16"] and eh <= TOL["bf16"]
+
+
 def test_forward_config_fp32_B1_T256_N4():
     """The float32 workload B=1, T=256, N=4 (seed 0), element by element."""
     w = m2rnn_inputs.WORKLOADS["fwd_f32_B1_T256_N4"]
