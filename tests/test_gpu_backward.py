@@ -213,3 +213,21 @@ def test_backward_bf16_weight_range():
     W[0, 0, :4] = torch.tensor([1e-6, -3e-6, 5e-7, 2e-5])   # below 2^-14
     x["W"] = W.to(torch.bfloat16)
     check(gpu_grads(x, ck), ref_grads(x), TOL["bf16"], "bf16 small W")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_zero_dy(dtype):
+    """dy = 0: with no dH_T every gradient is exactly zero (the gradient scale
+    of an all-zero input is 1, not a division by zero); with a dH_T alone the
+    scale follows dH_T and the gradients match the oracle."""
+    B, T, N, ck = 2, 70, 5, 16
+    x = make(B, T, N, dtype, seed=47, with_dy=True)
+    x["dy"] = torch.zeros_like(x["dy"])
+    g = to_gpu(x)
+    _, _, Hck = m2.forward(g["q"], g["k"], g["v"], g["f"], g["W"], g["wr"], ckpt_every=ck)
+    out = m2.backward(g["q"], g["k"], g["v"], g["f"], g["W"], g["wr"], Hck, ck, g["dy"], want_dH_0=True)
+    torch.cuda.synchronize()
+    for name, t in out.items():
+        assert bool((t == 0).all()), name
+    dHT = torch.randn(B, N, 64, 16, generator=torch.Generator().manual_seed(5)) * 1e-3
+    check(gpu_grads(x, ck, dHT), ref_grads(x, dHT), TOL[dtype], f"{dtype} dy = 0 with dH_T")
