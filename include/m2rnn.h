@@ -39,6 +39,11 @@
  *     y empty and sets H_T = H_0 (zero when H_0 is NULL) and dH_0 = dH_T
  *     (zero when dH_T is NULL).  This build supports K == 64 and
  *     V == 16 only (other values return M2RNN_ERR_UNSUPPORTED).
+ *   - Size limits (beyond them M2RNN_ERR_UNSUPPORTED; each keeps a kernel
+ *     launch under 2^32 work-items): B T N V <= 2^40; B ceil(N/4) < 2^22,
+ *     about 16.7 M (b, n) chains or 64 GiB of state; and in the backward,
+ *     when ckpt_every > 4, B ceil(N/4) ceil(T/ckpt_every) < 2^24.  The
+ *     workspace query returns 0 beyond the first two.
  *   - f is used as given (not clamped); the method expects f in [0, 1].
  *   - Precision with bf16 inputs: the forward keeps the fp32 state to an
  *     fp16 hi/lo pair (2^-22 relative) in its H W contraction, and the

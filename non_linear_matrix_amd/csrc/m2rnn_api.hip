@@ -27,13 +27,19 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // Largest element count any single tensor may have (64-bit indexing is used in
 // the kernels; this only keeps products of int sizes from overflowing).
 constexpr long long kMaxElems = 1LL << 40;
+// A launch holds fewer than 2^32 work-items.  The backward's workgroups of four
+// heads have 1024 threads, the replay's 256 per checkpoint interval: these
+// bound the groups of four heads, and the backward's groups times intervals.
+constexpr long long kMaxHeadGroups = (1LL << 22) - 1;
+constexpr long long kMaxReplayGroups = (1LL << 24) - 1;
 
 int check_sizes(int B, int T, int N, int K, int V, int dtype) {
   if (B < 0 || T < 0 || N < 0) return fail(M2RNN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d T=%d N=%d)", B, T, N);
   if (K != 64 || V != 16) return fail(M2RNN_ERR_UNSUPPORTED, "this build supports K=64, V=16 only (got K=%d V=%d)", K, V);
   if (dtype != M2RNN_F32 && dtype != M2RNN_BF16) return fail(M2RNN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if ((long long)B * T * N * V > kMaxElems) return fail(M2RNN_ERR_UNSUPPORTED, "problem too large");
-  if ((long long)B * ((N + 3) / 4) > 0x7fffffffLL) return fail(M2RNN_ERR_UNSUPPORTED, "too many (batch, head) groups");
+  if ((long long)B * ((N + 3) / 4) > kMaxHeadGroups)
+    return fail(M2RNN_ERR_UNSUPPORTED, "B * ceil(N / 4) must be below 2^22 (B=%d N=%d)", B, N);
   return M2RNN_OK;
 }
 
@@ -109,6 +115,7 @@ extern "C" int m2rnn_forward_gated(int B, int T, int N, int K, int V, int dtype,
 
 extern "C" size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckpt_every) {
   if (B <= 0 || T <= 0 || N <= 0 || K != 64 || V != 16 || ckpt_every < 1) return 0;
+  if ((long long)B * T * N * V > kMaxElems || (long long)B * ((N + 3) / 4) > kMaxHeadGroups) return 0;
   size_t o1, o2, o3, o4, o5, o6;
   int ng;
   return sizeof(float) * m2rnn::backward_workspace_floats(B, T, N, ckpt_every, &o1, &o2, &o3, &o4, &o5, &o6, &ng);
@@ -125,6 +132,9 @@ static int backward_impl(bool gated, int B, int T, int N, int K, int V, int dtyp
   int st = check_sizes(B, T, N, K, V, dtype);
   if (st) return st;
   if (ckpt_every < 1) return fail(M2RNN_ERR_INVALID_ARG, "ckpt_every must be >= 1 for the backward");
+  if (ckpt_every > m2rnn::backward_sub_steps() &&
+      (long long)B * ((N + 3) / 4) * ((T + (long long)ckpt_every - 1) / ckpt_every) > kMaxReplayGroups)
+    return fail(M2RNN_ERR_UNSUPPORTED, "B * ceil(N / 4) * ceil(T / ckpt_every) must be below 2^24");
   const size_t es = dtype == M2RNN_F32 ? 4 : 2;
   const long long BT = (long long)B * T, BTN = BT * N, BN = (long long)B * N;
   const int nck = T > 0 ? (T + ckpt_every - 1) / ckpt_every : 0;

@@ -77,6 +77,38 @@ def test_argument_errors_without_launch(m2):
     assert b(1, 4, 2, 64, 16, 0, *args6, dummy, 64, dummy, None, *grads, None, None, 0, None) == m2.M2RNN_ERR_WORKSPACE
 
 
+def test_size_limits_without_launch(m2):
+    """Sizes whose launches would not fit 2^32 work-items are refused before
+    anything runs; the largest accepted sizes pass validation (they then fail
+    on the missing workspace, not on size)."""
+    dummy = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    args6 = [dummy] * 6
+    f = m2.lib.m2rnn_forward
+    # B ceil(N/4) < 2^22
+    assert f(1 << 20, 1, 16, 64, 16, 0, *args6, None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert "2^22" in m2.m2rnn_last_error()
+    assert f((1 << 20) - 1, 1, 16, 64, 16, 1, *args6, None, None, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert "y must" in m2.m2rnn_last_error()
+    # B T N V <= 2^40
+    assert f(1 << 10, 1 << 20, 128, 64, 16, 0, *args6, None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert "too large" in m2.m2rnn_last_error()
+    d = m2.lib.m2rnn_decode
+    assert d(1 << 22, 4, 64, 16, 0, *args6, dummy, dummy, None) == m2.M2RNN_ERR_UNSUPPORTED
+    # the backward's replay: B ceil(N/4) ceil(T/ckpt_every) < 2^24 once ckpt_every > 4
+    b = m2.lib.m2rnn_backward
+    grads = [dummy] * 6
+    assert b(1 << 10, 1 << 20, 4, 64, 16, 0, *args6, dummy, 64, dummy, None, *grads, None, dummy, 16, None) == \
+        m2.M2RNN_ERR_UNSUPPORTED
+    assert "2^24" in m2.m2rnn_last_error()
+    assert b(1 << 10, (1 << 20) - 64, 4, 64, 16, 0, *args6, dummy, 64, dummy, None, *grads, None, dummy, 16,
+             None) == m2.M2RNN_ERR_WORKSPACE
+    assert b(1 << 10, 1 << 20, 4, 64, 16, 0, *args6, dummy, 4, dummy, None, *grads, None, dummy, 16, None) == \
+        m2.M2RNN_ERR_WORKSPACE   # states every 4 steps are given: no replay
+    ws = m2.m2rnn_backward_workspace_bytes
+    assert ws(1 << 20, 1, 16, 64, 16, 64) == 0 and ws((1 << 20) - 1, 1, 16, 64, 16, 64) > 0
+    assert ws(1 << 10, 1 << 20, 128, 64, 16, 64) == 0
+
+
 def test_gated_argument_errors_without_launch(m2):
     dummy = ctypes.c_void_p(256)   # never dereferenced: validation fails first
     q3 = [dummy] * 3
