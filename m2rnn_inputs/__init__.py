@@ -111,6 +111,30 @@ def make_inputs(B, T, N, K=K_DIM, V=V_DIM, dtype="f32", f_mu=2.0, seed=0, with_d
     return out
 
 
+def make_inputs_on(device, B, T, N, K=K_DIM, V=V_DIM, dtype="f32", f_mu=2.0, seed=0, with_dy=False):
+    """make_inputs drawn on `device` from a generator of that device: the same
+    distributions and draw order (on the CPU the same numbers; a GPU's
+    generator gives another stream).  For sizes too large to draw on the host
+    (tensors of billions of elements)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    td = torch_dtype(dtype)
+
+    def draw(*shape):
+        return torch.randn(*shape, generator=g, dtype=torch.float32, device=device)
+
+    out = {}
+    out["q"] = torch.nn.functional.silu(draw(B, T, K)).to(td)
+    out["k"] = torch.nn.functional.silu(draw(B, T, K)).to(td)
+    out["v"] = torch.nn.functional.silu(draw(B, T, N, V)).to(td)
+    out["f"] = torch.sigmoid(draw(B, T, N) + f_mu).to(td)
+    out["W"] = (draw(N, V, V) * 0.25).to(td)
+    out["wr"] = draw(N, V).to(td)
+    if with_dy:
+        out["dy"] = draw(B, T, N, V)
+    return {n: t.contiguous() for n, t in out.items()}
+
+
 def make_workload(w: Workload, seed=0, with_dy=None):
     return make_inputs(w.B, w.T, w.N, w.K, w.V, w.dtype, w.f_mu, seed,
                        w.backward if with_dy is None else with_dy)
