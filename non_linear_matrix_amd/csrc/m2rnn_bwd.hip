@@ -624,15 +624,19 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       // and four lane groups -> workspace [b][grp][t][dq | dk][64]
       const int s = lane / 16, r4 = lane % 16;
       const float* src = qkbuf + (2 * s + rw) * HPW * 256;
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      // bf16: lane group 0's copy of the whole sum per head; fp32: four
+      // lane-group partials per head.  The sum starts from the first term.
+      constexpr int kParts = kHalf ? 1 : 4;
+      auto part = [&](int hh, int gg) {
+        return kHalf ? *(const f4*)(src + hh * 256 + 4 * r4)
+                     : *(const f4*)(src + hh * 256 + gg * 64 + (((r4 + 4 * gg) & 15) << 2));
+      };
+      f4 acc = part(0, 0);
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
-        if constexpr (kHalf) {
-          acc += *(const f4*)(src + hh * 256 + 4 * r4);   // lane group 0's copy of the whole sum
-        } else {
 #pragma unroll
-          for (int gg = 0; gg < 4; ++gg) acc += *(const f4*)(src + hh * 256 + gg * 64 + (((r4 + 4 * gg) & 15) << 2));
-        }
+        for (int gg = 0; gg < kParts; ++gg)
+          if (hh + gg > 0) acc += part(hh, gg);
       }
       acc *= rw == 0 ? kInvScale * isig : isig;
       float* dst = a.ws_dqk + (((size_t)b * ngroups + grp) * a.T + t0) * 128;   // uniform
@@ -839,13 +843,11 @@ template <typename TIn, int HPW, bool GATE>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   typedef BwdCfg<HPW, GATE> Cfg;
   static_assert(Cfg::kBytes <= 160 * 1024, "backward LDS budget");
-  static bool attr_set = false;   // per process; the attribute is per kernel
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)m2rnn_bwd_kernel<TIn, HPW, GATE>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // once per process and kernel (a function-local static is initialised once,
+  // also when several host threads launch at the same time)
+  static const hipError_t attr = hipFuncSetAttribute((const void*)m2rnn_bwd_kernel<TIn, HPW, GATE>,
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kBytes);
+  if (attr != hipSuccess) return attr;
   dim3 grid((unsigned)(a.B * a.ngroups)), block(Cfg::NT);
   hipLaunchKernelGGL((m2rnn_bwd_kernel<TIn, HPW, GATE>), grid, block, Cfg::kBytes, stream, a);
   hipError_t e = hipGetLastError();
