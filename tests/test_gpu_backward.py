@@ -203,6 +203,23 @@ def test_backward_full_size_sampled(chains):
             assert err <= 5e-3 * scale
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_backward_f_zero(dtype):
+    """f = 0, the plain tanh recurrence with no direct path through time:
+    C_{t-1} = D_t W^T carries every gradient back, and df = <R, H_{t-1} - Z>
+    still flows.  Against the oracle, four heads per workgroup and checkpoint
+    intervals past the 4-step replay window.  W is halved (standard deviation
+    1/8): with f = 0 and the full-scale W some chains expand gradients
+    backward in time, and there a half-ulp fp32 change of the inputs already
+    moves the exact gradients by 1e-4 of their maximum, so no fp32 computation
+    meets the bar; with W halved that sensitivity is 1e-7."""
+    B, T, N, ck = 2, 90, 520, 16
+    x = make(B, T, N, dtype, seed=57, with_dy=True)
+    x["f"] = torch.zeros_like(x["f"])
+    x["W"] = (x["W"].float() * 0.5).to(x["W"].dtype)
+    check(gpu_grads(x, ck), ref_grads(x), TOL[dtype], f"{dtype} f = 0")
+
+
 def test_backward_bf16_weight_range():
     """bf16 inputs with W of order 1e-5 and entries down to 5e-7, below
     fp16's normal range, where the fp16 operands round: every gradient still

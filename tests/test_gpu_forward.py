@@ -132,6 +132,27 @@ def test_forward_rnn_embedding():
         assert max_abs(y[:, :, n], h.numpy()) <= 1e-4
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_forward_zero_w_zero_f_closed_form(dtype):
+    """W = 0 and f = 0: every step forgets the past, so H_t = tanh(k_t v_t^T)
+    elementwise and y_t = H_t^T q_t + w_r v_t, written out in float64 from the
+    same (bf16-rounded) inputs; on the launch shape of four heads per
+    workgroup with a ragged chunk."""
+    B, T, N = 4, 77, 300
+    x = make(B, T, N, dtype, seed=23)
+    x["W"] = torch.zeros_like(x["W"])
+    x["f"] = torch.zeros_like(x["f"])
+    y, HT, ck = run(x, ckpt_every=16)
+    q, k, v, wr = (x[n].double() for n in ("q", "k", "v", "wr"))
+    H = torch.tanh(k[:, :, None, :, None] * v[:, :, :, None, :])        # [B,T,N,K,V]
+    y_ref = torch.einsum("btnkv,btk->btnv", H, q) + wr * v
+    tol = TOL[dtype]
+    assert max_abs(y, y_ref.numpy()) <= tol
+    assert max_abs(HT, H[:, -1].numpy()) <= tol
+    assert max_abs(ck[:, :, 1:], H[:, 15:T - 1:16].permute(0, 2, 1, 3, 4).numpy()) <= tol
+    assert np.all(ck[:, :, 0] == 0.0)
+
+
 def test_forward_deterministic():
     x = make(2, 200, 8, "bf16", seed=2)
     a = run(x)
