@@ -186,3 +186,48 @@ def test_conv_silu_argument_errors_without_launch(m2):
     assert "du" in m2.m2rnn_last_error()
     assert bwd(2, 3, 8, 0, dummy, dummy, None, dummy, dummy, dummy, ctypes.c_void_p(260), dummy, 1 << 20, None) == \
         m2.M2RNN_ERR_INVALID_ARG
+
+
+def test_size_validation_property(m2):
+    """Random and extreme sizes: the backward's validation gives the status
+    that follows from the documented rules, computed here in Python integers
+    (no overflow), and never reaches a launch.  The workspace offered is
+    always 16 bytes, so every size that passes validation stops at
+    M2RNN_ERR_WORKSPACE (or succeeds without a launch when there are no
+    steps to run, which needs an empty tensor)."""
+    from hypothesis import given, settings, strategies as st
+
+    dummy = ctypes.c_void_p(256)   # never dereferenced: validation fails first
+    args6 = [dummy] * 6
+    grads = [dummy] * 6
+    big = st.one_of(st.integers(-2, 70), st.integers(0, 2 ** 31 - 1), st.sampled_from([2 ** 20, 2 ** 22, 2 ** 24]))
+
+    def expected(B, T, N, K, V, dtype, ck):
+        if B < 0 or T < 0 or N < 0:
+            return m2.M2RNN_ERR_INVALID_ARG
+        if K != 64 or V != 16:
+            return m2.M2RNN_ERR_UNSUPPORTED
+        if dtype not in (0, 1):
+            return m2.M2RNN_ERR_INVALID_ARG
+        if B * T * N * V > 2 ** 40 or B * ((N + 3) // 4) > 2 ** 22 - 1:
+            return m2.M2RNN_ERR_UNSUPPORTED
+        if ck < 1:
+            return m2.M2RNN_ERR_INVALID_ARG
+        if ck > 4 and B * ((N + 3) // 4) * ((T + ck - 1) // ck) > 2 ** 24 - 1:
+            return m2.M2RNN_ERR_UNSUPPORTED
+        if B * T * N == 0:
+            return None   # the empty-tensor path: zero fills only, not reached here
+        return m2.M2RNN_ERR_WORKSPACE
+
+    @settings(max_examples=400, deadline=None)
+    @given(B=big, T=big, N=big, K=st.sampled_from([64, 64, 32]), V=st.sampled_from([16, 16, 8]),
+           dtype=st.sampled_from([0, 1, 2]), ck=st.one_of(st.integers(-1, 80), st.sampled_from([2 ** 30])))
+    def check(B, T, N, K, V, dtype, ck):
+        want = expected(B, T, N, K, V, dtype, ck)
+        if want is None:
+            return
+        got = m2.lib.m2rnn_backward(B, T, N, K, V, dtype, *args6, dummy, ck, dummy, None, *grads, None, dummy, 16,
+                                    None)
+        assert got == want, (B, T, N, K, V, dtype, ck, got, want, m2.m2rnn_last_error())
+
+    check()
