@@ -236,9 +236,7 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
     const float* F_s = V_s + TC * HPW * 16;
     const int steps = min(TC, te - t0);
     if (live) {
-      for (int tt = 0; tt < steps; ++tt) {
-        if (!DENSE && tt == 0) st.load(a, b, n0, tn, te, tid);
-        const int t = t0 + tt;
+      auto ckpt = [&](int t) {
         if (t == next_ck) {
           float* dst = a.H_ckpt + (((size_t)b * a.N + n) * a.nck + ck_idx) * 1024;
           next_ck += a.ckpt_every;
@@ -247,6 +245,8 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
           for (int j = 0; j < TPW; ++j)   // the replay's states stay scaled by c (only the sweep reads them)
             *(f4*)(dst + (16 * (j0 + j) + m) * 16 + 4 * g) = DENSE ? P[j] : P[j] * kInvScale;
         }
+      };
+      auto step = [&](int tt) {
         const TileVals<TPW> kq = load_tiles<TPW>(K_s + tt * 64 + m * 4 + j0);   // c k[16j+m]
         const TileVals<TPW> qq = load_tiles<TPW>(Q_s + tt * 64 + m * 4 + j0);   // q[16j+m] / c
         const f4 vv = *(const f4*)(V_s + (tt * HPW + hw) * 16 + 4 * g);
@@ -285,6 +285,25 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
           // stores it (the four lanes of each c write the same value)
           const float ys = row_sum16x4(p, m);
           ystage[((tt * HPW + hw) * WPH + ts) * 16 + 4 * g + ((m & 1) << 1) + ((m >> 1) & 1)] = ys;
+        }
+      };
+      // In the forward, a whole chunk whose checkpoints (if any) all fall on
+      // every fourth step runs four steps per iteration: the checkpoint test
+      // and the loop control once per four steps, the LDS offsets folded into
+      // the reads.  (The replay, which stores every fourth state, measured
+      // slightly slower this way and keeps the step loop.)
+      if (!DENSE && steps == TC && (!a.H_ckpt || ((a.ckpt_every & 3) == 0 && ((next_ck - t0) & 3) == 0))) {
+        for (int tt0 = 0; tt0 < TC; tt0 += 4) {
+          if (!DENSE && tt0 == 0) st.load(a, b, n0, tn, te, tid);
+          ckpt(t0 + tt0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) step(tt0 + u);
+        }
+      } else {
+        for (int tt = 0; tt < steps; ++tt) {
+          if (!DENSE && tt == 0) st.load(a, b, n0, tn, te, tid);
+          ckpt(t0 + tt);
+          step(tt);
         }
       }
     }
