@@ -203,21 +203,69 @@ def test_backward_full_size_sampled(chains):
             assert err <= 5e-3 * scale
 
 
+def low_f_inputs(dtype, N, fval, w_scale=1.0):
+    """B=2, T=90 with a constant forget gate: f = 0 is the plain tanh
+    recurrence with no direct path through time (C_{t-1} = D_t W^T carries
+    every gradient back), f = 0.3 a weak one; the slides allow f anywhere in
+    [0, 1] (slide "The gate preserves a direct path through time", paper
+    Eqs. (13), (17))."""
+    x = make(2, 90, N, dtype, seed=57, with_dy=True)
+    x["f"] = torch.full_like(x["f"], fval)
+    if w_scale != 1.0:
+        x["W"] = (x["W"].float() * w_scale).to(x["W"].dtype)
+    return x
+
+
+@pytest.mark.parametrize("fval", [0.0, 0.3])
+def test_backward_low_f_full_w_bf16(fval):
+    """bf16 inputs, f = 0 and f = 0.3, W at its full scale (standard deviation
+    1/4): N=520 gives 1040 chains, so the sweep runs four heads per workgroup,
+    with checkpoint intervals past the 4-step replay window.  Every gradient
+    element against the oracle at the bf16 bar."""
+    x = low_f_inputs("bf16", 520, fval)
+    check(gpu_grads(x, 16), ref_grads(x), TOL["bf16"], f"bf16 f = {fval} full W (B=2 T=90 N=520)")
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_f_zero(dtype):
-    """f = 0, the plain tanh recurrence with no direct path through time:
-    C_{t-1} = D_t W^T carries every gradient back, and df = <R, H_{t-1} - Z>
-    still flows.  Against the oracle, four heads per workgroup and checkpoint
-    intervals past the 4-step replay window.  W is halved (standard deviation
-    1/8): with f = 0 and the full-scale W some chains expand gradients
-    backward in time, and there a half-ulp fp32 change of the inputs already
-    moves the exact gradients by 1e-4 of their maximum, so no fp32 computation
-    meets the bar; with W halved that sensitivity is 1e-7."""
-    B, T, N, ck = 2, 90, 520, 16
-    x = make(B, T, N, dtype, seed=57, with_dy=True)
-    x["f"] = torch.zeros_like(x["f"])
-    x["W"] = (x["W"].float() * 0.5).to(x["W"].dtype)
-    check(gpu_grads(x, ck), ref_grads(x), TOL[dtype], f"{dtype} f = 0")
+def test_backward_from_exact_checkpoints_ill_conditioned(dtype):
+    """The draw with N=300, f = 0 and the full-scale W is ill-conditioned:
+    moving q, k, v, W by half an fp32 ulp moves the exact gradients by 1e-3
+    (fp32 inputs) and 3.7e-3 (bf16 inputs) of their maximum
+    (tests/test_conditioning.py), and the rounding errors of any fp32 forward
+    grow along its trajectory.  Handed the oracle's checkpoints (rounded to
+    fp32), the backward kernels alone (chunk replay, reverse sweep,
+    reductions) meet the bar there: every gradient element within 1e-4 (fp32
+    inputs) or 5e-3 (bf16 inputs)."""
+    x = low_f_inputs(dtype, 300, 0.0)
+    ck = 16
+    g = to_gpu(x)
+    Hck = torch.from_numpy(oracle.forward(*to_f64(x), ckpt_every=ck)[2]).float().cuda()
+    out = m2.backward(g["q"], g["k"], g["v"], g["f"], g["W"], g["wr"], Hck, ck, g["dy"])
+    torch.cuda.synchronize()
+    gg = {k: v.cpu().numpy() for k, v in out.items()}
+    check(gg, ref_grads(x), TOL[dtype], f"{dtype} f = 0 full W from the oracle's checkpoints")
+
+
+def test_backward_f_zero_f32_half_w():
+    """fp32 inputs, f = 0 at N=520, with W halved (standard deviation 1/8): at
+    the full scale a half-ulp change of the inputs already moves the exact
+    gradients by more than the fp32 bar of 1e-4 (tests/test_conditioning.py),
+    so no fp32 computation can be held to it there; with W halved that
+    sensitivity is 1e-7."""
+    x = low_f_inputs("f32", 520, 0.0, w_scale=0.5)
+    check(gpu_grads(x, 16), ref_grads(x), TOL["f32"], "f32 f = 0 half W")
+
+
+@pytest.mark.xfail(strict=False, reason="ill-conditioned draw (B=2 T=90 N=300, f = 0, full W, bf16 inputs): a "
+                   "half-ulp change of the inputs moves the exact gradients by 3.7e-3 of their maximum, the "
+                   "forward's rounding errors grow along the trajectory, and the end-to-end error measured "
+                   "1.1e-2 to 1.7e-2 (dk); from exact checkpoints the backward meets the bar (1.2e-3)")
+def test_backward_f_zero_full_w_bf16_ill_conditioned():
+    """End to end on the ill-conditioned draw of
+    test_backward_from_exact_checkpoints_ill_conditioned: kept to record the
+    error, expected to miss the bf16 bar."""
+    x = low_f_inputs("bf16", 300, 0.0)
+    check(gpu_grads(x, 16), ref_grads(x), TOL["bf16"], "bf16 f = 0 full W (B=2 T=90 N=300) end to end")
 
 
 def test_backward_bf16_weight_range():
