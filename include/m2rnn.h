@@ -25,8 +25,10 @@
  *
  * Conventions for every entry point:
  *   - All tensors are dense, row-major (C-contiguous) DEVICE buffers owned by
- *     the caller.  The library never allocates, frees or synchronises, and
- *     keeps no state between calls except the thread-local error message.
+ *     the caller.  The library never allocates, frees or synchronises.
+ *     Between calls it keeps only the thread-local error message, the
+ *     per-device address of its scratch array (m2rnn_gate_rmsnorm_backward_noalloc)
+ *     and a per-device kernel attribute set on a device's first backward.
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls are
  *     asynchronous on that stream; results are ready when it is.
  *   - Inputs q, k, v, f, W, w_r all have dtype `dtype` (M2RNN_F32 or
@@ -260,6 +262,25 @@ int m2rnn_gate_rmsnorm_backward(int B, int T, int N, int V, int dtype,
                                 const float* y, const void* g, const void* w, float eps,
                                 const float* dout, float* dy, float* dg, float* dw,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * m2rnn_gate_rmsnorm_backward for callers that cannot allocate device memory
+ * (code under HIP graph capture, serving loops, harnesses that forbid
+ * allocation): the same arguments without the workspace, and the same
+ * results and errors.  Its dw partial sums go to a scratch array inside the
+ * library, 8,650,752 bytes on each GPU it runs on (held until the process
+ * ends), which covers every size the entry point accepts (N V <= 2048);
+ * a workspace beyond it would return M2RNN_ERR_UNSUPPORTED.  The GPU is the
+ * one `stream` belongs to (the current device for the NULL stream).  It calls
+ * no allocation routine.  All calls on one GPU share that GPU's array: calls
+ * that may run at the same time on one GPU (different streams, or different
+ * host threads without ordering) race on it and give wrong dw; order them on
+ * one stream.
+ */
+int m2rnn_gate_rmsnorm_backward_noalloc(int B, int T, int N, int V, int dtype,
+                                        const float* y, const void* g, const void* w, float eps,
+                                        const float* dout, float* dy, float* dg, float* dw,
+                                        void* stream);
 
 /*
  * One token of the recurrence for every (b, n), state held by the caller

@@ -70,6 +70,8 @@ lib.m2rnn_gate_rmsnorm_backward_workspace_bytes.argtypes = [_i] * 4
 lib.m2rnn_gate_rmsnorm_backward.restype = _i
 lib.m2rnn_gate_rmsnorm_backward.argtypes = ([_i] * 5 + [_p] * 3 + [ctypes.c_float] + [_p] * 4
                                             + [_p, ctypes.c_size_t, _p])
+lib.m2rnn_gate_rmsnorm_backward_noalloc.restype = _i
+lib.m2rnn_gate_rmsnorm_backward_noalloc.argtypes = [_i] * 5 + [_p] * 3 + [ctypes.c_float] + [_p] * 4 + [_p]
 lib.m2rnn_decode.restype = _i
 lib.m2rnn_decode.argtypes = [_i] * 5 + [_p] * 6 + [_p, _p, _p]
 lib.m2rnn_last_error.restype = ctypes.c_char_p
@@ -294,6 +296,27 @@ def gate_rmsnorm_backward(y, g, w, dout, eps=0.0, out=None, workspace=None):
     _check(lib.m2rnn_gate_rmsnorm_backward(B, T, N, Vv, _dtype_code(g), _ptr(y), _ptr(g), _ptr(w), float(eps),
                                            _ptr(dout), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(workspace),
                                            wbytes, _stream(dev)))
+    return out
+
+
+def m2rnn_gate_rmsnorm_backward_noalloc(B, T, N, V_, dtype, y, g, w, eps, dout, dy, dg, dw, stream):
+    """Raw C-ABI call with ctypes pointers; returns the status code."""
+    return lib.m2rnn_gate_rmsnorm_backward_noalloc(B, T, N, V_, dtype, y, g, w, eps, dout, dy, dg, dw, stream)
+
+
+def gate_rmsnorm_backward_noalloc(y, g, w, dout, eps=0.0, out=None):
+    """gate_rmsnorm_backward without a workspace: the library's own scratch
+    array on the GPU holds the dw partial sums (calls on one GPU must be
+    ordered on one stream).  Returns (dy, dg, dw) float32; `out` may pass
+    them."""
+    B, T, N, Vv = y.shape
+    dev = y.device
+    if out is None:
+        out = (torch.empty_like(y, dtype=torch.float32), torch.empty_like(y, dtype=torch.float32),
+               torch.empty((N * Vv,), device=dev, dtype=torch.float32))
+    _check(lib.m2rnn_gate_rmsnorm_backward_noalloc(B, T, N, Vv, _dtype_code(g), _ptr(y), _ptr(g), _ptr(w), float(eps),
+                                                   _ptr(dout), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
+                                                   _stream(dev)))
     return out
 
 

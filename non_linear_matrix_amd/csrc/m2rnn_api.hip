@@ -8,6 +8,8 @@
 #include <stdint.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "m2rnn_internal.h"
 
 namespace {
@@ -275,12 +277,17 @@ extern "C" size_t m2rnn_gate_rmsnorm_backward_workspace_bytes(int B, int T, int 
   return sizeof(float) * m2rnn::norm_backward_workspace_floats(ntok, (int)d);
 }
 
-extern "C" int m2rnn_gate_rmsnorm_backward(int B, int T, int N, int V, int dtype, const float* y, const void* g,
-                                           const void* w, float eps, const float* dout, float* dy, float* dg,
-                                           float* dw, void* workspace, size_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
+namespace {
+
+// Validation shared by both backward entry points.  Returns M2RNN_OK with
+// *done set when nothing needs a workspace (d == 0, or B T == 0 where dw = 0
+// is written), else fills *a for the launch.
+int norm_backward_prepare(int B, int T, int N, int V, int dtype, const float* y, const void* g, const void* w,
+                          float eps, const float* dout, float* dy, float* dg, float* dw, void* stream,
+                          m2rnn::NormArgs* a, bool* done) {
   long long ntok;
   int d, st;
+  *done = true;
   if ((st = norm_check(B, T, N, V, dtype, eps, &ntok, &d))) return st;
   const size_t es = dtype == M2RNN_F32 ? 4 : 2;
   const long long n = ntok * d;
@@ -288,22 +295,110 @@ extern "C" int m2rnn_gate_rmsnorm_backward(int B, int T, int N, int V, int dtype
       (st = need(dout, "dout", n, 16)) || (st = need(dy, "dy", n, 16)) || (st = need(dg, "dg", n, 16)) ||
       (st = need(dw, "dw", d, 16)))
     return st;
-  hipStream_t s = (hipStream_t)stream;
   if (d == 0) return M2RNN_OK;
   if (ntok == 0) {   // dw = 0
-    hipError_t e = m2rnn::launch_fill_zero(dw, (size_t)d, s);
+    hipError_t e = m2rnn::launch_fill_zero(dw, (size_t)d, (hipStream_t)stream);
     return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "dw = 0: %s", hipGetErrorString(e));
   }
+  *a = m2rnn::NormArgs{};
+  a->y = y; a->g = g; a->w = w; a->dout = dout; a->dy = dy; a->dg = dg; a->dw = dw;
+  a->ntok = ntok; a->d = d; a->eps = eps;
+  *done = false;
+  return M2RNN_OK;
+}
+
+int norm_backward_launch(const m2rnn::NormArgs& a, int dtype, void* stream) {
+  hipError_t e = m2rnn::launch_norm_backward(a, dtype, (hipStream_t)stream);
+  return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "gate_rmsnorm backward launch: %s", hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" int m2rnn_gate_rmsnorm_backward(int B, int T, int N, int V, int dtype, const float* y, const void* g,
+                                           const void* w, float eps, const float* dout, float* dy, float* dg,
+                                           float* dw, void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  m2rnn::NormArgs a;
+  bool done;
+  int st = norm_backward_prepare(B, T, N, V, dtype, y, g, w, eps, dout, dy, dg, dw, stream, &a, &done);
+  if (st || done) return st;
   const size_t need_bytes = m2rnn_gate_rmsnorm_backward_workspace_bytes(B, T, N, V);
   if (!workspace || workspace_bytes < need_bytes)
     return fail(M2RNN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need_bytes,
                 workspace ? workspace_bytes : (size_t)0);
   if (!aligned(workspace, 16)) return fail(M2RNN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  m2rnn::NormArgs a{};
-  a.y = y; a.g = g; a.w = w; a.dout = dout; a.dy = dy; a.dg = dg; a.dw = dw; a.ws = (float*)workspace;
-  a.ntok = ntok; a.d = d; a.eps = eps;
-  hipError_t e = m2rnn::launch_norm_backward(a, dtype, s);
-  return e == hipSuccess ? M2RNN_OK : fail(M2RNN_ERR_HIP, "gate_rmsnorm backward launch: %s", hipGetErrorString(e));
+  a.ws = (float*)workspace;
+  return norm_backward_launch(a, dtype, stream);
+}
+
+// ---------------------- output gate and RMSNorm backward without a workspace
+//
+// For callers that cannot allocate device memory: the dw partial sums go to
+// `scratch`, a file-scope device array (one copy per GPU, held from the
+// library's load until the process ends), sized for the largest workspace the
+// backward takes: kNormMaxGroups partial rows and kColsumRowBlocks second-level
+// rows of at most kNormMaxD floats.  Every element the kernels read from it is
+// written earlier in the same call, so nothing needs clearing.  Host code
+// never names `scratch` in a launch or a copy: its host-side name is not a
+// device address.  The address comes from hipGetSymbolAddress, taken once per
+// device with that device current.
+namespace {
+constexpr size_t kNormScratchFloats =
+    ((size_t)m2rnn::kNormMaxGroups + m2rnn::kColsumRowBlocks) * (size_t)m2rnn::kNormMaxD;
+}  // namespace
+
+static __device__ __align__(256) float scratch[kNormScratchFloats];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the GPU that `stream` runs on (the
+// current device for the NULL stream).
+int scratch_address(void* stream, float** out) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(M2RNN_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(M2RNN_ERR_UNSUPPORTED, "device %d: only devices 0..%d are served", dev,
+                                                 kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return fail(M2RNN_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(M2RNN_ERR_HIP, "hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess || !p)
+      return fail(M2RNN_ERR_HIP, "address of the scratch array on device %d: %s", dev, hipGetErrorString(e));
+    if (e2 != hipSuccess) return fail(M2RNN_ERR_HIP, "hipSetDevice(%d): %s", cur, hipGetErrorString(e2));
+    g_scratch_ptr[dev] = (float*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return M2RNN_OK;
+}
+
+}  // namespace
+
+extern "C" int m2rnn_gate_rmsnorm_backward_noalloc(int B, int T, int N, int V, int dtype, const float* y,
+                                                   const void* g, const void* w, float eps, const float* dout,
+                                                   float* dy, float* dg, float* dw, void* stream) {
+  g_err[0] = 0;
+  m2rnn::NormArgs a;
+  bool done;
+  int st = norm_backward_prepare(B, T, N, V, dtype, y, g, w, eps, dout, dy, dg, dw, stream, &a, &done);
+  if (st || done) return st;
+  const size_t need_bytes = m2rnn_gate_rmsnorm_backward_workspace_bytes(B, T, N, V);
+  if (need_bytes > sizeof(scratch))
+    return fail(M2RNN_ERR_UNSUPPORTED, "needs %zu bytes of scratch; the library holds %zu", need_bytes,
+                sizeof(scratch));
+  float* ws = nullptr;
+  if ((st = scratch_address(stream, &ws))) return st;
+  a.ws = ws;
+  return norm_backward_launch(a, dtype, stream);
 }
 
 // ------------------------------------------------ causal Conv1D and SiLU

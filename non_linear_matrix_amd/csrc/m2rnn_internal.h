@@ -65,6 +65,7 @@ struct NormArgs {
   float eps;
 };
 constexpr int kNormMaxD = 2048;
+constexpr int kNormMaxGroups = 1024;   // workgroups (dw partial rows) of the backward, at most
 // Workgroups (and dw partial rows) of the backward, and its workspace.
 int norm_backward_groups(long long ntok, int d);
 size_t norm_backward_workspace_floats(long long ntok, int d);

@@ -175,7 +175,7 @@ hipError_t norm_bwd_t(const NormArgs& a, hipStream_t stream) {
 int norm_backward_groups(long long ntok, int d) {
   (void)d;
   long long wg = (ntok + kWaves - 1) / kWaves;
-  if (wg > 1024) wg = 1024;
+  if (wg > kNormMaxGroups) wg = kNormMaxGroups;
   return wg < 1 ? 1 : (int)wg;
 }
 

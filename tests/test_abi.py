@@ -27,8 +27,9 @@ def test_header_declares_the_entry_points():
     assert declared() == ["m2rnn_backward", "m2rnn_backward_gated", "m2rnn_backward_workspace_bytes",
                           "m2rnn_conv_silu_backward", "m2rnn_conv_silu_backward_workspace_bytes",
                           "m2rnn_conv_silu_forward", "m2rnn_decode", "m2rnn_forward", "m2rnn_forward_gated",
-                          "m2rnn_gate_rmsnorm_backward", "m2rnn_gate_rmsnorm_backward_workspace_bytes",
-                          "m2rnn_gate_rmsnorm_forward", "m2rnn_last_error"]
+                          "m2rnn_gate_rmsnorm_backward", "m2rnn_gate_rmsnorm_backward_noalloc",
+                          "m2rnn_gate_rmsnorm_backward_workspace_bytes", "m2rnn_gate_rmsnorm_forward",
+                          "m2rnn_last_error"]
 
 
 def test_library_exports_every_declared_symbol(m2):
@@ -161,6 +162,15 @@ def test_gate_rmsnorm_argument_errors_without_launch(m2):
     assert bwd(2, 3, 5, 16, 0, dummy, dummy, dummy, 0.0, dummy, dummy, None, dummy, dummy, 1 << 20, None) == \
         m2.M2RNN_ERR_INVALID_ARG
     assert "dg" in m2.m2rnn_last_error()
+    # the variant without a workspace validates the same way, before it looks up its scratch array
+    na = m2.lib.m2rnn_gate_rmsnorm_backward_noalloc
+    assert na(2, 3, 5, 16, 0, dummy, dummy, dummy, 0.0, dummy, dummy, None, dummy, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert "dg" in m2.m2rnn_last_error()
+    assert na(2, 3, 129, 16, 0, dummy, dummy, dummy, 0.0, dummy, dummy, dummy, dummy, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert na(2, 3, 5, 16, 0, dummy, dummy, dummy, ctypes.c_float(-1.0), dummy, dummy, dummy, dummy, None) == \
+        m2.M2RNN_ERR_INVALID_ARG
+    # its scratch array covers the largest workspace: 1024 partial rows and 32 second-level rows of 2048 floats
+    assert ws(64, 4096, 128, 16) == (1024 + 32) * 2048 * 4 == 8650752
 
 
 def test_conv_silu_argument_errors_without_launch(m2):
