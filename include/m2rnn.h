@@ -53,7 +53,9 @@
  *     m2rnn_backward), so W must lie within fp16's range, |W| <= 65504
  *     (entries below 2^-14 in magnitude round to within 2^-25; entries
  *     beyond the range make the results non-finite).  fp32 inputs use exact
- *     fp32 products throughout.
+ *     fp32 products throughout.  tanh is 1 - 2 / (1 + 2^{2x / ln 2}) with the
+ *     hardware exp2 and reciprocal: within 2.5e-7 of tanh (measured over
+ *     [-10, 10], |x| < 1e-3 and |x| >= 20), exactly +-1 for |x| >= 20.
  *   - Errors are reported before anything is launched: a negative status is
  *     returned and m2rnn_last_error() describes it.  A failed kernel launch
  *     returns M2RNN_ERR_HIP.

@@ -105,10 +105,65 @@ def _dtype_code(t):
     raise TypeError(f"inputs must be float32 or bfloat16, got {t.dtype}")
 
 
-def _sizes(q, v):
+def _tensor(t, name, shape, dtype, device):
+    """Raise ValueError unless t is a contiguous tensor of this shape, dtype
+    and device: the C ABI sees only the data pointer, so a mismatch would be
+    read as the wrong bytes (or past the end of the buffer) on the GPU."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device} (all tensors on one device)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _opt(t, name, shape, dtype, device):
+    return None if t is None else _tensor(t, name, shape, dtype, device)
+
+
+def _gpu(device):
+    if device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU, got {device}")
+
+
+def _in_dtype(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"inputs must be float32 or bfloat16, got {name} in {t.dtype}")
+    return t.dtype
+
+
+def _scan_inputs(q, k, v, f, W, w_r, f_name="f", alpha=None, beta=None):
+    """Checks the scan's inputs (all of q's dtype, contiguous, on q's device)
+    and returns B, T, N, K, V and the device."""
+    dt = _in_dtype(q, "q")
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B, T, K], got shape {tuple(q.shape)}")
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise ValueError("v must be a 4-D tensor [B, T, N, V]")
     B, T, Kq = q.shape
     N, Vv = v.shape[2], v.shape[3]
-    return B, T, N, Kq, Vv
+    dev = q.device
+    _tensor(q, "q", (B, T, Kq), dt, dev)
+    _tensor(k, "k", (B, T, Kq), dt, dev)
+    _tensor(v, "v", (B, T, N, Vv), dt, dev)
+    _tensor(f, f_name, (B, T, N), dt, dev)
+    _tensor(W, "W", (N, Vv, Vv), dt, dev)
+    _tensor(w_r, "w_r", (N, Vv), dt, dev)
+    if alpha is not None or beta is not None:
+        _tensor(alpha, "alpha", (N,), dt, dev)
+        _tensor(beta, "beta", (N,), dt, dev)
+    return B, T, N, Kq, Vv, dev
+
+
+def _n_ckpt(T, ckpt_every):
+    return (T + ckpt_every - 1) // ckpt_every if ckpt_every > 0 else 0
 
 
 def m2rnn_forward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_0, y, H_T, H_ckpt, ckpt_every, stream):
@@ -151,18 +206,26 @@ def m2rnn_last_error():
     return lib.m2rnn_last_error().decode()
 
 
-def _fwd_outputs(q, v, ckpt_every, out):
-    B, T, N, Kq, Vv = _sizes(q, v)
-    dev = q.device
+def _fwd_outputs(B, T, N, Kq, Vv, dev, ckpt_every, out, H_0):
+    f32 = torch.float32
+    if int(ckpt_every) < 0:
+        raise ValueError("ckpt_every must be >= 0")
+    _opt(H_0, "H_0", (B, N, Kq, Vv), f32, dev)
+    shape_ck = (B, N, _n_ckpt(T, ckpt_every), Kq, Vv)
     if out is None:
-        y = torch.empty((B, T, N, Vv), device=dev, dtype=torch.float32)
-        H_T = torch.empty((B, N, Kq, Vv), device=dev, dtype=torch.float32)
-        H_ck = None
-        if ckpt_every > 0:
-            H_ck = torch.empty((B, N, (T + ckpt_every - 1) // ckpt_every, Kq, Vv), device=dev, dtype=torch.float32)
+        _gpu(dev)
+        y = torch.empty((B, T, N, Vv), device=dev, dtype=f32)
+        H_T = torch.empty((B, N, Kq, Vv), device=dev, dtype=f32)
+        H_ck = torch.empty(shape_ck, device=dev, dtype=f32) if ckpt_every > 0 else None
     else:
         y, H_T = out[0], out[1]
         H_ck = out[2] if len(out) > 2 else None
+        if (H_ck is None) != (ckpt_every <= 0):
+            raise ValueError("out holds H_ckpt exactly when ckpt_every > 0")
+        _tensor(y, "y", (B, T, N, Vv), f32, dev)
+        _tensor(H_T, "H_T", (B, N, Kq, Vv), f32, dev)
+        _opt(H_ck, "H_ckpt", shape_ck, f32, dev)
+    _gpu(dev)
     return y, H_T, H_ck
 
 
@@ -171,8 +234,8 @@ def forward(q, k, v, f, W, w_r, ckpt_every=0, out=None, H_0=None):
     H_ckpt [B,N,ceil(T/ckpt_every),K,V].  `out` may pass preallocated
     (y, H_T[, H_ckpt]) tensors; H_0 [B,N,K,V] float32 is the initial state
     (None: zero) and may be the same tensor as H_T."""
-    B, T, N, Kq, Vv = _sizes(q, v)
-    y, H_T, H_ck = _fwd_outputs(q, v, ckpt_every, out)
+    B, T, N, Kq, Vv, dev = _scan_inputs(q, k, v, f, W, w_r)
+    y, H_T, H_ck = _fwd_outputs(B, T, N, Kq, Vv, dev, ckpt_every, out, H_0)
     _check(lib.m2rnn_forward(B, T, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W),
                              _ptr(w_r), _ptr(H_0), _ptr(y), _ptr(H_T), _ptr(H_ck), int(ckpt_every),
                              _stream(q.device)))
@@ -182,30 +245,57 @@ def forward(q, k, v, f, W, w_r, ckpt_every=0, out=None, H_0=None):
 def forward_gated(q, k, v, a, alpha, beta, W, w_r, ckpt_every=0, out=None, H_0=None):
     """forward() with f = exp(-alpha[n] softplus(a + beta[n])) computed in the
     kernel from the gate pre-activation a [B,T,N] and alpha, beta [N]."""
-    B, T, N, Kq, Vv = _sizes(q, v)
-    y, H_T, H_ck = _fwd_outputs(q, v, ckpt_every, out)
+    B, T, N, Kq, Vv, dev = _scan_inputs(q, k, v, a, W, w_r, f_name="a", alpha=alpha, beta=beta)
+    y, H_T, H_ck = _fwd_outputs(B, T, N, Kq, Vv, dev, ckpt_every, out, H_0)
     _check(lib.m2rnn_forward_gated(B, T, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                    _ptr(alpha), _ptr(beta), _ptr(W), _ptr(w_r), _ptr(H_0), _ptr(y), _ptr(H_T),
                                    _ptr(H_ck), int(ckpt_every), _stream(q.device)))
     return (y, H_T) if H_ck is None else (y, H_T, H_ck)
 
 
+def _bwd_outputs(B, T, N, Kq, Vv, dev, H_ckpt, ckpt_every, dy, dH_T, out, want_dH_0, df_name):
+    f32 = torch.float32
+    if int(ckpt_every) < 1:
+        raise ValueError("ckpt_every must be >= 1 for the backward")
+    _tensor(H_ckpt, "H_ckpt", (B, N, _n_ckpt(T, ckpt_every), Kq, Vv), f32, dev)
+    _tensor(dy, "dy", (B, T, N, Vv), f32, dev)
+    _opt(dH_T, "dH_T", (B, N, Kq, Vv), f32, dev)
+    shapes = dict(dq=(B, T, Kq), dk=(B, T, Kq), dv=(B, T, N, Vv), dW=(N, Vv, Vv), dw_r=(N, Vv))
+    shapes[df_name] = (B, T, N)
+    if df_name == "da":
+        shapes.update(dalpha=(N,), dbeta=(N,))
+    if out is not None:
+        for n, sh in shapes.items():
+            if n not in out:
+                raise ValueError(f"out has no {n}")
+            _tensor(out[n], n, sh, f32, dev)
+        _opt(out.get("dH_0"), "dH_0", (B, N, Kq, Vv), f32, dev)
+    _gpu(dev)
+    if out is None:
+        out = {n: torch.empty(sh, device=dev, dtype=f32) for n, sh in shapes.items()}
+        if want_dH_0:
+            out["dH_0"] = torch.empty((B, N, Kq, Vv), device=dev, dtype=f32)
+    return out
+
+
+def _bwd_workspace(B, T, N, Kq, Vv, dev, ckpt_every, workspace):
+    nbytes = int(lib.m2rnn_backward_workspace_bytes(B, T, N, Kq, Vv, int(ckpt_every)))
+    if workspace is None:
+        if nbytes > 0:
+            workspace = torch.empty((nbytes,), device=dev, dtype=torch.uint8)
+    else:
+        _tensor(workspace, "workspace", (workspace.numel(),), workspace.dtype, dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, wbytes
+
+
 def backward(q, k, v, f, W, w_r, H_ckpt, ckpt_every, dy, dH_T=None, out=None, workspace=None, want_dH_0=False):
     """Gradients of sum(y*dy) + sum(H_T*dH_T): dict dq, dk [B,T,K]; dv [B,T,N,V];
     df [B,T,N]; dW [N,V,V]; dw_r [N,V] and, with want_dH_0 (or a "dH_0"
     entry in `out`), dH_0 [B,N,K,V] (float32)."""
-    B, T, N, Kq, Vv = _sizes(q, v)
-    dev = q.device
-    if out is None:
-        out = dict(dq=torch.empty((B, T, Kq), device=dev), dk=torch.empty((B, T, Kq), device=dev),
-                   dv=torch.empty((B, T, N, Vv), device=dev), df=torch.empty((B, T, N), device=dev),
-                   dW=torch.empty((N, Vv, Vv), device=dev), dw_r=torch.empty((N, Vv), device=dev))
-        if want_dH_0:
-            out["dH_0"] = torch.empty((B, N, Kq, Vv), device=dev)
-    nbytes = int(lib.m2rnn_backward_workspace_bytes(B, T, N, Kq, Vv, int(ckpt_every)))
-    if workspace is None and nbytes > 0:
-        workspace = torch.empty((nbytes,), device=dev, dtype=torch.uint8)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    B, T, N, Kq, Vv, dev = _scan_inputs(q, k, v, f, W, w_r)
+    out = _bwd_outputs(B, T, N, Kq, Vv, dev, H_ckpt, ckpt_every, dy, dH_T, out, want_dH_0, "df")
+    workspace, wbytes = _bwd_workspace(B, T, N, Kq, Vv, dev, ckpt_every, workspace)
     _check(lib.m2rnn_backward(B, T, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W),
                               _ptr(w_r), _ptr(H_ckpt), int(ckpt_every), _ptr(dy), _ptr(dH_T),
                               _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["df"]),
@@ -218,19 +308,9 @@ def backward_gated(q, k, v, a, alpha, beta, W, w_r, H_ckpt, ckpt_every, dy, dH_T
                    want_dH_0=False):
     """backward() of forward_gated(): the dict holds da [B,T,N] and dalpha,
     dbeta [N] in place of df."""
-    B, T, N, Kq, Vv = _sizes(q, v)
-    dev = q.device
-    if out is None:
-        out = dict(dq=torch.empty((B, T, Kq), device=dev), dk=torch.empty((B, T, Kq), device=dev),
-                   dv=torch.empty((B, T, N, Vv), device=dev), da=torch.empty((B, T, N), device=dev),
-                   dalpha=torch.empty((N,), device=dev), dbeta=torch.empty((N,), device=dev),
-                   dW=torch.empty((N, Vv, Vv), device=dev), dw_r=torch.empty((N, Vv), device=dev))
-        if want_dH_0:
-            out["dH_0"] = torch.empty((B, N, Kq, Vv), device=dev)
-    nbytes = int(lib.m2rnn_backward_workspace_bytes(B, T, N, Kq, Vv, int(ckpt_every)))
-    if workspace is None and nbytes > 0:
-        workspace = torch.empty((nbytes,), device=dev, dtype=torch.uint8)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    B, T, N, Kq, Vv, dev = _scan_inputs(q, k, v, a, W, w_r, f_name="a", alpha=alpha, beta=beta)
+    out = _bwd_outputs(B, T, N, Kq, Vv, dev, H_ckpt, ckpt_every, dy, dH_T, out, want_dH_0, "da")
+    workspace, wbytes = _bwd_workspace(B, T, N, Kq, Vv, dev, ckpt_every, workspace)
     _check(lib.m2rnn_backward_gated(B, T, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                     _ptr(alpha), _ptr(beta), _ptr(W), _ptr(w_r), _ptr(H_ckpt), int(ckpt_every),
                                     _ptr(dy), _ptr(dH_T), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
@@ -243,10 +323,23 @@ def backward_gated(q, k, v, a, alpha, beta, W, w_r, H_ckpt, ckpt_every, dy, dH_T
 def decode(q, k, v, f, W, w_r, H, y=None):
     """One token for every (b, n): q, k [B,K]; v [B,N,V]; f [B,N]; H [B,N,K,V]
     float32, advanced in place.  Returns y [B,N,V] float32."""
+    dt = _in_dtype(q, "q")
+    if q.dim() != 2 or not isinstance(v, torch.Tensor) or v.dim() != 3:
+        raise ValueError("decode takes q, k [B, K] and v [B, N, V]")
     B, Kq = q.shape
     N, Vv = v.shape[1], v.shape[2]
+    dev = q.device
+    _tensor(q, "q", (B, Kq), dt, dev)
+    _tensor(k, "k", (B, Kq), dt, dev)
+    _tensor(v, "v", (B, N, Vv), dt, dev)
+    _tensor(f, "f", (B, N), dt, dev)
+    _tensor(W, "W", (N, Vv, Vv), dt, dev)
+    _tensor(w_r, "w_r", (N, Vv), dt, dev)
+    _tensor(H, "H", (B, N, Kq, Vv), torch.float32, dev)
+    _opt(y, "y", (B, N, Vv), torch.float32, dev)
+    _gpu(dev)
     if y is None:
-        y = torch.empty((B, N, Vv), device=q.device, dtype=torch.float32)
+        y = torch.empty((B, N, Vv), device=dev, dtype=torch.float32)
     _check(lib.m2rnn_decode(B, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W), _ptr(w_r),
                             _ptr(H), _ptr(y), _stream(q.device)))
     return y
@@ -268,12 +361,29 @@ def m2rnn_gate_rmsnorm_backward_workspace_bytes(B, T, N, V_=V):
     return int(lib.m2rnn_gate_rmsnorm_backward_workspace_bytes(B, T, N, V_))
 
 
+def _norm_inputs(y, g, w):
+    """Checks y (float32 [B,T,N,V]), g (y's shape, the input dtype) and w
+    ([N,V] or [N*V], g's dtype); returns B, T, N, V and the device."""
+    if not isinstance(y, torch.Tensor) or y.dim() != 4:
+        raise ValueError("y must be a 4-D tensor [B, T, N, V]")
+    B, T, N, Vv = y.shape
+    dev = y.device
+    dt = _in_dtype(g, "g")
+    _tensor(y, "y", (B, T, N, Vv), torch.float32, dev)
+    _tensor(g, "g", (B, T, N, Vv), dt, dev)
+    _tensor(w, "w", (N, Vv) if isinstance(w, torch.Tensor) and w.dim() == 2 else (N * Vv,), dt, dev)
+    return B, T, N, Vv, dev
+
+
 def gate_rmsnorm_forward(y, g, w, eps=0.0, out=None, rstd=None):
     """out = w * x * s with x = y * g and s = (mean over the N*V features of
     x^2 + eps)^-1/2, per token.  y [B,T,N,V] float32; g like y and w [N,V]
     (or [N*V]) in the input dtype.  Returns out [B,T,N,V] float32 (`out` may
     be y itself); `rstd` [B,T] float32, if given, receives s."""
-    B, T, N, Vv = y.shape
+    B, T, N, Vv, dev = _norm_inputs(y, g, w)
+    _opt(out, "out", (B, T, N, Vv), torch.float32, dev)
+    _opt(rstd, "rstd", (B, T), torch.float32, dev)
+    _gpu(dev)
     if out is None:
         out = torch.empty_like(y, dtype=torch.float32)
     _check(lib.m2rnn_gate_rmsnorm_forward(B, T, N, Vv, _dtype_code(g), _ptr(y), _ptr(g), _ptr(w), float(eps),
@@ -281,17 +391,31 @@ def gate_rmsnorm_forward(y, g, w, eps=0.0, out=None, rstd=None):
     return out
 
 
+def _norm_grads(B, T, N, Vv, dev, dout, out):
+    f32 = torch.float32
+    _tensor(dout, "dout", (B, T, N, Vv), f32, dev)
+    if out is not None:
+        _tensor(out[0], "dy", (B, T, N, Vv), f32, dev)
+        _tensor(out[1], "dg", (B, T, N, Vv), f32, dev)
+        _tensor(out[2], "dw", (N, Vv) if isinstance(out[2], torch.Tensor) and out[2].dim() == 2 else (N * Vv,), f32,
+                dev)
+    _gpu(dev)
+    if out is None:
+        out = (torch.empty((B, T, N, Vv), device=dev, dtype=f32), torch.empty((B, T, N, Vv), device=dev, dtype=f32),
+               torch.empty((N * Vv,), device=dev, dtype=f32))
+    return out
+
+
 def gate_rmsnorm_backward(y, g, w, dout, eps=0.0, out=None, workspace=None):
     """Gradients of sum(out * dout) for gate_rmsnorm_forward: (dy [B,T,N,V],
     dg [B,T,N,V], dw [N*V]) float32.  `out` may pass (dy, dg, dw)."""
-    B, T, N, Vv = y.shape
-    dev = y.device
-    if out is None:
-        out = (torch.empty_like(y, dtype=torch.float32), torch.empty_like(y, dtype=torch.float32),
-               torch.empty((N * Vv,), device=dev, dtype=torch.float32))
+    B, T, N, Vv, dev = _norm_inputs(y, g, w)
+    out = _norm_grads(B, T, N, Vv, dev, dout, out)
     nbytes = int(lib.m2rnn_gate_rmsnorm_backward_workspace_bytes(B, T, N, Vv))
     if workspace is None and nbytes > 0:
         workspace = torch.empty((nbytes,), device=dev, dtype=torch.uint8)
+    elif workspace is not None:
+        _tensor(workspace, "workspace", (workspace.numel(),), workspace.dtype, dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.m2rnn_gate_rmsnorm_backward(B, T, N, Vv, _dtype_code(g), _ptr(y), _ptr(g), _ptr(w), float(eps),
                                            _ptr(dout), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(workspace),
@@ -309,11 +433,8 @@ def gate_rmsnorm_backward_noalloc(y, g, w, dout, eps=0.0, out=None):
     array on the GPU holds the dw partial sums (calls on one GPU must be
     ordered on one stream).  Returns (dy, dg, dw) float32; `out` may pass
     them."""
-    B, T, N, Vv = y.shape
-    dev = y.device
-    if out is None:
-        out = (torch.empty_like(y, dtype=torch.float32), torch.empty_like(y, dtype=torch.float32),
-               torch.empty((N * Vv,), device=dev, dtype=torch.float32))
+    B, T, N, Vv, dev = _norm_inputs(y, g, w)
+    out = _norm_grads(B, T, N, Vv, dev, dout, out)
     _check(lib.m2rnn_gate_rmsnorm_backward_noalloc(B, T, N, Vv, _dtype_code(g), _ptr(y), _ptr(g), _ptr(w), float(eps),
                                                    _ptr(dout), _ptr(out[0]), _ptr(out[1]), _ptr(out[2]),
                                                    _stream(dev)))
@@ -337,17 +458,31 @@ def m2rnn_conv_silu_backward_workspace_bytes(B, T, C):
 
 def _conv_shape(u):
     """u [B, T, C] or [B, T, N, V] (treated as C = N V)."""
+    if not isinstance(u, torch.Tensor) or u.dim() not in (3, 4):
+        raise ValueError("u must be [B, T, C] or [B, T, N, V]")
     C = 1
     for s in u.shape[2:]:
         C *= s
     return u.shape[0], u.shape[1], C
 
 
+def _conv_inputs(u, w, bias):
+    B, T, C = _conv_shape(u)
+    dt = _in_dtype(u, "u")
+    dev = u.device
+    _tensor(u, "u", tuple(u.shape), dt, dev)
+    _tensor(w, "w", (C, 4), dt, dev)
+    _opt(bias, "bias", (C,), dt, dev)
+    return B, T, C, dev
+
+
 def conv_silu_forward(u, w, bias=None, out=None):
     """z = SiLU(bias + causal depthwise conv of width 4 over time) with taps
     w [C, 4] in torch conv1d order (the last tap on the current step).  u is
     [B, T, C] or [B, T, N, V]; z has u's shape and dtype."""
-    B, T, C = _conv_shape(u)
+    B, T, C, dev = _conv_inputs(u, w, bias)
+    _opt(out, "z", tuple(u.shape), u.dtype, dev)
+    _gpu(dev)
     if out is None:
         out = torch.empty_like(u)
     _check(lib.m2rnn_conv_silu_forward(B, T, C, _dtype_code(u), _ptr(u), _ptr(w), _ptr(bias), _ptr(out),
@@ -358,14 +493,22 @@ def conv_silu_forward(u, w, bias=None, out=None):
 def conv_silu_backward(u, w, bias, dz, out=None, workspace=None, want_dbias=True):
     """Gradients of sum(z * dz) for conv_silu_forward: (du like u in float32,
     dw [C, 4], dbias [C] or None) float32.  `out` may pass (du, dw, dbias)."""
-    B, T, C = _conv_shape(u)
-    dev = u.device
+    B, T, C, dev = _conv_inputs(u, w, bias)
+    f32 = torch.float32
+    _tensor(dz, "dz", tuple(u.shape), f32, dev)
+    if out is not None:
+        _tensor(out[0], "du", tuple(u.shape), f32, dev)
+        _tensor(out[1], "dw", (C, 4), f32, dev)
+        _opt(out[2], "dbias", (C,), f32, dev)
+    _gpu(dev)
     if out is None:
-        out = (torch.empty(u.shape, device=dev, dtype=torch.float32), torch.empty((C, 4), device=dev),
-               torch.empty((C,), device=dev) if want_dbias else None)
+        out = (torch.empty(u.shape, device=dev, dtype=f32), torch.empty((C, 4), device=dev, dtype=f32),
+               torch.empty((C,), device=dev, dtype=f32) if want_dbias else None)
     nbytes = int(lib.m2rnn_conv_silu_backward_workspace_bytes(B, T, C))
     if workspace is None and nbytes > 0:
         workspace = torch.empty((nbytes,), device=dev, dtype=torch.uint8)
+    elif workspace is not None:
+        _tensor(workspace, "workspace", (workspace.numel(),), workspace.dtype, dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.m2rnn_conv_silu_backward(B, T, C, _dtype_code(u), _ptr(u), _ptr(w), _ptr(bias), _ptr(dz),
                                         _ptr(out[0]), _ptr(out[1]), _ptr(out[2]), _ptr(workspace), wbytes,

@@ -42,6 +42,8 @@
 //  * per-lane partials of df, dv, dq and dk go to LDS and are reduced once per
 //    sub-chunk; the sums over workgroups (dq, dk) and batch rows (dW, dw_r)
 //    are a second, fixed-order reduction kernel.
+#include <mutex>
+
 #include "m2rnn_device.h"
 #include "m2rnn_internal.h"
 
@@ -708,11 +710,18 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   }
 }
 
-// Largest magnitude of dy and dH_T, the gradients that enter the sweep, as
-// kAmaxParts per-workgroup partial maxima (grid = kAmaxParts workgroups);
-// every sweep workgroup reduces them to the same scale.  NaNs are skipped.
+// Largest finite magnitude of dy and dH_T, the gradients that enter the
+// sweep, as kAmaxParts per-workgroup partial maxima (grid = kAmaxParts
+// workgroups); every sweep workgroup reduces them to the same scale.  NaN and
+// infinite values are skipped, so a non-finite gradient of one chain leaves
+// the scale, and with it every other chain's results, as they would be
+// without it.
+__device__ __forceinline__ float finite_abs(float x) {
+  const float a = fabsf(x);
+  return a <= 3.4028235e38f ? a : 0.0f;
+}
 __device__ __forceinline__ float absmax4(f4 v) {
-  return fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  return fmaxf(fmaxf(finite_abs(v[0]), finite_abs(v[1])), fmaxf(finite_abs(v[2]), finite_abs(v[3])));
 }
 
 __global__ __launch_bounds__(256) void m2rnn_bwd_absmax_kernel(const float* dy, size_t ndy4, const float* dH,
@@ -839,14 +848,38 @@ size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* of
   return o;
 }
 
+// The sweep's dynamic LDS exceeds the default limit, so its kernel takes the
+// attribute that allows it, once per device (with that device current) and
+// kernel instance; later launches on that device find it set.
+constexpr int kMaxDevices = 64;
+
+template <typename TIn, int HPW, bool GATE>
+static hipError_t set_lds_attribute(hipStream_t stream) {
+  static std::mutex mu;
+  static bool done[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (done[dev]) return hipSuccess;
+  int cur = -1;
+  if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+  if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+  e = hipFuncSetAttribute((const void*)m2rnn_bwd_kernel<TIn, HPW, GATE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          BwdCfg<HPW, GATE>::kBytes);
+  const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+  if (e != hipSuccess) return e;
+  if (e2 != hipSuccess) return e2;
+  done[dev] = true;
+  return hipSuccess;
+}
+
 template <typename TIn, int HPW, bool GATE>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   typedef BwdCfg<HPW, GATE> Cfg;
   static_assert(Cfg::kBytes <= 160 * 1024, "backward LDS budget");
-  // once per process and kernel (a function-local static is initialised once,
-  // also when several host threads launch at the same time)
-  static const hipError_t attr = hipFuncSetAttribute((const void*)m2rnn_bwd_kernel<TIn, HPW, GATE>,
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kBytes);
+  const hipError_t attr = set_lds_attribute<TIn, HPW, GATE>(stream);
   if (attr != hipSuccess) return attr;
   dim3 grid((unsigned)(a.B * a.ngroups)), block(Cfg::NT);
   hipLaunchKernelGGL((m2rnn_bwd_kernel<TIn, HPW, GATE>), grid, block, Cfg::kBytes, stream, a);

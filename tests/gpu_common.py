@@ -39,3 +39,12 @@ def make(B, T, N, dtype="f32", f_mu=2.0, seed=0, with_dy=False):
 
 def oracle_forward(x, ckpt_every=0):
     return oracle.forward(*to_f64(x), ckpt_every=ckpt_every)
+
+
+def batch_rows(x, b0, b1, with_dy=False):
+    """Inputs of batch rows b0 .. b1-1 with every head (rows never interact
+    in the forward; W and w_r are shared and kept whole)."""
+    out = dict(q=x["q"][b0:b1], k=x["k"][b0:b1], v=x["v"][b0:b1], f=x["f"][b0:b1], W=x["W"], wr=x["wr"])
+    if with_dy:
+        out["dy"] = x["dy"][b0:b1]
+    return out

@@ -68,3 +68,45 @@ def test_bf16_draw_near_its_bar():
     print(f"bf16 half-ulp sensitivity: N=300 {s300:.2e}, N=520 {s520:.2e}")
     assert s300 >= 2e-3
     assert s520 < 2e-3
+
+
+def headline_chain(b=24, n=38):
+    """Inputs of chain (b, n) of the B=32, T=4096, N=64 workload (the same
+    seeded draw as the GPU tests and the benchmark)."""
+    x = m2rnn_inputs.make_workload(m2rnn_inputs.WORKLOADS["fwdbwd_bf16_B32_T4096_N64"])
+    return dict(q=x["q"][b:b + 1], k=x["k"][b:b + 1], v=x["v"][b:b + 1, :, n:n + 1].contiguous(),
+                f=x["f"][b:b + 1, :, n:n + 1].contiguous(), W=x["W"][n:n + 1], wr=x["wr"][n:n + 1],
+                dy=x["dy"][b:b + 1, :, n:n + 1].contiguous())
+
+
+def test_headline_chain_beyond_an_fp32_state():
+    """Chain (b=24, n=38) of the B=32, T=4096, N=64 workload: its gradients
+    grow by three orders of magnitude backward over t = 2048..2560 (max|df|
+    1.4e5, against 1e2 elsewhere).  Half an fp32 ulp on its q, k, v, W moves
+    them by more than 2e-3 of their maximum (measured 2.5e-3).  And rounding
+    the state once, at t = 2304 inside that window, by half an fp32 ulp and
+    running the rest of the sequence from there moves the gradients of those
+    steps by up to 2e-3 of their maximum (three random roundings; the largest
+    is asserted above 1e-3).  A computation that keeps its state in fp32
+    rounds it at every step of the window, so it cannot hold this chain's
+    gradients to the bf16 bar of 5e-3; the GPU tests hold them to ten times
+    their sensitivity instead."""
+    sl = headline_chain()
+    names = ("q", "k", "v", "f", "W", "wr")
+    s_in = half_ulp_sensitivity(sl)
+    t0 = 2304
+    _, _, ck = oracle.forward(*[sl[n].double().numpy() for n in names], ckpt_every=t0)
+    H0 = ck[:, :, 1]                                                    # the state at t0
+    seg = {n: (t[:, t0:] if n in ("q", "k", "v", "f", "dy") else t).double().numpy() for n, t in sl.items()}
+    ref = oracle.backward(*[seg[n] for n in names], seg["dy"], H_0=H0)
+    moves = []
+    for seed in range(3):
+        rng = np.random.default_rng(seed)
+        got = oracle.backward(*[seg[n] for n in names], seg["dy"],
+                              H_0=H0 * (1.0 + 2.0 ** -24 * rng.choice([-1.0, 1.0], size=H0.shape)))
+        moves.append(max(float(np.max(np.abs(got[n] - ref[n]))) / max(1.0, float(np.max(np.abs(ref[n]))))
+                         for n in ("dk", "dv", "df")))
+    print(f"chain (24, 38): half-ulp sensitivity to the inputs {s_in:.2e}; to the state at t = {t0}: "
+          + " ".join(f"{m:.2e}" for m in moves))
+    assert s_in >= 2e-3
+    assert max(moves) >= 1e-3

@@ -11,7 +11,7 @@ import torch
 import m2rnn_inputs
 import non_linear_matrix_amd as m2
 import oracle
-from gpu_common import NAMES, make, to_f64, to_gpu
+from gpu_common import NAMES, batch_rows, make, to_f64, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -153,9 +153,16 @@ def test_backward_workspace_and_argument_errors():
         m2.backward(x["q"], x["k"], x["v"], x["f"], x["W"], x["wr"], Hck, 16, x["dy"],
                     workspace=torch.empty(nbytes - 256, dtype=torch.uint8, device="cuda"))
     assert e.value.status == m2.M2RNN_ERR_WORKSPACE
-    with pytest.raises(m2.M2RNNError) as e:
+    # a zero interval: the binding rejects it, and so does the C ABI behind it
+    with pytest.raises(ValueError):
         m2.backward(x["q"], x["k"], x["v"], x["f"], x["W"], x["wr"], Hck, 0, x["dy"])
-    assert e.value.status == m2.M2RNN_ERR_INVALID_ARG
+    P = m2._ptr
+    g = [P(x[n]) for n in ("q", "k", "v", "f", "W", "wr")]
+    grads = [P(torch.empty(s, device="cuda")) for s in ((1, 20, 64), (1, 20, 64), (1, 20, 2, 16), (1, 20, 2),
+                                                        (2, 16, 16), (2, 16))]
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    assert m2.m2rnn_backward(1, 20, 2, 64, 16, 0, *g, P(Hck), 0, P(x["dy"]), None, *grads, None, P(ws), nbytes,
+                             m2._stream(Hck.device)) == m2.M2RNN_ERR_INVALID_ARG
     assert m2.m2rnn_backward_workspace_bytes(1, 20, 2, 32, 16, 16) == 0
 
 
@@ -172,35 +179,125 @@ def test_backward_zero_length():
     assert torch.all(out["dW"] == 0) and torch.all(out["dw_r"] == 0)
 
 
-@pytest.mark.parametrize("chains", [[(0, 0), (31, 63), (13, 37)]])
-def test_backward_full_size_sampled(chains):
-    """The B=32, T=4096, N=64 forward + backward in the launch configuration
-    the benchmark times.  Per-chain gradients (dv, df) of sampled (b, n)
-    chains are checked against the oracle run on those chains alone; the
-    shared-input gradients (dq, dk sum over heads; dW, dw_r sum over batch
-    rows) are checked through properties that hold at any size: finiteness
-    and, for dw_r, its closed form sum_t u * v."""
+# Per-tensor partial sums: ("dq", "dk") per batch row, ("dv", "df") per chain,
+# ("dW", "dw_r") per head; the oracle's own gradient names
+ROW_GRADS = (("dq", "dq"), ("dk", "dk"))
+CHAIN_GRADS = (("dv", "dv"), ("df", "df"))
+HEAD_GRADS = (("dW", "dW"), ("dw_r", "dwr"))
+
+
+def half_ulp_moved(sl, rng, W_moved):
+    """A batch row's inputs with q, k, v multiplied by 1 +- 2^-24 (random
+    signs) and W replaced by W_moved (the same for every row)."""
+    out = {n: t.double().numpy() for n, t in sl.items()}
+    for n in ("q", "k", "v"):
+        out[n] = out[n] * (1.0 + 2.0 ** -24 * rng.choice([-1.0, 1.0], size=out[n].shape))
+    out["W"] = W_moved
+    return out
+
+
+def test_backward_headline_every_gradient():
+    """The B=32, T=4096, N=64 forward + backward (checkpoints every 64 steps)
+    in the launch configuration the benchmark times: four heads per sweep
+    workgroup, dq and dk sums over 16 workgroups' partials, dW and dw_r sums
+    over 32 batch rows (slide "Shared queries and keys buy more recurrent
+    capacity", paper Alg. 1; slide "Backup: the recurrent gradient needs both
+    paths").  The oracle runs one batch row (all 64 heads) at a time; the
+    rows' dW and dw_r are summed in ascending b.
+
+    1. From the oracle's checkpoints (rounded to fp32): every element of every
+       gradient within 5e-3 * max(1, max|g_ref|) per tensor.  This holds the
+       backward kernels themselves to the bar at full size.
+    2. End to end (the GPU's own forward): the oracle also reruns each row
+       with q, k, v and W moved by half an fp32 ulp, which gives each output's
+       sensitivity s (scaled like the error: per batch row for dq, dk, per
+       chain for dv, df, per head for dW, dw_r).  Where s < 1e-3, a fifth of
+       the bar, the bar holds (5e-3, scaled per tensor over those outputs).
+       Where it does not, the exact answer itself is not fixed to the bar by
+       an fp32 state (a chain whose gradients grow by orders of magnitude
+       backward in time), and the error must stay within 10 s, the spread of
+       fp32-state computations there (tests/test_conditioning.py)."""
     w = m2rnn_inputs.WORKLOADS["fwdbwd_bf16_B32_T4096_N64"]
+    B, N, ck = w.B, w.N, w.ckpt_every
     x = m2rnn_inputs.make_workload(w)
     g = to_gpu(x)
-    _, _, Hck = m2.forward(g["q"], g["k"], g["v"], g["f"], g["W"], g["wr"], ckpt_every=w.ckpt_every)
-    out = m2.backward(g["q"], g["k"], g["v"], g["f"], g["W"], g["wr"], Hck, w.ckpt_every, g["dy"])
-    torch.cuda.synchronize()
-    for name in ("dq", "dk", "dv", "df", "dW", "dw_r"):
-        assert bool(torch.isfinite(out[name]).all()), name
-    dwr_ref = (g["dy"].double() * g["v"].double()).sum(dim=(0, 1))
-    assert float((out["dw_r"].double() - dwr_ref).abs().max()) <= 1e-3 * max(1.0, float(dwr_ref.abs().max()))
-    for b, n in chains:
-        sl = dict(q=x["q"][b:b + 1], k=x["k"][b:b + 1], v=x["v"][b:b + 1, :, n:n + 1], f=x["f"][b:b + 1, :, n:n + 1],
-                  W=x["W"][n:n + 1], wr=x["wr"][n:n + 1], dy=x["dy"][b:b + 1, :, n:n + 1])
-        gr = ref_grads(sl)
-        for name, rname in (("dv", "dv"), ("df", "df")):
-            got = out[name][b:b + 1, :, n:n + 1].cpu().numpy()
-            ref = gr[rname]
-            err = float(np.max(np.abs(got - ref)))
-            scale = max(1.0, float(np.max(np.abs(ref))))
-            print(f"chain ({b},{n}) {name}: max err {err:.3e} (scale {scale:.2f})")
-            assert err <= 5e-3 * scale
+    names = ("q", "k", "v", "f", "W", "wr")
+    # oracle checkpoints, row by row
+    Hck_ref = torch.empty(B, N, (w.T + ck - 1) // ck, 64, 16)
+    for b in range(B):
+        Hck_ref[b] = torch.from_numpy(oracle.forward(*to_f64(batch_rows(x, b, b + 1)), ckpt_every=ck)[2][0]).float()
+    runs = {}
+    _, _, Hck = m2.forward(g["q"], g["k"], g["v"], g["f"], g["W"], g["wr"], ckpt_every=ck)
+    for label, H in (("end to end", Hck), ("exact checkpoints", Hck_ref.cuda())):
+        out = m2.backward(g["q"], g["k"], g["v"], g["f"], g["W"], g["wr"], H, ck, g["dy"])
+        torch.cuda.synchronize()
+        runs[label] = {k: v.cpu().numpy() for k, v in out.items()}
+    del Hck, Hck_ref
+    # oracle, and the oracle on half-ulp-moved inputs, one batch row at a time
+    rng_W = np.random.default_rng(1000)
+    W_moved = x["W"].double().numpy() * (1.0 + 2.0 ** -24 * rng_W.choice([-1.0, 1.0], size=tuple(x["W"].shape)))
+    ref = {n: np.zeros(runs["end to end"][n].shape) for n, _ in GRADS}
+    moved = {n: np.zeros(runs["end to end"][n].shape) for n, _ in GRADS}
+    for b in range(B):
+        sl = batch_rows(x, b, b + 1, with_dy=True)
+        dy = sl["dy"].double().numpy()
+        gr = oracle.backward(*to_f64(sl), dy)
+        gm = oracle.backward(*[half_ulp_moved({n: sl[n] for n in names}, np.random.default_rng(b), W_moved)[n]
+                               for n in names], dy)
+        for name, rname in ROW_GRADS + CHAIN_GRADS:
+            ref[name][b] = gr[rname][0]
+            moved[name][b] = gm[rname][0]
+        for name, rname in HEAD_GRADS:   # ascending b
+            ref[name] += gr[rname]
+            moved[name] += gm[rname]
+    # 1. from exact checkpoints: every element
+    got = runs["exact checkpoints"]
+    for name, _ in GRADS:
+        scale = max(1.0, float(np.max(np.abs(ref[name]))))
+        err = float(np.max(np.abs(got[name] - ref[name])))
+        print(f"headline from exact checkpoints {name}: scaled err {err / scale:.3e}")
+        assert err <= 5e-3 * scale, f"from exact checkpoints {name}: {err / scale:.3e}"
+    # 2. end to end, split by each output's sensitivity
+    got = runs["end to end"]
+
+    def per_unit(a, name):   # max |a| per batch row, chain or head
+        a = np.abs(a)
+        if name in ("dq", "dk"):
+            return a.max(axis=(1, 2))                       # [B]
+        if name == "dv":
+            return a.max(axis=(1, 3))                       # [B, N]
+        if name == "df":
+            return a.max(axis=1)                            # [B, N]
+        return a.reshape(N, -1).max(axis=1)                 # [N]
+
+    def spread(unit_vals, name, shape):   # back to the tensor's shape
+        if name in ("dq", "dk"):
+            return np.broadcast_to(unit_vals[:, None, None], shape)
+        if name == "dv":
+            return np.broadcast_to(unit_vals[:, None, :, None], shape)
+        if name == "df":
+            return np.broadcast_to(unit_vals[:, None, :], shape)
+        return np.broadcast_to(unit_vals.reshape((N,) + (1,) * (len(shape) - 1)), shape)
+
+    for name, _ in GRADS:
+        shape = ref[name].shape
+        unit_scale = np.maximum(1.0, per_unit(ref[name], name))
+        sens = per_unit(moved[name] - ref[name], name) / unit_scale
+        err_unit = per_unit(got[name] - ref[name], name) / unit_scale
+        ill = sens >= 1e-3
+        well = ~spread(ill, name, shape)
+        scale = max(1.0, float(np.max(np.abs(ref[name][well])))) if well.any() else 1.0
+        err = float(np.max(np.abs(got[name] - ref[name])[well])) if well.any() else 0.0
+        print(f"headline end to end {name}: scaled err {err / scale:.3e} on {int(well.sum())} elements; "
+              f"{int(ill.sum())} of {ill.size} units with half-ulp sensitivity >= 1e-3"
+              + (f" (worst: err {err_unit[ill].max():.2e}, sensitivity {sens[ill][np.argmax(err_unit[ill])]:.2e})"
+                 if ill.any() else ""))
+        assert err <= 5e-3 * scale, f"end to end {name}: {err / scale:.3e}"
+        assert np.all(err_unit[ill] <= 10.0 * sens[ill]), name
+        # ill-conditioned chains are the exception (at most 2% of them); a row
+        # or head sum is ill-conditioned when one chain in it is
+        if name in ("dv", "df"):
+            assert ill.sum() <= 0.02 * ill.size, name
 
 
 def low_f_inputs(dtype, N, fval, w_scale=1.0):

@@ -7,7 +7,7 @@ import torch
 
 import m2rnn_inputs
 import non_linear_matrix_amd as m2
-from gpu_common import TOL, chain_slice, make, max_abs, oracle_forward, to_f64, to_gpu
+from gpu_common import TOL, batch_rows, chain_slice, make, max_abs, oracle_forward, to_f64, to_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -197,24 +197,26 @@ def test_forward_rejects_bad_arguments():
     assert m2.m2rnn_forward(1, 4, 2, 64, 16, 0, *args, None, P(y), P(H), P(H), 0, s) == m2.M2RNN_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("name,chains", [
-    ("fwd_bf16_B8_T2048_N16", [(0, 0), (7, 15), (3, 9)]),
-    ("fwd_bf16_B2_T32768_N32", [(1, 31)]),
-    ("fwd_bf16_B32_T4096_N64", [(0, 0), (31, 63), (17, 40)]),
+@pytest.mark.parametrize("name,rows", [
+    ("fwd_bf16_B8_T2048_N16", None),
+    ("fwd_bf16_B2_T32768_N32", None),
+    ("fwd_bf16_B32_T4096_N64", [(0, 4), (15, 17), (28, 32)]),
 ])
-def test_forward_full_size_sampled(name, chains):
-    """Full-size workloads in the launch configuration the benchmark times;
-    sampled (b, n) chains are checked against the oracle run on just those
-    chains, and every output is checked for |H_T| <= 1 and finiteness."""
+def test_forward_full_size(name, rows):
+    """Full-size workloads in the launch configuration the benchmark times,
+    against the oracle element by element: every y and H_T element of the
+    B=8, T=2048, N=16 and B=2, T=32768, N=32 workloads, and every element of
+    eight whole batch rows (all 64 heads, first, middle and last) of the
+    B=32, T=4096, N=64 one; every output is finite with |H_T| <= 1."""
     w = m2rnn_inputs.WORKLOADS[name]
     x = m2rnn_inputs.make_workload(w)
     g = to_gpu(x)
     y, HT = m2.forward(g["q"], g["k"], g["v"], g["f"], g["W"], g["wr"])
     torch.cuda.synchronize()
     assert bool(torch.isfinite(y).all()) and float(HT.abs().max()) <= 1.0 + 2.0 ** -22
-    for b, n in chains:
-        yr, HTr = oracle_forward(chain_slice(x, b, n))
-        ey = max_abs(y[b:b + 1, :, n:n + 1].cpu().numpy(), yr)
-        eh = max_abs(HT[b:b + 1, n:n + 1].cpu().numpy(), HTr)
-        print(f"{name} chain ({b},{n}): max|dy|={ey:.3e} max|dH_T|={eh:.3e}")
+    for b0, b1 in rows or [(0, w.B)]:
+        yr, HTr = oracle_forward(batch_rows(x, b0, b1))
+        ey = max_abs(y[b0:b1].cpu().numpy(), yr)
+        eh = max_abs(HT[b0:b1].cpu().numpy(), HTr)
+        print(f"{name} rows {b0}..{b1 - 1}: max|dy|={ey:.3e} max|dH_T|={eh:.3e}")
         assert ey <= TOL[w.dtype] and eh <= TOL[w.dtype]
