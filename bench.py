@@ -33,9 +33,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=None)
-    ap.add_argument("--pass", dest="which", choices=["fwdbwd", "fwd", "epilogue", "prologue"], default="fwdbwd",
+    ap.add_argument("--pass", dest="which", choices=["fwdbwd", "fwd", "epilogue", "prologue", "decode"],
+                    default="fwdbwd",
                     help="epilogue: the output gate and RMSNorm after the readout; prologue: the causal Conv1D "
-                         "and SiLU of q, k and v; each forward + backward")
+                         "and SiLU of q, k and v (each forward + backward); decode: one token per call. "
+                         "--workload picks a scan workload and with it the pass")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0)
@@ -104,37 +106,64 @@ def profiled_traffic(workload, which):
     return float(vals[key]) if key in vals else None
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, x, which, threads, seconds):
     """The fp64 oracle timed on a bounded sample of the same inputs: the first
-    batch rows and heads at the full length, sized from a short calibration
-    run to take about `seconds`."""
+    batch rows and heads at the full length, on every host core (one thread
+    per core the OS reports), sized from a short calibration run so that each
+    of three timed runs takes about a quarter of `seconds`; the value is the
+    median of the three.  A run on one thread over a smaller sample gives the
+    per-core rate."""
+    import statistics
     import oracle
-    nthreads = threads or min(16, os.cpu_count() or 1)
+    nthreads = threads or (os.cpu_count() or 1)
     T = w.T
 
-    def run(Bs, Ns):
+    def run(Bs, Ns, nth):
         sl = dict(q=x["q"][:Bs], k=x["k"][:Bs], v=x["v"][:Bs, :, :Ns], f=x["f"][:Bs, :, :Ns],
                   W=x["W"][:Ns], wr=x["wr"][:Ns])
         ins = [sl[n].double().numpy() for n in ("q", "k", "v", "f", "W", "wr")]
         dy = x["dy"][:Bs, :, :Ns].double().numpy() if which == "fwdbwd" else None
         t0 = time.perf_counter()
-        oracle.forward(*ins, nthreads=nthreads)
+        oracle.forward(*ins, nthreads=nth)
         if which == "fwdbwd":
-            oracle.backward(*ins, dy, nthreads=nthreads)
+            oracle.backward(*ins, dy, nthreads=nth)
         return time.perf_counter() - t0
 
-    # calibration: one batch row, as many heads as threads
-    Ns0 = min(w.N, nthreads)
-    rate = 1 * T * Ns0 / max(run(1, Ns0), 1e-6)
-    chains = max(1, int(seconds * rate / T))
-    Ns = min(w.N, max(1, chains))
-    Bs = min(w.B, max(1, chains // Ns))
-    dt = run(Bs, Ns)
+    def shape_for(chains):   # the first `chains` (b, n) chains, whole batch rows first
+        chains = max(1, min(w.B * w.N, chains))
+        Ns = min(w.N, chains)
+        return max(1, min(w.B, chains // Ns)), Ns
+
+    # calibration: as many chains as threads (at least one batch row's worth)
+    Bc, Nc = shape_for(nthreads)
+    rate = Bc * Nc * T / max(run(Bc, Nc, nthreads), 1e-6)          # head-tokens/s on all threads
+    Bs, Ns = shape_for(max(nthreads, int(seconds / 4 * rate / T)))
+    times = [run(Bs, Ns, nthreads) for _ in range(3)]
+    dt = statistics.median(times)
     htok = Bs * T * Ns
-    return {"value": htok / dt, "unit": "head-tokens/s", "cores": min(nthreads, Bs * Ns), "kind": "oracle",
+    cores = min(nthreads, Bs * Ns)
+    # one thread: a sample about 1/8 of the budget
+    B1, N1 = shape_for(int(seconds / 8 * rate / max(cores, 1) / T))
+    t1 = run(B1, N1, 1)
+    return {"value": htok / dt, "unit": "head-tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{'forward+backward' if which == 'fwdbwd' else 'forward'} of the fp64 oracle on the first "
-                      f"B={Bs} batch rows x N={Ns} heads at T={T} of the same inputs ({htok} head-tokens), "
-                      f"{dt:.1f} s on {min(nthreads, Bs * Ns)} threads"}
+                      f"B={Bs} batch rows x N={Ns} heads at T={T} of the same inputs ({htok} head-tokens): median "
+                      f"of 3 runs ({', '.join(f'{t:.2f}' for t in times)} s) on {cores} threads",
+            "cpu_model": cpu_model(), "host_cores": os.cpu_count(),
+            "per_core_value": B1 * N1 * T / t1,
+            "per_core_sample": f"B={B1} x N={N1} heads at T={T} on 1 thread, {t1:.2f} s"}
 
 
 def bench_epilogue(args):
@@ -198,7 +227,7 @@ def bench_epilogue(args):
         "value": htok * args.steps / (total_ms * 1e-3),
         "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": total_ms / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16 in (g, w), fp32 y and arithmetic",
         "data": "synthetic (seeded; y = 3 N(0,1), g = sigmoid(N(0,1)), w = 1 + N(0,1/100), dout = N(0,1))",
         "config": {"workload": name, "pass": "forward+backward", "B": B, "T": T, "N": N, "V": V_DIM,
                    "input_dtype": dtype, "eps": 0.0},
@@ -300,7 +329,7 @@ def bench_prologue(args):
         "value": htok * args.steps / (total_ms * 1e-3),
         "unit": "head-tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": total_ms / args.steps, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16 in and out (u, w, bias, z), fp32 arithmetic and gradients",
         "data": "synthetic (seeded; u = N(0,1), w and bias U(-1/2,1/2), dz = N(0,1))",
         "config": {"workload": name, "pass": "forward+backward", "B": B, "T": T, "N": N,
                    "channels": chans, "input_dtype": dtype},
@@ -330,35 +359,113 @@ def bench_prologue(args):
     return 0
 
 
+def sq_counters(workload):
+    """Matrix-core busy and VALU issue shares per kernel from the committed
+    SQ-counter summary of this workload, while the kernel sources still hash
+    to the value recorded there (else None)."""
+    path = os.path.join(ROOT, "profiles", f"m2rnn_{workload}_sq_counters.md")
+    if not os.path.exists(path):
+        return None
+    out, sha = {}, None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("source_sha256:"):
+                sha = line.split(":", 1)[1].strip()
+            cells = [c.strip() for c in line.split("|")]
+            if len(cells) > 9 and cells[1].startswith("`m2rnn_") and cells[8].endswith("%"):
+                out[cells[1].strip("`")] = {"mfma_busy": cells[8], "valu_issue": cells[9]}
+    if sha != kernel_source_sha256(workload_kind(workload)):
+        return None
+    return out or None
+
+
+CLOCK_GHZ = 2.4   # MI355X peak engine clock
+
+
+def bench_decode(args):
+    """One token per call for every (b, n) at B=32, N=64 (bf16 inputs, fp32
+    state): m2rnn_decode timed per call.  Each call reads and rewrites the
+    whole state, 4 KB per head, so the roofline object prices those bytes
+    (plus the token's inputs and y) against MI355X's 8 TB/s."""
+    import torch
+    import m2rnn_inputs
+    import non_linear_matrix_amd as m2
+    B, N, dtype = 32, 64, "bf16"
+    steps = max(args.steps, 100)
+    x = {k: v.cuda() for k, v in m2rnn_inputs.make_inputs(B, steps, N, dtype=dtype, seed=args.seed).items()}
+    dev = x["q"].device
+    H = torch.zeros((B, N, K_DIM, V_DIM), device=dev)
+    y = torch.empty((B, N, V_DIM), device=dev)
+    toks = [{n: x[n][:, t].contiguous() for n in ("q", "k", "v", "f")} for t in range(steps)]
+    stream = torch.cuda.current_stream(dev)
+    for t in range(min(args.warmup + 1, steps)):
+        m2.decode(toks[t]["q"], toks[t]["k"], toks[t]["v"], toks[t]["f"], x["W"], x["wr"], H, y=y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(steps):
+        m2.decode(toks[t]["q"], toks[t]["k"], toks[t]["v"], toks[t]["f"], x["W"], x["wr"], H, y=y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    es = 2
+    nbytes = B * N * K_DIM * V_DIM * 4 * 2 + B * (2 * K_DIM * es + N * (V_DIM + 1) * es + N * V_DIM * 4) \
+        + N * (V_DIM * V_DIM + V_DIM) * es
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "M2RNN decode head-tokens/s (K=64,V=16), one token per call for every (b, n); % of HBM roofline",
+        "value": B * N / (ms * 1e-3), "unit": "head-tokens/s", "n_gpus": 1, "steps": steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 in, fp32 state; fp16-pair MFMA, fp32 VALU and accumulation",
+        "data": "synthetic (seeded; as the scan workloads)",
+        "config": {"workload": f"decode_{dtype}_B{B}_N{N}", "pass": "decode", "B": B, "N": N, "K": K_DIM, "V": V_DIM,
+                   "input_dtype": dtype},
+        "us_per_token": ms * 1e3,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "m2rnn_decode (one launch)",
+                     "kernel_ms": ms, "algorithmic": f"{nbytes} B per call (state read and written, token inputs, y)"},
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main():
     args = parse()
-    if args.which == "epilogue" and args.gpus == 1:
-        return bench_epilogue(args)
-    if args.which == "prologue" and args.gpus == 1:
-        return bench_prologue(args)
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
                                    "(the scan shards over batch rows/heads with no communication, "
                                    "but no multi-GPU path is built)"}))
         return 2
+    if args.which == "epilogue":
+        return bench_epilogue(args)
+    if args.which == "prologue":
+        return bench_prologue(args)
+    if args.which == "decode":
+        return bench_decode(args)
 
     import torch
     import m2rnn_inputs
     import non_linear_matrix_amd as m2
 
-    name = args.workload or ("fwdbwd_bf16_B32_T4096_N64" if args.which == "fwdbwd" else "fwd_bf16_B32_T4096_N64")
-    w = m2rnn_inputs.WORKLOADS[name]
+    if args.workload:
+        name = args.workload
+        w = m2rnn_inputs.WORKLOADS[name]
+        which = "fwdbwd" if w.backward else "fwd"
+    else:
+        which = args.which
+        name = "fwdbwd_bf16_B32_T4096_N64" if which == "fwdbwd" else "fwd_bf16_B32_T4096_N64"
+        w = m2rnn_inputs.WORKLOADS[name]
     ck = 64
-    x_cpu = m2rnn_inputs.make_workload(w, seed=args.seed, with_dy=(args.which == "fwdbwd"))
+    x_cpu = m2rnn_inputs.make_workload(w, seed=args.seed, with_dy=(which == "fwdbwd"))
     x = {k: v.cuda() for k, v in x_cpu.items()}
     dev = x["q"].device
     B, T, N = w.B, w.T, w.N
     y = torch.empty((B, T, N, V_DIM), device=dev)
     HT = torch.empty((B, N, K_DIM, V_DIM), device=dev)
     Hck = torch.empty((B, N, (T + ck - 1) // ck, K_DIM, V_DIM), device=dev)
-    fwd_out = (y, HT, Hck) if args.which == "fwdbwd" else (y, HT)
+    fwd_out = (y, HT, Hck) if which == "fwdbwd" else (y, HT)
     grads = ws = None
-    if args.which == "fwdbwd":
+    if which == "fwdbwd":
         grads = dict(dq=torch.empty((B, T, K_DIM), device=dev), dk=torch.empty((B, T, K_DIM), device=dev),
                      dv=torch.empty((B, T, N, V_DIM), device=dev), df=torch.empty((B, T, N), device=dev),
                      dW=torch.empty((N, V_DIM, V_DIM), device=dev), dw_r=torch.empty((N, V_DIM), device=dev))
@@ -371,10 +478,10 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         m2.forward(x["q"], x["k"], x["v"], x["f"], x["W"], x["wr"],
-                   ckpt_every=ck if args.which == "fwdbwd" else 0, out=fwd_out)
+                   ckpt_every=ck if which == "fwdbwd" else 0, out=fwd_out)
         if ev is not None:
             ev[1].record(stream)
-        if args.which == "fwdbwd":
+        if which == "fwdbwd":
             m2.backward(x["q"], x["k"], x["v"], x["f"], x["W"], x["wr"], Hck, ck, x["dy"],
                         out=grads, workspace=ws)
             if ev is not None:
@@ -403,12 +510,16 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
     fwd_ms = sum(e[0].elapsed_time(e[1]) for e in events) / args.steps
-    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps if args.which == "fwdbwd" else 0.0
+    bwd_ms = sum(e[1].elapsed_time(e[2]) for e in events) / args.steps if which == "fwdbwd" else 0.0
 
     htok = w.head_tokens
     value = htok * args.steps / (total_ms * 1e-3)
+
+    def frac(flop_per_htok, ms):
+        return flop_per_htok * htok / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS
+
     # dominant kernel and its algorithmic MFMA work per launch
-    if args.which == "fwdbwd" and bwd_ms > fwd_ms:
+    if which == "fwdbwd" and bwd_ms > fwd_ms:
         # the backward call: replay, reverse-sweep and reduction launches on one stream
         dom = ("m2rnn_backward (m2rnn_fwd_kernel<...,true> replay + m2rnn_bwd_kernel + "
                "m2rnn_bwd_reduce_qk_kernel + m2rnn_bwd_reduce_head_kernel)")
@@ -418,6 +529,15 @@ def main():
         dom, dom_ms, flops = "m2rnn_fwd_kernel", fwd_ms, FLOP_PER_CONTRACTION * htok
         traffic = profiled_traffic(name, "fwd")
     achieved = flops / (dom_ms * 1e-3) / 1e12
+    passes = {"forward": {"ms": fwd_ms, "flop_per_head_token": FLOP_PER_CONTRACTION,
+                          "frac": frac(FLOP_PER_CONTRACTION, fwd_ms),
+                          "clocks_per_time_step": fwd_ms * 1e-3 * CLOCK_GHZ * 1e9 / T}}
+    if which == "fwdbwd":
+        passes["backward"] = {"ms": bwd_ms, "flop_per_head_token": 3 * FLOP_PER_CONTRACTION,
+                              "frac": frac(3 * FLOP_PER_CONTRACTION, bwd_ms),
+                              "clocks_per_time_step": bwd_ms * 1e-3 * CLOCK_GHZ * 1e9 / T}
+        passes["step"] = {"ms": ms_step, "flop_per_head_token": 4 * FLOP_PER_CONTRACTION,
+                          "frac": frac(4 * FLOP_PER_CONTRACTION, ms_step)}
     res = {
         "metric": "M2RNN scan head-tokens/s (K=64,V=16) fwd & bwd; % of HBM/MFMA roofline",
         "value": value,
@@ -429,11 +549,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic (seeded; SiLU(N(0,1)) q,k,v; sigmoid(N(2,1)) f; N(0,1/16) W; N(0,1) w_r, dy)",
-        "config": {"workload": name, "pass": "forward+backward" if args.which == "fwdbwd" else "forward",
+        "dtype": (f"{w.dtype} in, fp32 state; " + ("exact fp32 MFMA" if w.dtype == "f32" else
+                  "fp16-pair MFMA (forward, replay), fp16 MFMA (sweep)") + ", fp32 VALU and accumulation"),
+        "data": "synthetic (seeded; SiLU(N(0,1)) q,k,v; sigmoid(N(%g,1)) f; N(0,1/16) W; N(0,1) w_r, dy)" % w.f_mu,
+        "config": {"workload": name, "pass": "forward+backward" if which == "fwdbwd" else "forward",
                    "B": B, "T": T, "N": N, "K": K_DIM, "V": V_DIM, "input_dtype": w.dtype,
-                   "ckpt_every": ck if args.which == "fwdbwd" else 0},
+                   "ckpt_every": ck if which == "fwdbwd" else 0},
         "copy_calibration_bytes": args.copy_calibration_bytes,
         "fwd_ms": fwd_ms,
         "bwd_ms": bwd_ms,
@@ -442,12 +563,17 @@ def main():
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / FP32_MFMA_PEAK_TFLOPS, "traffic": traffic, "kernel": dom,
                      "kernel_ms": dom_ms,
-                     "algorithmic": f"{flops / htok:.0f} flop/head-token x {htok} head-tokens per launch"},
+                     "algorithmic": f"{flops / htok:.0f} flop/head-token x {htok} head-tokens per launch",
+                     "pricing": "fp32-equivalent: the algorithmic 2KV^2 flop of each state contraction at the fp32 "
+                                "matrix peak (the state is fp32 to the pages); the kernels issue fp16 MFMA and fp32 "
+                                "VALU instructions and are bound by instruction issue (counters below)"},
+        "passes": passes,
+        "counters": sq_counters(name),
         "hbm": {"fwd_algorithmic_bytes": algorithmic_bytes_fwd(w),
                 "fwd_achieved_GBs": algorithmic_bytes_fwd(w) / (fwd_ms * 1e-3) / 1e9, "peak_GBs": HBM_PEAK_GBS},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, x_cpu, args.which, args.cpu_threads, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, x_cpu, which, args.cpu_threads, args.cpu_seconds)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -49,8 +49,8 @@ def test_forward_beyond_2_31_elements():
 def test_backward_beyond_2_31_elements():
     """B=40, T=4096, N=64 with checkpoints every 64 steps: the backward's
     replayed states every 4 steps hold 40 * 64 * 1024 * 1024 = 2.68e9 floats.
-    dv and df of sampled chains against the oracle; dw_r against its closed
-    form sum over b, t of dy * v."""
+    dv and df of sampled chains and dq, dk of the last batch row against the
+    oracle; dw_r against its closed form sum over b, t of dy * v."""
     B, T, N, ck = 40, 4096, 64, 64
     print(f"large backward B{B} T{T} N{N}", flush=True)
     x = m2rnn_inputs.make_inputs_on("cuda", B, T, N, dtype="bf16", seed=72, with_dy=True)
@@ -68,3 +68,21 @@ def test_backward_beyond_2_31_elements():
         ef = scaled(out["df"][b:b + 1, :, n:n + 1].cpu(), gr["df"])
         print(f"chain ({b},{n}): dv {ev:.2e} df {ef:.2e}")
         assert ev <= TOL and ef <= TOL
+    # dq, dk of the last batch row (sums over its 64 heads), against the oracle
+    # on that row; where the row's own half-ulp sensitivity s reaches 1e-3 (a
+    # chain whose gradients explode backward in time), the bar is 10 s
+    b = B - 1
+    row = {k: t[b:b + 1].cpu() for k, t in x.items() if k in ("q", "k", "v", "f", "dy")}
+    row.update(W=x["W"].cpu(), wr=x["wr"].cpu())
+    ins = to_f64(row)
+    gr = oracle.backward(*ins, row["dy"].double().numpy())
+    rng = np.random.default_rng(0)
+    moved = [a * (1.0 + 2.0 ** -24 * rng.choice([-1.0, 1.0], size=a.shape)) if i in (0, 1, 2, 4) else a
+             for i, a in enumerate(ins)]
+    gm = oracle.backward(*moved, row["dy"].double().numpy())
+    for name in ("dq", "dk"):
+        scale = max(1.0, float(np.max(np.abs(gr[name]))))
+        sens = float(np.max(np.abs(gm[name] - gr[name]))) / scale
+        err = scaled(out[name][b:b + 1].cpu(), gr[name])
+        print(f"row {b} {name}: scaled err {err:.2e}, half-ulp sensitivity {sens:.2e}")
+        assert err <= (TOL if sens < 1e-3 else 10.0 * sens)
