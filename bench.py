@@ -464,6 +464,8 @@ def main():
     HT = torch.empty((B, N, K_DIM, V_DIM), device=dev)
     Hck = torch.empty((B, N, (T + ck - 1) // ck, K_DIM, V_DIM), device=dev)
     fwd_out = (y, HT, Hck) if which == "fwdbwd" else (y, HT)
+    fwd_ws_bytes = m2.m2rnn_forward_workspace_bytes(B, T, N)
+    fwd_ws = torch.empty((fwd_ws_bytes,), device=dev, dtype=torch.uint8) if fwd_ws_bytes else None
     grads = ws = None
     if which == "fwdbwd":
         grads = dict(dq=torch.empty((B, T, K_DIM), device=dev), dk=torch.empty((B, T, K_DIM), device=dev),
@@ -478,7 +480,7 @@ def main():
         if ev is not None:
             ev[0].record(stream)
         m2.forward(x["q"], x["k"], x["v"], x["f"], x["W"], x["wr"],
-                   ckpt_every=ck if which == "fwdbwd" else 0, out=fwd_out)
+                   ckpt_every=ck if which == "fwdbwd" else 0, out=fwd_out, workspace=fwd_ws)
         if ev is not None:
             ev[1].record(stream)
         if which == "fwdbwd":
@@ -526,7 +528,9 @@ def main():
         dom_ms, flops = bwd_ms, 3 * FLOP_PER_CONTRACTION * htok
         traffic = profiled_traffic(name, "bwd")
     else:
-        dom, dom_ms, flops = "m2rnn_fwd_kernel", fwd_ms, FLOP_PER_CONTRACTION * htok
+        dom = ("m2rnn_forward (m2rnn_fwd_rows_kernel + m2rnn_fwd_rows_reduce_kernel)" if fwd_ws_bytes
+               else "m2rnn_fwd_kernel")
+        dom_ms, flops = fwd_ms, FLOP_PER_CONTRACTION * htok
         traffic = profiled_traffic(name, "fwd")
     achieved = flops / (dom_ms * 1e-3) / 1e12
     passes = {"forward": {"ms": fwd_ms, "flop_per_head_token": FLOP_PER_CONTRACTION,

@@ -74,7 +74,7 @@ typedef enum {
   M2RNN_OK = 0,
   M2RNN_ERR_INVALID_ARG = -1, /* null/misaligned pointer, negative size, bad dtype */
   M2RNN_ERR_UNSUPPORTED = -2, /* K != 64 or V != 16, or a size beyond the limits */
-  M2RNN_ERR_WORKSPACE = -3,   /* backward workspace missing or too small */
+  M2RNN_ERR_WORKSPACE = -3,   /* workspace missing or too small */
   M2RNN_ERR_HIP = -4          /* the HIP runtime reported an error */
 } m2rnn_status;
 
@@ -95,14 +95,28 @@ typedef enum { M2RNN_F32 = 0, M2RNN_BF16 = 1 } m2rnn_dtype;
  *           t = j * ckpt_every (j = 0 gives H_0); NULL with
  *           ckpt_every == 0 stores none.  These are what m2rnn_backward
  *           restarts its recompute from.
+ *   workspace  m2rnn_forward_workspace_bytes(B, T, N, K, V) bytes of device
+ *           memory, 256-byte aligned, contents on entry ignored; may be NULL
+ *           when that is 0 (else M2RNN_ERR_WORKSPACE).
  * H_T may be the same buffer as H_0 (each state tile is read before it is
  * overwritten); no other outputs may overlap the inputs.
+ *
+ * Few chains (B N <= 128) take a forward that spreads each head's 64 rows over
+ * 16 waves, one state element per lane, with exact fp32 products in H W (for
+ * bf16 inputs too); a head's rows then span four workgroups, whose readout
+ * partial sums go through the workspace (B N T 256 bytes) and are added in a
+ * fixed order.  More chains need no workspace.  Either way the results are
+ * bitwise the same from run to run.
  */
 int m2rnn_forward(int B, int T, int N, int K, int V, int dtype,
                   const void* q, const void* k, const void* v, const void* f,
                   const void* W, const void* w_r, const float* H_0,
                   float* y, float* H_T, float* H_ckpt, int ckpt_every,
-                  void* stream);
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace m2rnn_forward and m2rnn_forward_gated need for
+ * these sizes (0 if none, and for sizes they reject). */
+size_t m2rnn_forward_workspace_bytes(int B, int T, int N, int K, int V);
 
 /*
  * Forward scan with the forget gate computed in the kernel from a
@@ -120,7 +134,7 @@ int m2rnn_forward_gated(int B, int T, int N, int K, int V, int dtype,
                         const void* alpha, const void* beta,
                         const void* W, const void* w_r, const float* H_0,
                         float* y, float* H_T, float* H_ckpt, int ckpt_every,
-                        void* stream);
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Bytes of device workspace m2rnn_backward and m2rnn_backward_gated need
@@ -291,7 +305,8 @@ int m2rnn_gate_rmsnorm_backward_noalloc(int B, int T, int N, int V, int dtype,
  *   q, k  [B][K]; v [B][N][V]; f [B][N]; W [N][V][V]; w_r [N][V] (dtype)
  *   H     [B][N][K][V] float32 in/out
  *   y     [B][N][V]    float32 out
- * Same as m2rnn_forward with T = 1, H_0 = H_T = H and no checkpoints.
+ * Same as m2rnn_forward with T = 1, H_0 = H_T = H and no checkpoints; it
+ * needs no workspace (it always takes the forward of four waves per head).
  */
 int m2rnn_decode(int B, int N, int K, int V, int dtype,
                  const void* q, const void* k, const void* v, const void* f,

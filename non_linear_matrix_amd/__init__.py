@@ -6,7 +6,7 @@ the library is missing or fails to load, importing this package raises: there
 is no CPU fallback.
 
     import non_linear_matrix_amd as m2
-    y, H_T = m2.forward(q, k, v, f, W, w_r)                    # H_0 = 0
+    y, H_T = m2.forward(q, k, v, f, W, w_r)                    # H_0 = 0 (workspace allocated if needed)
     y, H_T, H_ckpt = m2.forward(q, k, v, f, W, w_r, ckpt_every=64)
     grads = m2.backward(q, k, v, f, W, w_r, H_ckpt, 64, dy)     # dict
     y2, H_T2 = m2.forward(q2, k2, v2, f2, W, w_r, H_0=H_T)     # resume
@@ -47,13 +47,15 @@ lib = ctypes.CDLL(LIB_PATH)
 _i = ctypes.c_int
 _p = ctypes.c_void_p
 lib.m2rnn_forward.restype = _i
-lib.m2rnn_forward.argtypes = [_i] * 6 + [_p] * 7 + [_p, _p, _p, _i, _p]
+lib.m2rnn_forward.argtypes = [_i] * 6 + [_p] * 7 + [_p, _p, _p, _i] + [_p, ctypes.c_size_t, _p]
+lib.m2rnn_forward_workspace_bytes.restype = ctypes.c_size_t
+lib.m2rnn_forward_workspace_bytes.argtypes = [_i] * 5
 lib.m2rnn_backward_workspace_bytes.restype = ctypes.c_size_t
 lib.m2rnn_backward_workspace_bytes.argtypes = [_i] * 6
 lib.m2rnn_backward.restype = _i
 lib.m2rnn_backward.argtypes = [_i] * 6 + [_p] * 6 + [_p, _i] + [_p, _p] + [_p] * 7 + [_p, ctypes.c_size_t, _p]
 lib.m2rnn_forward_gated.restype = _i
-lib.m2rnn_forward_gated.argtypes = [_i] * 6 + [_p] * 9 + [_p, _p, _p, _i, _p]
+lib.m2rnn_forward_gated.argtypes = [_i] * 6 + [_p] * 9 + [_p, _p, _p, _i] + [_p, ctypes.c_size_t, _p]
 lib.m2rnn_backward_gated.restype = _i
 lib.m2rnn_backward_gated.argtypes = ([_i] * 6 + [_p] * 8 + [_p, _i] + [_p, _p] + [_p] * 9
                                      + [_p, ctypes.c_size_t, _p])
@@ -166,9 +168,15 @@ def _n_ckpt(T, ckpt_every):
     return (T + ckpt_every - 1) // ckpt_every if ckpt_every > 0 else 0
 
 
-def m2rnn_forward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_0, y, H_T, H_ckpt, ckpt_every, stream):
+def m2rnn_forward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_0, y, H_T, H_ckpt, ckpt_every, workspace,
+                  workspace_bytes, stream):
     """Raw C-ABI call with ctypes pointers; returns the status code."""
-    return lib.m2rnn_forward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_0, y, H_T, H_ckpt, ckpt_every, stream)
+    return lib.m2rnn_forward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_0, y, H_T, H_ckpt, ckpt_every, workspace,
+                             workspace_bytes, stream)
+
+
+def m2rnn_forward_workspace_bytes(B, T, N, K_=K, V_=V):
+    return int(lib.m2rnn_forward_workspace_bytes(B, T, N, K_, V_))
 
 
 def m2rnn_backward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_ckpt, ckpt_every, dy, dH_T,
@@ -179,10 +187,10 @@ def m2rnn_backward(B, T, N, K_, V_, dtype, q, k, v, f, W, w_r, H_ckpt, ckpt_ever
 
 
 def m2rnn_forward_gated(B, T, N, K_, V_, dtype, q, k, v, a, alpha, beta, W, w_r, H_0, y, H_T, H_ckpt, ckpt_every,
-                        stream):
+                        workspace, workspace_bytes, stream):
     """Raw C-ABI call with ctypes pointers; returns the status code."""
     return lib.m2rnn_forward_gated(B, T, N, K_, V_, dtype, q, k, v, a, alpha, beta, W, w_r, H_0, y, H_T, H_ckpt,
-                                   ckpt_every, stream)
+                                   ckpt_every, workspace, workspace_bytes, stream)
 
 
 def m2rnn_backward_gated(B, T, N, K_, V_, dtype, q, k, v, a, alpha, beta, W, w_r, H_ckpt, ckpt_every, dy, dH_T,
@@ -229,27 +237,41 @@ def _fwd_outputs(B, T, N, Kq, Vv, dev, ckpt_every, out, H_0):
     return y, H_T, H_ck
 
 
-def forward(q, k, v, f, W, w_r, ckpt_every=0, out=None, H_0=None):
+def _fwd_workspace(B, T, N, Kq, Vv, dev, workspace):
+    nbytes = int(lib.m2rnn_forward_workspace_bytes(B, T, N, Kq, Vv))
+    if workspace is None:
+        if nbytes > 0:
+            workspace = torch.empty((nbytes,), device=dev, dtype=torch.uint8)
+    else:
+        _tensor(workspace, "workspace", (workspace.numel(),), workspace.dtype, dev)
+    return workspace, 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
+def forward(q, k, v, f, W, w_r, ckpt_every=0, out=None, H_0=None, workspace=None):
     """y [B,T,N,V], H_T [B,N,K,V] (float32) and, if ckpt_every > 0,
     H_ckpt [B,N,ceil(T/ckpt_every),K,V].  `out` may pass preallocated
     (y, H_T[, H_ckpt]) tensors; H_0 [B,N,K,V] float32 is the initial state
-    (None: zero) and may be the same tensor as H_T."""
+    (None: zero) and may be the same tensor as H_T.  `workspace` may pass
+    m2rnn_forward_workspace_bytes(B, T, N) bytes of device memory (allocated
+    here when needed and not given)."""
     B, T, N, Kq, Vv, dev = _scan_inputs(q, k, v, f, W, w_r)
     y, H_T, H_ck = _fwd_outputs(B, T, N, Kq, Vv, dev, ckpt_every, out, H_0)
+    workspace, wbytes = _fwd_workspace(B, T, N, Kq, Vv, dev, workspace)
     _check(lib.m2rnn_forward(B, T, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(f), _ptr(W),
                              _ptr(w_r), _ptr(H_0), _ptr(y), _ptr(H_T), _ptr(H_ck), int(ckpt_every),
-                             _stream(q.device)))
+                             _ptr(workspace), wbytes, _stream(q.device)))
     return (y, H_T) if H_ck is None else (y, H_T, H_ck)
 
 
-def forward_gated(q, k, v, a, alpha, beta, W, w_r, ckpt_every=0, out=None, H_0=None):
+def forward_gated(q, k, v, a, alpha, beta, W, w_r, ckpt_every=0, out=None, H_0=None, workspace=None):
     """forward() with f = exp(-alpha[n] softplus(a + beta[n])) computed in the
     kernel from the gate pre-activation a [B,T,N] and alpha, beta [N]."""
     B, T, N, Kq, Vv, dev = _scan_inputs(q, k, v, a, W, w_r, f_name="a", alpha=alpha, beta=beta)
     y, H_T, H_ck = _fwd_outputs(B, T, N, Kq, Vv, dev, ckpt_every, out, H_0)
+    workspace, wbytes = _fwd_workspace(B, T, N, Kq, Vv, dev, workspace)
     _check(lib.m2rnn_forward_gated(B, T, N, Kq, Vv, _dtype_code(q), _ptr(q), _ptr(k), _ptr(v), _ptr(a),
                                    _ptr(alpha), _ptr(beta), _ptr(W), _ptr(w_r), _ptr(H_0), _ptr(y), _ptr(H_T),
-                                   _ptr(H_ck), int(ckpt_every), _stream(q.device)))
+                                   _ptr(H_ck), int(ckpt_every), _ptr(workspace), wbytes, _stream(q.device)))
     return (y, H_T) if H_ck is None else (y, H_T, H_ck)
 
 

@@ -58,11 +58,19 @@ int need(const void* p, const char* name, long long elems, size_t align) {
 
 extern "C" const char* m2rnn_last_error(void) { return g_err; }
 
+extern "C" size_t m2rnn_forward_workspace_bytes(int B, int T, int N, int K, int V) {
+  if (B <= 0 || T <= 0 || N <= 0 || K != 64 || V != 16) return 0;
+  if ((long long)B * T * N * V > kMaxElems || (long long)B * ((N + 3) / 4) > kMaxHeadGroups) return 0;
+  return sizeof(float) * m2rnn::forward_workspace_floats(B, T, N);
+}
+
 // f is given, or computed from the gate pre-activation ga and (galpha, gbeta).
+// `workspace` feeds the row-split forward (few chains); the decode step
+// passes none and always takes the MFMA forward.
 static int forward_impl(bool gated, int B, int T, int N, int K, int V, int dtype, const void* q, const void* k,
                         const void* v, const void* f, const void* ga, const void* galpha, const void* gbeta,
                         const void* W, const void* w_r, const float* H_0, float* y, float* H_T, float* H_ckpt,
-                        int ckpt_every, void* stream) {
+                        int ckpt_every, void* workspace, size_t workspace_bytes, bool mfma_only, void* stream) {
   g_err[0] = 0;
   int st = check_sizes(B, T, N, K, V, dtype);
   if (st) return st;
@@ -95,24 +103,37 @@ static int forward_impl(bool gated, int B, int T, int N, int K, int V, int dtype
   if (gated) { a.ga = ga; a.galpha = galpha; a.gbeta = gbeta; }
   a.y = y; a.H_T = H_T; a.H_ckpt = ckpt_every > 0 ? H_ckpt : nullptr;
   a.B = B; a.T = T; a.N = N; a.ckpt_every = ckpt_every; a.nck = nck;
-  hipError_t e = m2rnn::launch_forward(a, dtype, s);
+  const size_t ws_need = mfma_only ? 0 : sizeof(float) * m2rnn::forward_workspace_floats(B, T, N);
+  hipError_t e;
+  if (ws_need > 0) {
+    if (!workspace || workspace_bytes < ws_need)
+      return fail(M2RNN_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", ws_need,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256)) return fail(M2RNN_ERR_INVALID_ARG, "workspace must be 256-byte aligned");
+    a.ypart = (float*)workspace;
+    e = m2rnn::launch_forward_rows(a, dtype, s);
+  } else {
+    e = m2rnn::launch_forward(a, dtype, s);
+  }
   if (e != hipSuccess) return fail(M2RNN_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return M2RNN_OK;
 }
 
 extern "C" int m2rnn_forward(int B, int T, int N, int K, int V, int dtype, const void* q, const void* k,
                              const void* v, const void* f, const void* W, const void* w_r, const float* H_0,
-                             float* y, float* H_T, float* H_ckpt, int ckpt_every, void* stream) {
+                             float* y, float* H_T, float* H_ckpt, int ckpt_every, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   return forward_impl(false, B, T, N, K, V, dtype, q, k, v, f, nullptr, nullptr, nullptr, W, w_r, H_0, y, H_T, H_ckpt,
-                      ckpt_every, stream);
+                      ckpt_every, workspace, workspace_bytes, false, stream);
 }
 
 extern "C" int m2rnn_forward_gated(int B, int T, int N, int K, int V, int dtype, const void* q, const void* k,
                                    const void* v, const void* a, const void* alpha, const void* beta,
                                    const void* W, const void* w_r, const float* H_0, float* y, float* H_T,
-                                   float* H_ckpt, int ckpt_every, void* stream) {
+                                   float* H_ckpt, int ckpt_every, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
   return forward_impl(true, B, T, N, K, V, dtype, q, k, v, nullptr, a, alpha, beta, W, w_r, H_0, y, H_T, H_ckpt,
-                      ckpt_every, stream);
+                      ckpt_every, workspace, workspace_bytes, false, stream);
 }
 
 extern "C" size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckpt_every) {
@@ -229,7 +250,8 @@ extern "C" int m2rnn_decode(int B, int N, int K, int V, int dtype, const void* q
   int st = check_sizes(B, 1, N, K, V, dtype);
   if (st) return st;
   if ((long long)B * N > 0 && !H) return fail(M2RNN_ERR_INVALID_ARG, "H must not be NULL");
-  return m2rnn_forward(B, 1, N, K, V, dtype, q, k, v, f, W, w_r, H, y, H, nullptr, 0, stream);
+  return forward_impl(false, B, 1, N, K, V, dtype, q, k, v, f, nullptr, nullptr, nullptr, W, w_r, H, y, H, nullptr, 0,
+                      nullptr, 0, true, stream);
 }
 
 // ------------------------------------------------- output gate and RMSNorm

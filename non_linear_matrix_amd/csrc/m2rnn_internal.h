@@ -19,9 +19,17 @@ struct FwdArgs {
   // replay from stored states (backward): checkpoints H_src every src_every steps
   const float* H_src = nullptr;
   int src_every = 0, src_nck = 0;
+  // row-split forward: per-row-group readout partials [B][N][4][T][16]
+  float* ypart = nullptr;
 };
 
 hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t stream);
+// Few chains (B N <= kRowsMaxChains): the row-split forward, one state element
+// per lane (m2rnn_fwd_rows.hip), which needs forward_workspace_floats(B, T, N)
+// floats of workspace in a.ypart for its readout partials (0 for more chains).
+constexpr long long kRowsMaxChains = 128;
+size_t forward_workspace_floats(int B, int T, int N);
+hipError_t launch_forward_rows(const FwdArgs& a, int dtype, hipStream_t stream);
 // Replay every checkpoint chunk of H_src in parallel, writing H every
 // ckpt_every steps into H_ckpt (no y, no H_T).
 hipError_t launch_densify(const FwdArgs& a, int dtype, hipStream_t stream);

@@ -27,6 +27,7 @@ def test_header_declares_the_entry_points():
     assert declared() == ["m2rnn_backward", "m2rnn_backward_gated", "m2rnn_backward_workspace_bytes",
                           "m2rnn_conv_silu_backward", "m2rnn_conv_silu_backward_workspace_bytes",
                           "m2rnn_conv_silu_forward", "m2rnn_decode", "m2rnn_forward", "m2rnn_forward_gated",
+                          "m2rnn_forward_workspace_bytes",
                           "m2rnn_gate_rmsnorm_backward", "m2rnn_gate_rmsnorm_backward_noalloc",
                           "m2rnn_gate_rmsnorm_backward_workspace_bytes", "m2rnn_gate_rmsnorm_forward",
                           "m2rnn_last_error"]
@@ -48,22 +49,42 @@ def test_workspace_query(m2):
     assert ws(2, 100, 5, 32, 16, 64) == 0 and ws(2, 100, 5, 64, 16, 0) == 0 and ws(0, 100, 5, 64, 16, 64) == 0
 
 
+def test_forward_workspace(m2):
+    """Few chains (B N <= 128) take the row-split forward, whose readout
+    partials need B N T 256 bytes of workspace; more chains need none.  A
+    missing or short workspace is refused before anything is launched."""
+    ws = m2.m2rnn_forward_workspace_bytes
+    assert ws(1, 4, 2) == 1 * 2 * 4 * 256 and ws(8, 2048, 16) == 8 * 16 * 2048 * 256
+    assert ws(1, 4, 129) == 0 and ws(129, 4, 1) == 0 and ws(32, 4096, 64) == 0
+    assert ws(0, 4, 2) == 0 and ws(1, 0, 2) == 0 and ws(1, 4, 2, 32, 16) == 0
+    dummy = ctypes.c_void_p(256)   # never dereferenced: the workspace check fails first
+    f = m2.lib.m2rnn_forward
+    assert f(1, 4, 2, 64, 16, 0, *[dummy] * 6, None, dummy, dummy, None, 0, None, 0, None) == m2.M2RNN_ERR_WORKSPACE
+    assert "workspace" in m2.m2rnn_last_error()
+    assert f(1, 4, 2, 64, 16, 0, *[dummy] * 6, None, dummy, dummy, None, 0, dummy, 2047, None) == \
+        m2.M2RNN_ERR_WORKSPACE
+    assert f(1, 4, 2, 64, 16, 0, *[dummy] * 6, None, dummy, dummy, None, 0, ctypes.c_void_p(256 + 16), 2048, None) == \
+        m2.M2RNN_ERR_INVALID_ARG   # 256-byte alignment
+    fg = m2.lib.m2rnn_forward_gated
+    assert fg(1, 4, 2, 64, 16, 0, *[dummy] * 8, None, dummy, dummy, None, 0, None, 0, None) == m2.M2RNN_ERR_WORKSPACE
+
+
 def test_argument_errors_without_launch(m2):
     dummy = ctypes.c_void_p(256)   # never dereferenced: validation fails first
     args6 = [dummy] * 6
     f = m2.lib.m2rnn_forward
-    assert f(1, 4, 2, 32, 16, 0, *args6, None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert f(1, 4, 2, 32, 16, 0, *args6, None, dummy, dummy, None, 0, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
     assert "K=64" in m2.m2rnn_last_error()
-    assert f(1, 4, 2, 64, 8, 0, *args6, None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
-    assert f(1, 4, 2, 64, 16, 5, *args6, None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
-    assert f(-1, 4, 2, 64, 16, 0, *args6, None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
-    assert f(1, 4, 2, 64, 16, 0, None, *args6[1:], None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 8, 0, *args6, None, dummy, dummy, None, 0, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert f(1, 4, 2, 64, 16, 5, *args6, None, dummy, dummy, None, 0, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(-1, 4, 2, 64, 16, 0, *args6, None, dummy, dummy, None, 0, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 16, 0, None, *args6[1:], None, dummy, dummy, None, 0, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
     assert "q" in m2.m2rnn_last_error()
     odd = ctypes.c_void_p(256 + 4)   # y must be 16-byte aligned
-    assert f(1, 4, 2, 64, 16, 0, *args6, None, odd, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
-    assert f(1, 4, 2, 64, 16, 0, *args6, None, dummy, dummy, dummy, 0, None) == m2.M2RNN_ERR_INVALID_ARG
-    assert f(1, 4, 2, 64, 16, 0, *args6, None, dummy, dummy, None, -3, None) == m2.M2RNN_ERR_INVALID_ARG
-    assert f(1, 4, 2, 64, 16, 0, *args6, odd, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 16, 0, *args6, None, odd, dummy, None, 0, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 16, 0, *args6, None, dummy, dummy, dummy, 0, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 16, 0, *args6, None, dummy, dummy, None, -3, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f(1, 4, 2, 64, 16, 0, *args6, odd, dummy, dummy, None, 0, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
     assert "H_0" in m2.m2rnn_last_error()
     d = m2.lib.m2rnn_decode
     assert d(1, 2, 64, 16, 0, *args6, None, dummy, None) == m2.M2RNN_ERR_INVALID_ARG   # H is required
@@ -86,12 +107,12 @@ def test_size_limits_without_launch(m2):
     args6 = [dummy] * 6
     f = m2.lib.m2rnn_forward
     # B ceil(N/4) < 2^22
-    assert f(1 << 20, 1, 16, 64, 16, 0, *args6, None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert f(1 << 20, 1, 16, 64, 16, 0, *args6, None, dummy, dummy, None, 0, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
     assert "2^22" in m2.m2rnn_last_error()
-    assert f((1 << 20) - 1, 1, 16, 64, 16, 1, *args6, None, None, dummy, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
+    assert f((1 << 20) - 1, 1, 16, 64, 16, 1, *args6, None, None, dummy, None, 0, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG
     assert "y must" in m2.m2rnn_last_error()
     # B T N V <= 2^40
-    assert f(1 << 10, 1 << 20, 128, 64, 16, 0, *args6, None, dummy, dummy, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
+    assert f(1 << 10, 1 << 20, 128, 64, 16, 0, *args6, None, dummy, dummy, None, 0, None, 0, None) == m2.M2RNN_ERR_UNSUPPORTED
     assert "too large" in m2.m2rnn_last_error()
     d = m2.lib.m2rnn_decode
     assert d(1 << 22, 4, 64, 16, 0, *args6, dummy, dummy, None) == m2.M2RNN_ERR_UNSUPPORTED
@@ -115,14 +136,14 @@ def test_gated_argument_errors_without_launch(m2):
     q3 = [dummy] * 3
     fg = m2.lib.m2rnn_forward_gated
     # q, k, v, a, alpha, beta, W, w_r
-    assert fg(1, 4, 2, 64, 16, 0, *q3, None, dummy, dummy, dummy, dummy, None, dummy, dummy, None, 0, None) \
+    assert fg(1, 4, 2, 64, 16, 0, *q3, None, dummy, dummy, dummy, dummy, None, dummy, dummy, None, 0, None, 0, None) \
         == m2.M2RNN_ERR_INVALID_ARG
     assert "a must" in m2.m2rnn_last_error()
-    assert fg(1, 4, 2, 64, 16, 0, *q3, dummy, None, dummy, dummy, dummy, None, dummy, dummy, None, 0, None) \
+    assert fg(1, 4, 2, 64, 16, 0, *q3, dummy, None, dummy, dummy, dummy, None, dummy, dummy, None, 0, None, 0, None) \
         == m2.M2RNN_ERR_INVALID_ARG
     assert "alpha" in m2.m2rnn_last_error()
     assert fg(1, 4, 2, 64, 16, 1, *q3, dummy, dummy, ctypes.c_void_p(257), dummy, dummy, None, dummy, dummy,
-              None, 0, None) == m2.M2RNN_ERR_INVALID_ARG   # bf16 beta needs 2-byte alignment
+              None, 0, None, 0, None, 0, None) == m2.M2RNN_ERR_INVALID_ARG   # bf16 beta needs 2-byte alignment
     assert "beta" in m2.m2rnn_last_error()
     bg = m2.lib.m2rnn_backward_gated
     g3 = [dummy] * 3

@@ -33,12 +33,15 @@ def test_forward_parity_small(dtype, B, T, N):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("B,T,N", [(1, 70, 512), (3, 40, 201), (2, 20, 801), (1, 45, 1600)])
+@pytest.mark.parametrize("B,T,N", [(2, 70, 64), (1, 101, 128), (1, 45, 129), (1, 70, 512), (3, 40, 201),
+                                   (2, 20, 801), (1, 45, 1600)])
 def test_forward_parity_launch_shapes(dtype, B, T, N):
-    """Chain counts B*N in each launch shape the forward picks: at most 512
-    (one head per workgroup, one tile per wave), up to 1536 (two heads of two
-    waves each, with a head count that leaves the last workgroup half empty)
-    and above (four heads, one per wave, the last group partly empty)."""
+    """Chain counts B*N in each launch shape the forward picks: at most 128
+    (the row-split forward, one state element per lane, four workgroups per
+    head; 128 is its largest), up to 512 (one head per workgroup, one tile per
+    wave; 129 its smallest), up to 1536 (two heads of two waves each, with a
+    head count that leaves the last workgroup half empty) and above (four
+    heads, one per wave, the last group partly empty)."""
     x = make(B, T, N, dtype, seed=B * 7 + T + N)
     y, HT = run(x)
     yr, HTr = oracle_forward(x)
@@ -183,18 +186,18 @@ def test_forward_rejects_bad_arguments():
     P = m2._ptr
     s = m2._stream(dev)
     args = [P(x[n]) for n in ("q", "k", "v", "f", "W", "wr")]
-    assert m2.m2rnn_forward(1, 4, 2, 32, 16, 0, *args, None, P(y), P(H), None, 0, s) == m2.M2RNN_ERR_UNSUPPORTED
-    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 7, *args, None, P(y), P(H), None, 0, s) == m2.M2RNN_ERR_INVALID_ARG
-    assert m2.m2rnn_forward(-1, 4, 2, 64, 16, 0, *args, None, P(y), P(H), None, 0, s) == m2.M2RNN_ERR_INVALID_ARG
+    assert m2.m2rnn_forward(1, 4, 2, 32, 16, 0, *args, None, P(y), P(H), None, 0, None, 0, s) == m2.M2RNN_ERR_UNSUPPORTED
+    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 7, *args, None, P(y), P(H), None, 0, None, 0, s) == m2.M2RNN_ERR_INVALID_ARG
+    assert m2.m2rnn_forward(-1, 4, 2, 64, 16, 0, *args, None, P(y), P(H), None, 0, None, 0, s) == m2.M2RNN_ERR_INVALID_ARG
     bad = list(args)
     bad[0] = None
-    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 0, *bad, None, P(y), P(H), None, 0, s) == m2.M2RNN_ERR_INVALID_ARG
+    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 0, *bad, None, P(y), P(H), None, 0, None, 0, s) == m2.M2RNN_ERR_INVALID_ARG
     assert "q" in m2.m2rnn_last_error()
     mis = torch.empty(1, 4, 2, 16 + 1, device=dev)
-    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 0, *args, None, ctypes.c_void_p(mis.data_ptr() + 4), P(H), None, 0,
+    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 0, *args, None, ctypes.c_void_p(mis.data_ptr() + 4), P(H), None, 0, None, 0,
                             s) == m2.M2RNN_ERR_INVALID_ARG
     # checkpoint pointer without an interval
-    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 0, *args, None, P(y), P(H), P(H), 0, s) == m2.M2RNN_ERR_INVALID_ARG
+    assert m2.m2rnn_forward(1, 4, 2, 64, 16, 0, *args, None, P(y), P(H), P(H), 0, None, 0, s) == m2.M2RNN_ERR_INVALID_ARG
 
 
 @pytest.mark.parametrize("name,rows", [
