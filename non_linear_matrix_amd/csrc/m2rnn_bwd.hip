@@ -457,7 +457,17 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   if (live) Hnext = *(const f4*)(Hs + (size_t)(ns - 1) * 1024);
   __syncthreads();
 
+  // Wave priorities.  The four waves of a SIMD run the same dependent chains
+  // from the same barrier, and issue goes to the oldest ready wave, so
+  // without them the youngest wave finishes its replay last and runs its
+  // reverse sweep almost alone while the others wait at the barrier.  Each
+  // wave lowers its priority as it advances through the sub-chunk (3, 3, 2,
+  // 2 over the replay's steps, 2, 1, 1, 0 over the reverse steps), which
+  // hands the issue slots to the waves behind and keeps the four together;
+  // in the pass the loaders, whose staging store is its longest path, take
+  // priority 3 and the other roles 1.
   for (int sb = ns - 1, it = 0; sb >= 0; --sb, ++it) {
+    __builtin_amdgcn_s_setprio(3);
     const int t0 = sb * L, len = min(L, a.T - t0);
     f4 P = Hnext * a.ck_scale;
     // prefetch the next sub-chunk (registers live for this iteration only).
@@ -498,6 +508,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       // steps run unguarded.
 #pragma unroll
       for (int s = 0; s < kSub; ++s) {
+        if (s < 2) __builtin_amdgcn_s_setprio(3);
+        else __builtin_amdgcn_s_setprio(2);
         {
           const f4 vv = *(const f4*)(V_s + (s * HPW + hw) * 16 + 4 * g);
           const f4 fc = *(const f4*)(F_s + (s * HPW + hw) * 4);
@@ -574,6 +586,9 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       };
 #pragma unroll
       for (int s = kSub - 1; s >= 0; --s) {
+        if (s == kSub - 1) __builtin_amdgcn_s_setprio(2);
+        else if (s > 0) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
         {
           const f4 fc = *(const f4*)(F_s + (s * HPW + hw) * 4);   // f, c(1-f), -2c(1-f), 1-f
           const f4 uu = *(const f4*)(U_s + (s * HPW + hw) * 16 + 4 * g);
@@ -620,6 +635,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       drain(0);
     }
     __syncthreads();
+    if (rw >= Cfg::NWAVES - Stage::NL) __builtin_amdgcn_s_setprio(3);
+    else __builtin_amdgcn_s_setprio(1);
     // ---- pass: reduce this sub-chunk's partials; each wave has one role.
     if (rw < 2) {
       // dq (wave 0), dk (wave 1): lane (s, 4-row quad r4) sums the HPW heads
