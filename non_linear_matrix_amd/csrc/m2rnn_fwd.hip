@@ -226,6 +226,12 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
     // their first step: loads still in flight where the step loop (which
     // holds the checkpoint stores) is entered would be waited for there.
     const int tn = more ? t0 + TC : t0;
+    // Wave priorities: the waves of a SIMD start the chunk together and
+    // issue goes to the oldest ready wave, so the youngest would run its last
+    // steps alone while the others wait at the barrier.  Each wave steps its
+    // priority down (3, 2, 1, 0) over the four quarters of the chunk, which
+    // gives the issue slots to the waves that are behind.
+    __builtin_amdgcn_s_setprio(3);
     FwdStager<TIn, HPW, Cfg::NT, TC, GATE> st;
     if (DENSE || !live) st.load(a, b, n0, tn, te, tid);
 
@@ -245,6 +251,11 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
           for (int j = 0; j < TPW; ++j)   // the replay's states stay scaled by c (only the sweep reads them)
             *(f4*)(dst + (16 * (j0 + j) + m) * 16 + 4 * g) = DENSE ? P[j] : P[j] * kInvScale;
         }
+      };
+      auto step_priority = [](int tt) {
+        if (tt == TC / 4) __builtin_amdgcn_s_setprio(2);
+        else if (tt == TC / 2) __builtin_amdgcn_s_setprio(1);
+        else if (tt == 3 * TC / 4) __builtin_amdgcn_s_setprio(0);
       };
       auto step = [&](int tt) {
         const TileVals<TPW> kq = load_tiles<TPW>(K_s + tt * 64 + m * 4 + j0);   // c k[16j+m]
@@ -295,6 +306,7 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
       if (!DENSE && steps == TC && (!a.H_ckpt || ((a.ckpt_every & 3) == 0 && ((next_ck - t0) & 3) == 0))) {
         for (int tt0 = 0; tt0 < TC; tt0 += 4) {
           if (!DENSE && tt0 == 0) st.load(a, b, n0, tn, te, tid);
+          step_priority(tt0);
           ckpt(t0 + tt0);
 #pragma unroll
           for (int u = 0; u < 4; ++u) step(tt0 + u);
@@ -302,6 +314,7 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
       } else {
         for (int tt = 0; tt < steps; ++tt) {
           if (!DENSE && tt == 0) st.load(a, b, n0, tn, te, tid);
+          step_priority(tt);
           ckpt(t0 + tt);
           step(tt);
         }
