@@ -32,15 +32,17 @@ namespace m2rnn {
 // waves per head means more independent instruction streams per SIMD, which
 // is what the per-step VALU work needs; the readout of a head then combines
 // WPH per-wave partial sums through LDS.
-template <int HPW, int TPW, int TC>
+template <int HPW, int TPW, int TC, bool DENSE = false>
 struct FwdCfg {
   static constexpr int WPH = 4 / TPW;
   static constexpr int NWAVES = HPW * WPH;
   static constexpr int NT = 64 * NWAVES;
   // one staging buffer: K_s[TC][64], Q_s[TC][64], V_s[TC][HPW][16], F_s[TC][HPW][4]
   static constexpr int kBuf = TC * (128 + HPW * 20);
-  static constexpr int kY = TC * HPW * WPH * 16;  // per-wave readout partials
-  static constexpr int kWr = HPW * 16;
+  // per-wave readout partials and w_r (the replay has no readout: its
+  // 53 KB let three workgroups share a CU)
+  static constexpr int kY = DENSE ? 0 : TC * HPW * WPH * 16;
+  static constexpr int kWr = DENSE ? 0 : HPW * 16;
   static constexpr int kFloats = 2 * kBuf + kY + kWr;
   static constexpr int kBytes = kFloats * 4;
 };
@@ -154,7 +156,7 @@ template <int TPW> __device__ __forceinline__ TileVals<TPW> load_tiles(const flo
 // chunks of a sequence run in parallel.
 template <typename TIn, int HPW, int TPW, int TC, bool DENSE, bool GATE>
 __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
-  typedef FwdCfg<HPW, TPW, TC> Cfg;
+  typedef FwdCfg<HPW, TPW, TC, DENSE> Cfg;
   constexpr int WPH = Cfg::WPH;
   extern __shared__ float smem[];
   float* ystage = smem + 2 * Cfg::kBuf;
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
 
   WOperand<TIn> Aw;
   Aw.load(live ? (const TIn*)a.W + (size_t)n * 256 : nullptr, g, m);
-  if (tid < HPW * 16) {
+  if (!DENSE && tid < HPW * 16) {
     const int hh = tid / 16;
     wr_s[tid] = n0 + hh < a.N ? to_f32(((const TIn*)a.wr)[(size_t)(n0 + hh) * 16 + tid % 16]) : 0.0f;
   }
@@ -350,7 +352,7 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
 
 template <typename TIn, int HPW, int TPW, int TC, bool DENSE = false, bool GATE = false>
 static hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
-  typedef FwdCfg<HPW, TPW, TC> Cfg;
+  typedef FwdCfg<HPW, TPW, TC, DENSE> Cfg;
   static_assert(Cfg::kBytes <= 64 * 1024, "forward LDS budget");
   const int ngroups = (a.N + HPW - 1) / HPW;
   dim3 grid((unsigned)(a.B * ngroups * (DENSE ? a.src_nck : 1))), block(Cfg::NT);
