@@ -35,12 +35,18 @@ constexpr long long kMaxElems = 1LL << 40;
 constexpr long long kMaxHeadGroups = (1LL << 22) - 1;
 constexpr long long kMaxReplayGroups = (1LL << 24) - 1;
 
+// True when the product of non-negative sizes exceeds `limit`; the product is
+// formed in 128 bits, where four int factors cannot overflow.
+bool too_large(long long limit, long long a, long long b, long long c = 1, long long d = 1) {
+  return (__int128)a * b * c * d > limit;
+}
+
 int check_sizes(int B, int T, int N, int K, int V, int dtype) {
   if (B < 0 || T < 0 || N < 0) return fail(M2RNN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d T=%d N=%d)", B, T, N);
   if (K != 64 || V != 16) return fail(M2RNN_ERR_UNSUPPORTED, "this build supports K=64, V=16 only (got K=%d V=%d)", K, V);
   if (dtype != M2RNN_F32 && dtype != M2RNN_BF16) return fail(M2RNN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
-  if ((long long)B * T * N * V > kMaxElems) return fail(M2RNN_ERR_UNSUPPORTED, "problem too large");
-  if ((long long)B * ((N + 3) / 4) > kMaxHeadGroups)
+  if (too_large(kMaxElems, B, T, N, V)) return fail(M2RNN_ERR_UNSUPPORTED, "problem too large");
+  if ((long long)B * (((long long)N + 3) / 4) > kMaxHeadGroups)
     return fail(M2RNN_ERR_UNSUPPORTED, "B * ceil(N / 4) must be below 2^22 (B=%d N=%d)", B, N);
   return M2RNN_OK;
 }
@@ -60,7 +66,7 @@ extern "C" const char* m2rnn_last_error(void) { return g_err; }
 
 extern "C" size_t m2rnn_forward_workspace_bytes(int B, int T, int N, int K, int V) {
   if (B <= 0 || T <= 0 || N <= 0 || K != 64 || V != 16) return 0;
-  if ((long long)B * T * N * V > kMaxElems || (long long)B * ((N + 3) / 4) > kMaxHeadGroups) return 0;
+  if (too_large(kMaxElems, B, T, N, V) || (long long)B * (((long long)N + 3) / 4) > kMaxHeadGroups) return 0;
   return sizeof(float) * m2rnn::forward_workspace_floats(B, T, N);
 }
 
@@ -88,7 +94,7 @@ static int forward_impl(bool gated, int B, int T, int N, int K, int V, int dtype
       (st = need(H_T, "H_T", BN * K * V, 16)))
     return st;
   if (H_0 && !aligned(H_0, 16)) return fail(M2RNN_ERR_INVALID_ARG, "H_0 must be 16-byte aligned");
-  const int nck = ckpt_every > 0 ? (T + ckpt_every - 1) / ckpt_every : 0;
+  const int nck = ckpt_every > 0 ? (int)(((long long)T + ckpt_every - 1) / ckpt_every) : 0;
   if (ckpt_every > 0 && (st = need(H_ckpt, "H_ckpt", BN * nck * K * V, 16))) return st;
   if (BN == 0) return M2RNN_OK;
 
@@ -138,7 +144,7 @@ extern "C" int m2rnn_forward_gated(int B, int T, int N, int K, int V, int dtype,
 
 extern "C" size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckpt_every) {
   if (B <= 0 || T <= 0 || N <= 0 || K != 64 || V != 16 || ckpt_every < 1) return 0;
-  if ((long long)B * T * N * V > kMaxElems || (long long)B * ((N + 3) / 4) > kMaxHeadGroups) return 0;
+  if (too_large(kMaxElems, B, T, N, V) || (long long)B * (((long long)N + 3) / 4) > kMaxHeadGroups) return 0;
   size_t o1, o2, o3, o4, o5, o6;
   int ng;
   return sizeof(float) * m2rnn::backward_workspace_floats(B, T, N, ckpt_every, &o1, &o2, &o3, &o4, &o5, &o6, &ng);
@@ -156,11 +162,11 @@ static int backward_impl(bool gated, int B, int T, int N, int K, int V, int dtyp
   if (st) return st;
   if (ckpt_every < 1) return fail(M2RNN_ERR_INVALID_ARG, "ckpt_every must be >= 1 for the backward");
   if (ckpt_every > m2rnn::backward_sub_steps() &&
-      (long long)B * ((N + 3) / 4) * ((T + (long long)ckpt_every - 1) / ckpt_every) > kMaxReplayGroups)
+      (long long)B * (((long long)N + 3) / 4) * ((T + (long long)ckpt_every - 1) / ckpt_every) > kMaxReplayGroups)
     return fail(M2RNN_ERR_UNSUPPORTED, "B * ceil(N / 4) * ceil(T / ckpt_every) must be below 2^24");
   const size_t es = dtype == M2RNN_F32 ? 4 : 2;
   const long long BT = (long long)B * T, BTN = BT * N, BN = (long long)B * N;
-  const int nck = T > 0 ? (T + ckpt_every - 1) / ckpt_every : 0;
+  const int nck = T > 0 ? (int)(((long long)T + ckpt_every - 1) / ckpt_every) : 0;
   if ((st = need(q, "q", BT * K * (N > 0), 16)) || (st = need(k, "k", BT * K * (N > 0), 16)) ||
       (st = need(v, "v", BTN * V, 16)) || (st = need(gated ? ga : f, gated ? "a" : "f", BTN, es)) ||
       (st = need(galpha, "alpha", gated ? (long long)N : 0, es)) ||
@@ -218,7 +224,7 @@ static int backward_impl(bool gated, int B, int T, int N, int K, int V, int dtyp
   rp.q = q; rp.k = k; rp.v = v; rp.f = f; rp.W = W; rp.wr = w_r;
   if (gated) { rp.ga = ga; rp.galpha = galpha; rp.gbeta = gbeta; }
   rp.y = nullptr; rp.H_T = nullptr; rp.H_ckpt = ws + o_dense;
-  rp.B = B; rp.T = T; rp.N = N; rp.ckpt_every = L; rp.nck = (T + L - 1) / L;
+  rp.B = B; rp.T = T; rp.N = N; rp.ckpt_every = L; rp.nck = (int)(((long long)T + L - 1) / L);
   rp.H_src = H_ckpt; rp.src_every = ckpt_every; rp.src_nck = nck;
   hipError_t e = m2rnn::launch_backward(a, rp, dtype, s);
   if (e != hipSuccess) return fail(M2RNN_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
@@ -265,7 +271,7 @@ int norm_check(int B, int T, int N, int V, int dtype, float eps, long long* ntok
   const long long dd = (long long)N * V;
   if (dd % 4 != 0 || dd > m2rnn::kNormMaxD)
     return fail(M2RNN_ERR_UNSUPPORTED, "N*V must be a multiple of 4 and at most %d (got %lld)", m2rnn::kNormMaxD, dd);
-  if ((long long)B * T * dd > kMaxElems) return fail(M2RNN_ERR_UNSUPPORTED, "problem too large");
+  if (too_large(kMaxElems, B, T, dd)) return fail(M2RNN_ERR_UNSUPPORTED, "problem too large");
   *ntok = (long long)B * T;
   *d = (int)dd;
   return M2RNN_OK;
@@ -430,7 +436,7 @@ int conv_check(int B, int T, int C, int dtype) {
   if (B < 0 || T < 0 || C < 0) return fail(M2RNN_ERR_INVALID_ARG, "sizes must be >= 0 (B=%d T=%d C=%d)", B, T, C);
   if (dtype != M2RNN_F32 && dtype != M2RNN_BF16) return fail(M2RNN_ERR_INVALID_ARG, "unknown dtype %d", dtype);
   if (C % 4 != 0 || C > (1 << 20)) return fail(M2RNN_ERR_UNSUPPORTED, "C must be a multiple of 4, at most 2^20 (got %d)", C);
-  if ((long long)B * T * C > kMaxElems) return fail(M2RNN_ERR_UNSUPPORTED, "problem too large");
+  if (too_large(kMaxElems, B, T, C)) return fail(M2RNN_ERR_UNSUPPORTED, "problem too large");
   return M2RNN_OK;
 }
 

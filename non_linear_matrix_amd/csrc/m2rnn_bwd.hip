@@ -851,11 +851,11 @@ size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* of
                                  size_t* off_dW, size_t* off_dwr, size_t* off_dgate, size_t* off_amax,
                                  int* ngroups) {
   const int hpw = bwd_heads_per_group(B, N);
-  const int ng = (N + hpw - 1) / hpw;
+  const int ng = (int)(((long long)N + hpw - 1) / hpw);
   auto up = [](size_t x) { return (x + 63) & ~(size_t)63; };   // 256-byte aligned regions
   size_t o = 0;
   *off_dense = o;
-  if (ckpt_every > kSub) o += up((size_t)B * N * ((T + kSub - 1) / kSub) * 1024);
+  if (ckpt_every > kSub) o += up((size_t)B * N * (((size_t)T + kSub - 1) / kSub) * 1024);
   *off_dqk = o;  o += up((size_t)B * ng * T * 128);
   *off_dW = o;   o += up((size_t)B * N * 4 * 256);
   *off_dwr = o;  o += up((size_t)B * N * 16);

@@ -56,7 +56,7 @@ struct ConvTaps {
 template <typename TIn>
 __global__ __launch_bounds__(256) void conv_fwd_kernel(ConvArgs a) {
   const int CG = a.C / 4;
-  const int nstrips = (a.T + kConvStrip - 1) / kConvStrip;
+  const int nstrips = (int)(((long long)a.T + kConvStrip - 1) / kConvStrip);
   const long long items = (long long)a.B * nstrips * CG;
   const TIn* u = (const TIn*)a.u;
   TIn* z = (TIn*)a.z;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void conv_bwd_kernel(ConvArgs a) {
 
 template <typename TIn>
 hipError_t conv_fwd_t(const ConvArgs& a, hipStream_t stream) {
-  const long long items = (long long)a.B * ((a.T + kConvStrip - 1) / kConvStrip) * (a.C / 4);
+  const long long items = (long long)a.B * (((long long)a.T + kConvStrip - 1) / kConvStrip) * (a.C / 4);
   long long blocks = (items + 255) / 256;
   if (blocks > 16384) blocks = 16384;
   hipLaunchKernelGGL(conv_fwd_kernel<TIn>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
@@ -186,7 +186,7 @@ hipError_t conv_bwd_t(const ConvArgs& a, hipStream_t stream) {
 }  // namespace
 
 int conv_backward_workers(int B, int T, int C) {
-  const long long npairs = (long long)B * ((T + kConvStripBwd - 1) / kConvStripBwd);
+  const long long npairs = (long long)B * (((long long)T + kConvStripBwd - 1) / kConvStripBwd);
   // about 262144 threads in all, each with at least four strips to carry rows across
   long long R = 262144 / (C / 4 > 0 ? C / 4 : 1);
   if (R > npairs / 4) R = npairs / 4;
