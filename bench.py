@@ -360,7 +360,7 @@ def bench_prologue(args):
 
 
 def sq_counters(workload):
-    """Matrix-core busy and VALU issue shares per kernel from the committed
+    """Matrix-core busy and VALU busy shares per kernel from the committed
     SQ-counter summary of this workload, while the kernel sources still hash
     to the value recorded there (else None)."""
     path = os.path.join(ROOT, "profiles", f"m2rnn_{workload}_sq_counters.md")
@@ -373,7 +373,7 @@ def sq_counters(workload):
                 sha = line.split(":", 1)[1].strip()
             cells = [c.strip() for c in line.split("|")]
             if len(cells) > 9 and cells[1].startswith("`m2rnn_") and cells[8].endswith("%"):
-                out[cells[1].strip("`")] = {"mfma_busy": cells[8], "valu_issue": cells[9]}
+                out[cells[1].strip("`")] = {"mfma_busy": cells[8], "valu_busy": cells[9]}
     if sha != kernel_source_sha256(workload_kind(workload)):
         return None
     return out or None
@@ -570,7 +570,8 @@ def main():
                      "algorithmic": f"{flops / htok:.0f} flop/head-token x {htok} head-tokens per launch",
                      "pricing": "fp32-equivalent: the algorithmic 2KV^2 flop of each state contraction at the fp32 "
                                 "matrix peak (the state is fp32 to the pages); the kernels issue fp16 MFMA and fp32 "
-                                "VALU instructions and are bound by instruction issue (counters below)"},
+                                "VALU instructions, and the VALU work (tanh as exp2 + rcp, the gate, the rank-1 term) "
+                                "occupies most of each SIMD's cycles (counters below)"},
         "passes": passes,
         "counters": sq_counters(name),
         "hbm": {"fwd_algorithmic_bytes": algorithmic_bytes_fwd(w),
