@@ -384,9 +384,10 @@ CLOCK_GHZ = 2.4   # MI355X peak engine clock
 
 def bench_decode(args):
     """One token per call for every (b, n) at B=32, N=64 (bf16 inputs, fp32
-    state): m2rnn_decode timed per call.  Each call reads and rewrites the
-    whole state, 4 KB per head, so the roofline object prices those bytes
-    (plus the token's inputs and y) against MI355X's 8 TB/s."""
+    state): m2rnn_decode timed per call, back to back through the C ABI (the
+    value), and through the Python binding (us_per_call_python).  Each call
+    reads and rewrites the whole state, 4 KB per head, so the roofline object
+    prices those bytes (plus the token's inputs and y) against MI355X's 8 TB/s."""
     import torch
     import m2rnn_inputs
     import non_linear_matrix_amd as m2
@@ -402,11 +403,31 @@ def bench_decode(args):
         m2.decode(toks[t]["q"], toks[t]["k"], toks[t]["v"], toks[t]["f"], x["W"], x["wr"], H, y=y)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # through the Python binding (argument checks on every call)
     e0.record(stream)
     for t in range(steps):
         m2.decode(toks[t]["q"], toks[t]["k"], toks[t]["v"], toks[t]["f"], x["W"], x["wr"], H, y=y)
     e1.record(stream)
     torch.cuda.synchronize()
+    ms_python = e0.elapsed_time(e1) / steps
+    # back to back through the C ABI with the arguments prepared beforehand, as
+    # a native or captured caller would issue them: the launches queue up and
+    # the events time the kernels
+    import ctypes
+    vp = ctypes.c_void_p
+    common = (vp(x["W"].data_ptr()), vp(x["wr"].data_ptr()), vp(H.data_ptr()), vp(y.data_ptr()),
+              vp(stream.cuda_stream))
+    calls = [(B, N, K_DIM, V_DIM, m2.M2RNN_BF16, vp(tk["q"].data_ptr()), vp(tk["k"].data_ptr()),
+              vp(tk["v"].data_ptr()), vp(tk["f"].data_ptr())) + common for tk in toks]
+    fn = m2.lib.m2rnn_decode
+    for c in calls[:min(args.warmup + 1, steps)]:
+        assert fn(*c) == m2.M2RNN_OK, m2.m2rnn_last_error()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    status = [fn(*c) for c in calls]
+    e1.record(stream)
+    torch.cuda.synchronize()
+    assert all(st == m2.M2RNN_OK for st in status), m2.m2rnn_last_error()
     ms = e0.elapsed_time(e1) / steps
     es = 2
     nbytes = B * N * K_DIM * V_DIM * 4 * 2 + B * (2 * K_DIM * es + N * (V_DIM + 1) * es + N * V_DIM * 4) \
@@ -421,6 +442,7 @@ def bench_decode(args):
         "config": {"workload": f"decode_{dtype}_B{B}_N{N}", "pass": "decode", "B": B, "N": N, "K": K_DIM, "V": V_DIM,
                    "input_dtype": dtype},
         "us_per_token": ms * 1e3,
+        "us_per_call_python": ms_python * 1e3,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "m2rnn_decode (one launch)",
                      "kernel_ms": ms, "algorithmic": f"{nbytes} B per call (state read and written, token inputs, y)"},

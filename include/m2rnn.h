@@ -305,8 +305,11 @@ int m2rnn_gate_rmsnorm_backward_noalloc(int B, int T, int N, int V, int dtype,
  *   q, k  [B][K]; v [B][N][V]; f [B][N]; W [N][V][V]; w_r [N][V] (dtype)
  *   H     [B][N][K][V] float32 in/out
  *   y     [B][N][V]    float32 out
- * Same as m2rnn_forward with T = 1, H_0 = H_T = H and no checkpoints; it
- * needs no workspace (it always takes the forward of four waves per head).
+ * Same as m2rnn_forward with T = 1, H_0 = H_T = H and no checkpoints, and
+ * bit-identical to the first step of that forward at four heads of one wave
+ * each (more than 1536 chains); one wave per head reads its state, steps and
+ * writes it back, with no staging and no workspace.  q, k, v, H and y must be
+ * 16-byte aligned, f, W and w_r element-aligned.
  */
 int m2rnn_decode(int B, int N, int K, int V, int dtype,
                  const void* q, const void* k, const void* v, const void* f,

@@ -71,12 +71,11 @@ extern "C" size_t m2rnn_forward_workspace_bytes(int B, int T, int N, int K, int 
 }
 
 // f is given, or computed from the gate pre-activation ga and (galpha, gbeta).
-// `workspace` feeds the row-split forward (few chains); the decode step
-// passes none and always takes the MFMA forward.
+// `workspace` feeds the row-split forward (few chains).
 static int forward_impl(bool gated, int B, int T, int N, int K, int V, int dtype, const void* q, const void* k,
                         const void* v, const void* f, const void* ga, const void* galpha, const void* gbeta,
                         const void* W, const void* w_r, const float* H_0, float* y, float* H_T, float* H_ckpt,
-                        int ckpt_every, void* workspace, size_t workspace_bytes, bool mfma_only, void* stream) {
+                        int ckpt_every, void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = 0;
   int st = check_sizes(B, T, N, K, V, dtype);
   if (st) return st;
@@ -109,7 +108,7 @@ static int forward_impl(bool gated, int B, int T, int N, int K, int V, int dtype
   if (gated) { a.ga = ga; a.galpha = galpha; a.gbeta = gbeta; }
   a.y = y; a.H_T = H_T; a.H_ckpt = ckpt_every > 0 ? H_ckpt : nullptr;
   a.B = B; a.T = T; a.N = N; a.ckpt_every = ckpt_every; a.nck = nck;
-  const size_t ws_need = mfma_only ? 0 : sizeof(float) * m2rnn::forward_workspace_floats(B, T, N);
+  const size_t ws_need = sizeof(float) * m2rnn::forward_workspace_floats(B, T, N);
   hipError_t e;
   if (ws_need > 0) {
     if (!workspace || workspace_bytes < ws_need)
@@ -130,7 +129,7 @@ extern "C" int m2rnn_forward(int B, int T, int N, int K, int V, int dtype, const
                              float* y, float* H_T, float* H_ckpt, int ckpt_every, void* workspace,
                              size_t workspace_bytes, void* stream) {
   return forward_impl(false, B, T, N, K, V, dtype, q, k, v, f, nullptr, nullptr, nullptr, W, w_r, H_0, y, H_T, H_ckpt,
-                      ckpt_every, workspace, workspace_bytes, false, stream);
+                      ckpt_every, workspace, workspace_bytes, stream);
 }
 
 extern "C" int m2rnn_forward_gated(int B, int T, int N, int K, int V, int dtype, const void* q, const void* k,
@@ -139,7 +138,7 @@ extern "C" int m2rnn_forward_gated(int B, int T, int N, int K, int V, int dtype,
                                    float* H_ckpt, int ckpt_every, void* workspace, size_t workspace_bytes,
                                    void* stream) {
   return forward_impl(true, B, T, N, K, V, dtype, q, k, v, nullptr, a, alpha, beta, W, w_r, H_0, y, H_T, H_ckpt,
-                      ckpt_every, workspace, workspace_bytes, false, stream);
+                      ckpt_every, workspace, workspace_bytes, stream);
 }
 
 extern "C" size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckpt_every) {
@@ -255,9 +254,20 @@ extern "C" int m2rnn_decode(int B, int N, int K, int V, int dtype, const void* q
   g_err[0] = 0;
   int st = check_sizes(B, 1, N, K, V, dtype);
   if (st) return st;
-  if ((long long)B * N > 0 && !H) return fail(M2RNN_ERR_INVALID_ARG, "H must not be NULL");
-  return forward_impl(false, B, 1, N, K, V, dtype, q, k, v, f, nullptr, nullptr, nullptr, W, w_r, H, y, H, nullptr, 0,
-                      nullptr, 0, true, stream);
+  const long long BN = (long long)B * N;
+  const size_t es = dtype == M2RNN_F32 ? 4 : 2;
+  if ((st = need(H, "H", BN * K * V, 16)) || (st = need(q, "q", BN > 0 ? (long long)B * K : 0, 16)) ||
+      (st = need(k, "k", BN > 0 ? (long long)B * K : 0, 16)) || (st = need(v, "v", BN * V, 16)) ||
+      (st = need(f, "f", BN, es)) || (st = need(W, "W", BN > 0 ? (long long)N * V * V : 0, es)) ||
+      (st = need(w_r, "w_r", BN > 0 ? (long long)N * V : 0, es)) || (st = need(y, "y", BN * V, 16)))
+    return st;
+  if (BN == 0) return M2RNN_OK;
+  m2rnn::DecodeArgs a;
+  a.q = q; a.k = k; a.v = v; a.f = f; a.W = W; a.wr = w_r; a.H = H; a.y = y;
+  a.B = B; a.N = N;
+  const hipError_t e = m2rnn::launch_decode(a, dtype, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(M2RNN_ERR_HIP, "decode launch: %s", hipGetErrorString(e));
+  return M2RNN_OK;
 }
 
 // ------------------------------------------------- output gate and RMSNorm

@@ -216,15 +216,18 @@ __device__ __forceinline__ float row_sum16(float x) {
 // x[0..3]).  Returns, in lane m of the row, the row sum of x[c] with
 // c = 2 (m & 1) + ((m >> 1) & 1): two halving exchanges (each lane keeps half
 // of its values and adds the partner's matching half: lanes m ^ 1, then
-// m ^ 2), then two rotations within the row add the four quads.
+// m ^ 2), then two rotations within the row add the four quads: by 8 first,
+// which leaves lanes m and m + 8 with the same pair sum, then by 4, so that
+// lanes m, m + 4, m + 8 and m + 12 add the same two values (in either order:
+// IEEE addition commutes) and end with bitwise the same sum.
 __device__ __forceinline__ float row_sum16x4(f4 x, int m) {
   const bool b0 = (m & 1) != 0, b1 = (m & 2) != 0;
   const float k0 = b0 ? x[2] : x[0], k1 = b0 ? x[3] : x[1];
   const float s0 = b0 ? x[0] : x[2], s1 = b0 ? x[1] : x[3];
   const float y0 = k0 + dpp<0xB1>(s0), y1 = k1 + dpp<0xB1>(s1);   // quad_perm [1,0,3,2]
   float z = (b1 ? y1 : y0) + dpp<0x4E>(b1 ? y0 : y1);              // quad_perm [2,3,0,1]
-  z += dpp<0x124>(z);                                               // row_ror:4
   z += dpp<0x128>(z);                                               // row_ror:8
+  z += dpp<0x124>(z);                                               // row_ror:4
   return z;
 }
 

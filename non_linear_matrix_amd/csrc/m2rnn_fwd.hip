@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
           }
         if constexpr (!DENSE) {
           // lane m ends with the sum for value channel 4 g + c(m); every lane
-          // stores it (the four lanes of each c write the same value)
+          // stores it (lanes m, m + 4, m + 8, m + 12 hold bitwise the same sum)
           const float ys = row_sum16x4(p, m);
           ystage[((tt * HPW + hw) * WPH + ts) * 16 + 4 * g + ((m & 1) << 1) + ((m >> 1) & 1)] = ys;
         }

@@ -24,6 +24,15 @@ struct FwdArgs {
 };
 
 hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t stream);
+
+// One token for every (b, n) head from the caller's state H [B][N][64][16],
+// updated in place (m2rnn_decode.hip).
+struct DecodeArgs {
+  const void *q, *k, *v, *f, *W, *wr;
+  float *H, *y;
+  int B, N;
+};
+hipError_t launch_decode(const DecodeArgs& a, int dtype, hipStream_t stream);
 // Few chains (B N <= kRowsMaxChains): the row-split forward, one state element
 // per lane (m2rnn_fwd_rows.hip), which needs forward_workspace_floats(B, T, N)
 // floats of workspace in a.ypart for its readout partials (0 for more chains).

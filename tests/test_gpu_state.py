@@ -84,6 +84,42 @@ def test_decode_steps_match_forward(dtype):
     assert max_abs(H.cpu().numpy(), HT.cpu().numpy()) <= 1e-5
 
 
+def _decode(x, H, t=0):
+    return m2.decode(x["q"][:, t].contiguous(), x["k"][:, t].contiguous(), x["v"][:, t].contiguous(),
+                     x["f"][:, t].contiguous(), x["W"], x["wr"], H)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_decode_bit_identical_to_forward_first_step(dtype):
+    """At more than 1536 chains the forward runs four heads of one wave each;
+    the decode kernel runs the same arithmetic in the same order, so one
+    decode step from H_0 equals that forward's T = 1 outputs bit for bit."""
+    B, N = 32, 64
+    x = to_gpu(make(B, 1, N, dtype, seed=31))
+    H0 = m2rnn_inputs.make_state(B, N, seed=3).cuda()
+    y, HT = fwd(x, H_0=H0)
+    H = H0.clone()
+    yd = _decode(x, H)
+    torch.cuda.synchronize()
+    assert torch.equal(yd, y[:, 0]) and torch.equal(H, HT)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("B,N", [(3, 5), (1, 1), (2, 130)])
+def test_decode_against_oracle(dtype, B, N):
+    """One decode step from H_0 against the oracle's one-step forward from H_0,
+    for head counts that leave the last workgroup partly empty (15, 1, 260)."""
+    x = make(B, 1, N, dtype, seed=40 + N)
+    H0 = m2rnn_inputs.make_state(B, N, seed=N)
+    H = H0.clone().cuda()
+    y = _decode(to_gpu(x), H)
+    torch.cuda.synchronize()
+    yr, HTr = oracle.forward(*to_f64(x), H_0=H0.double().numpy())
+    ey, eh = max_abs(y.cpu().numpy(), yr[:, 0]), max_abs(H.cpu().numpy(), HTr)
+    print(f"decode {dtype} B{B} N{N}: max|dy|={ey:.3e} max|dH|={eh:.3e}")
+    assert ey <= TOL[dtype] and eh <= TOL[dtype]
+
+
 def _check(gg, gr, tol, label):
     worst = 0.0
     for name, rname in GRADS:
