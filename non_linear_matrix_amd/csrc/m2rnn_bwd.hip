@@ -81,7 +81,7 @@ __device__ __forceinline__ int gate_slot(int s, int h) {
   return (p >> 2) * 4 + 2 * (o & 1) + (o >> 1);
 }
 
-template <int HPW, bool GATE>
+template <int HPW, bool GATE, bool HALF>
 struct BwdCfg {
   // the reduction pass gives each wave a fixed role (lane = (step, 16 values))
   static_assert((HPW == 1 || HPW == 2 || HPW == 4) && kSub == 4, "backward workgroup shape");
@@ -98,32 +98,46 @@ struct BwdCfg {
   // contractions take as their A operand
   static constexpr int kStep = 192 + HPW * (GATE ? 54 : 52);
   static constexpr int kBuf = kSub * kStep;
-  // per wave, two slots of {H_{t-1} tile, D tile}; a tile is stored as
+  // Buffering.  bf16 inputs (HALF): three staging buffers and two sets of
+  // partials, so that one barrier per sub-chunk suffices: the sweep of
+  // sub-chunk i writes partials set i % 2 while waves still in the pass of
+  // i - 1 read the other set, and the pass of i stages sub-chunk i + 2 while
+  // the buffer of i + 1 is complete.  fp32 inputs, whose transposes and
+  // partials take four times the LDS, keep two staging buffers and one set,
+  // with a second barrier after the pass.
+  static constexpr int kNStage = HALF ? 3 : 2;
+  static constexpr int kNPart = HALF ? 2 : 1;
+  // per wave, two slots of {H_{t-1} tile, D tile}.  fp32: a tile is stored as
   // [v / 4][kk][v % 4] with a 72-float stride between the v / 4 blocks, which
   // keeps both the 16-byte writes and the operand-layout reads free of bank
   // conflicts (LDS: 32 four-byte banks, a 4-byte access served per 32 lanes,
-  // a 16-byte access per 8 lanes)
+  // a 16-byte access per 8 lanes); bf16: 64 chunks of four fp16 per tile (the
+  // layout is described at the sweep)
   static constexpr int kXs = 72;
   static constexpr int kTile = 3 * kXs + 64;
-  static constexpr int kXpose = NWAVES * 4 * kTile;
-  // per-lane partials of one sub-chunk, each a 256-float block per (step, head):
-  //   qk: [s][dq | dk][h] x [g][64 rows]; fp32 inputs: partials over the four
-  //       values of lane group g, the 4-row quads of group g rotated by 4 g
-  //       quads (conflict-free writes, 16-byte reads); bf16 inputs: every
-  //       group holds the whole sum (an MFMA), groups 1 and 3 rotated by 16
-  //       rows, and the pass reads group 0;
+  static constexpr int kXw = HALF ? 2 * 2 * 64 * 2 : 4 * kTile;   // floats per wave
+  static constexpr int kXpose = NWAVES * kXw;
+  // per-lane partials of one sub-chunk:
+  //   qk: [s][dq | dk][h] x kQKRow.  fp32 inputs: 256 per block, [g][64
+  //       rows], partials over the four values of lane group g, the 4-row
+  //       quads of group g rotated by 4 g quads (conflict-free writes,
+  //       16-byte reads); bf16 inputs: 64 per block, the whole sum of each
+  //       row (an MFMA leaves it in every lane group; group 0 writes it);
+  //   df: [s][h] x 256 lane partials (the pass sums the whole block, in any
+  //       order); fp32 inputs put them at the same offsets within the block
+  //       as the qk partials, so that a step's dk and df partials leave in
+  //       one ds_write2st64;
   //   dv: [s][h] x [v'][20], the 16 (tile, g) partials of row v' at column
-  //       (tile + 4 g + v') mod 16;
-  //   df: [s][h] x 256 lane partials, at the same offsets within the block
-  //       as the qk partials (the pass sums the whole block, in any order),
-  //       so that a step's dk and df partials leave in one ds_write2st64.
-  static constexpr int kQK = kSub * 2 * HPW * 256;
-  static constexpr int kDV = kSub * HPW * 320;
+  //       (tile + 4 g + v') mod 16.
+  static constexpr int kQKRow = HALF ? 64 : 256;
+  static constexpr int kQK = kSub * 2 * HPW * kQKRow;
   static constexpr int kDF = kSub * HPW * 256;
+  static constexpr int kDV = kSub * HPW * 320;
+  static constexpr int kPart = kQK + kDF + kDV;   // one set, in this order
   // with the gate: alpha, beta of the HPW heads, [h][2], then the dalpha,
   // dbeta sums of each df wave's four lane rows, [wave][row][2]
   static constexpr int kGpar = GATE ? 2 * HPW + HPW * 8 : 0;
-  static constexpr int kFloats = 2 * kBuf + kXpose + kQK + kDV + kDF + kGpar;
+  static constexpr int kFloats = kNStage * kBuf + kXpose + kNPart * kPart + kGpar;
   static constexpr int kBytes = kFloats * 4;
 };
 
@@ -359,16 +373,14 @@ __device__ __forceinline__ float sum4_over_lanes(float x0, float x1, float x2, f
 
 template <typename TIn, int HPW, bool GATE>
 __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) void m2rnn_bwd_kernel(BwdArgs a) {
-  typedef BwdCfg<HPW, GATE> Cfg;
   // bf16 inputs: fp16 LDS transposes, dv partials from k itself; fp32
   // inputs: fp32 transposes, dv partials from c k
   constexpr bool kHalf = sizeof(TIn) == 2;
+  typedef BwdCfg<HPW, GATE, kHalf> Cfg;
   constexpr float kDvScale = kHalf ? 1.0f : kInvScale;
   extern __shared__ float smem[];
-  float* xpose = smem + 2 * Cfg::kBuf;
-  float* qkbuf = xpose + Cfg::kXpose;
-  float* dfbuf = qkbuf + Cfg::kQK;   // right after qkbuf: a step's dk and df share one write
-  float* dvbuf = dfbuf + Cfg::kDF;
+  float* xpose = smem + Cfg::kNStage * Cfg::kBuf;
+  float* parts = xpose + Cfg::kXpose;   // kNPart sets of {qk, df, dv} partials
 
   const int tid = threadIdx.x;
   // wave-uniform indices live in scalar registers
@@ -384,17 +396,17 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   const int n = n0 + hw;
   const bool live = n < a.N;
   const int kk = 16 * j + m;                      // this lane's state row
-  float* xp = xpose + w * 4 * Cfg::kTile;
+  float* xp = xpose + w * Cfg::kXw;
   const size_t head = (size_t)b * a.N + n;
   // stored states H at t = s * L (s = 0 .. ns-1), L = a.ckpt_every <= kSub
   const int L = a.ckpt_every, ns = a.nck;
   const float* Hs = a.H_ckpt + head * (size_t)ns * 1024 + kk * 16 + 4 * g;
-  // this lane's slots in the partials blocks (see BwdCfg)
-  // (bf16 inputs: lane group g writes its copy rotated by 16 (g & 1) rows, so
-  // the two groups that share a write cycle hit different banks; the pass
-  // reads group 0's copy, which is not rotated)
-  const int qk_slot = hw * 256 + g * 64 +
-                      (kHalf ? ((kk + 16 * (g & 1)) & 63) : (((4 * j + m / 4 + 4 * g) & 15) << 2) + (m & 3));
+  // this lane's slots in the partials blocks (see BwdCfg).  bf16 inputs:
+  // lane group 0 writes row kk of the dq, dk blocks, and the df partial of
+  // lane group g sits in its quarter of the block rotated by 16 (g & 1) rows,
+  // so the two groups that share a write cycle hit different banks.
+  const int qk_slot = kHalf ? hw * 64 + kk : hw * 256 + g * 64 + (((4 * j + m / 4 + 4 * g) & 15) << 2) + (m & 3);
+  const int df_slot = kHalf ? hw * 256 + g * 64 + ((kk + 16 * (g & 1)) & 63) : qk_slot;
   const int dv_slot = hw * 320 + m * 20 + ((j + 4 * g + m) & 15);
 
   typename ReplayOperand<TIn>::type Af;
@@ -423,7 +435,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   // the gate parameters of the group's heads, read by the threads that stage
   // f; the df waves' dalpha, dbeta sums (slot gate_slot(s, h): row r of df
   // wave d accumulates its (step, head) pair over the sub-chunks)
-  float* gpar = dvbuf + Cfg::kDV;
+  float* gpar = parts + Cfg::kNPart * Cfg::kPart;
   float* gacc = gpar + 2 * HPW;
   if (GATE) {
     if (tid < HPW) {
@@ -441,15 +453,21 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   }
   if (!live) {
     // a missing head adds zero to the dq, dk sums of the pass
+    // (bf16 inputs: every lane group writes group 0's zero)
 #pragma unroll
-    for (int s = 0; s < 2 * kSub; ++s) qkbuf[s * HPW * 256 + qk_slot] = 0.f;
+    for (int ps = 0; ps < Cfg::kNPart; ++ps)
+#pragma unroll
+      for (int s = 0; s < 2 * kSub; ++s) parts[ps * Cfg::kPart + s * HPW * Cfg::kQKRow + qk_slot] = 0.f;
   }
 
-  {
+  // stage the first kNStage - 1 sub-chunks (the latest); one that does not
+  // exist stages sub-chunk 0 into a buffer no one reads
+#pragma unroll
+  for (int i = 0; i < Cfg::kNStage - 1; ++i) {
     Stage st;
-    const int t0 = (ns - 1) * L, len0 = min(L, a.T - t0);
+    const int t0 = max(ns - 1 - i, 0) * L, len0 = min(L, a.T - t0);
     st.load(a, rw, lane, b, n0, t0, len0);
-    st.store(smem, rw, lane, n0, len0, a.N, gpar, sig);
+    st.store(smem + i * Cfg::kBuf, rw, lane, n0, len0, a.N, gpar, sig);
   }
   // the next restart state, prefetched one sub-chunk ahead and scaled by c
   // only when it is used (so nothing waits on the load early)
@@ -470,15 +488,19 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     __builtin_amdgcn_s_setprio(3);
     const int t0 = sb * L, len = min(L, a.T - t0);
     f4 P = Hnext * a.ck_scale;
-    // prefetch the next sub-chunk (registers live for this iteration only).
-    // The last iteration fetches sub-chunk 0 again and stages it into the
-    // buffer no one reads: no branch, so nothing in flight gets copied.
-    const int sn = sb > 0 ? sb - 1 : 0;
+    // prefetch the sub-chunk this pass stages, kNStage - 1 ahead (registers
+    // live for this iteration only), and the next restart state.  Near the
+    // end sub-chunk 0 is fetched again and staged into a buffer no one reads:
+    // no branch, so nothing in flight gets copied.
+    const int sn = max(sb - (Cfg::kNStage - 1), 0), sr = sb > 0 ? sb - 1 : 0;
     Stage st;
     const int lenn = min(L, a.T - sn * L);
     st.load(a, rw, lane, b, n0, sn * L, lenn);
-    if (live) Hnext = *(const f4*)(Hs + (size_t)sn * 1024);
-    const float* buf = smem + (it & 1) * Cfg::kBuf;
+    if (live) Hnext = *(const f4*)(Hs + (size_t)sr * 1024);
+    const float* buf = smem + (it % Cfg::kNStage) * Cfg::kBuf;
+    float* qkbuf = parts + (it % Cfg::kNPart) * Cfg::kPart;
+    float* dfbuf = qkbuf + Cfg::kQK;
+    float* dvbuf = dfbuf + Cfg::kDF;
     const float* K_s = buf;
     const float* Q_s = K_s + kSub * 64;
     const float* V_s = Q_s + kSub * 64;
@@ -500,7 +522,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       // step's operand) in B, the whole sum in every lane group
       auto dq_half = [&](int s, h4 ph) {
         const h4 hu = *(const h4*)(Hu_s + (s * HPW + hw) * 16 + 4 * g);
-        qkbuf[(2 * s) * HPW * 256 + qk_slot] = mfma_f16(hu, ph, f4{0.f, 0.f, 0.f, 0.f})[0];
+        const float dq = mfma_f16(hu, ph, f4{0.f, 0.f, 0.f, 0.f})[0];
+        if (g == 0) qkbuf[(2 * s) * HPW * Cfg::kQKRow + qk_slot] = dq;
       };
       // Steps s >= len of a short last sub-chunk are staged as f = 1 with
       // q = k = v = u = 0: an exact identity for C and a zero contribution to
@@ -530,7 +553,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
             float dq = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) dq = fmaf(P[i], uu[i], dq);
-            qkbuf[(2 * s) * HPW * 256 + qk_slot] = dq;
+            qkbuf[(2 * s) * HPW * Cfg::kQKRow + qk_slot] = dq;
           }
         }
         __builtin_amdgcn_sched_barrier(0);   // keep each step's loads in its step
@@ -604,17 +627,18 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
             fR[i] = fc[0] * R[i];
           }
           // dk_t[kk] (this head) = sum_v' D[kk][v'] v_t[v'] (as dq above) and
-          // the per-lane partial of df_t, which sits at the same offset of its
-          // block
-          float* pq = qkbuf + qk_slot;
+          // the per-lane partial of df_t
+          float* pk = qkbuf + (2 * s + 1) * HPW * Cfg::kQKRow + qk_slot;
+          float* pf = dfbuf + s * HPW * 256 + df_slot;
           // C_{t-1} = f R + D W^T; stage H_{t-1} and D of this step, finish
           // the previous step
           if constexpr (kHalf) {
             const h4 Dh = to_half4(D);
             const h4 hv = *(const h4*)(Hv_s + (s * HPW + hw) * 16 + 4 * g);
             C = Ab.apply_half(Dh, fR);
-            pq[(2 * s + 1) * HPW * 256] = mfma_f16(hv, Dh, f4{0.f, 0.f, 0.f, 0.f})[0];
-            pq[Cfg::kQK + s * HPW * 256] = dfp;
+            const float dk = mfma_f16(hv, Dh, f4{0.f, 0.f, 0.f, 0.f})[0];
+            if (g == 0) *pk = dk;
+            *pf = dfp;
             xh[(s & 1) * 128 + xw] = Ph[s];
             xh[(s & 1) * 128 + 64 + xw] = Dh;
           } else {
@@ -622,8 +646,8 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
             float dk = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) dk = fmaf(D[i], vv[i], dk);
-            pq[(2 * s + 1) * HPW * 256] = dk;
-            pq[Cfg::kQK + s * HPW * 256] = dfp;
+            *pk = dk;
+            *pf = dfp;
             C = Ab.apply(D, fR);
             *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + g * Cfg::kXs + m * 4) = Pp[s];
             *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + Cfg::kTile + g * Cfg::kXs + m * 4) = D;
@@ -642,12 +666,12 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       // dq (wave 0), dk (wave 1): lane (s, 4-row quad r4) sums the HPW heads
       // and four lane groups -> workspace [b][grp][t][dq | dk][64]
       const int s = lane / 16, r4 = lane % 16;
-      const float* src = qkbuf + (2 * s + rw) * HPW * 256;
+      const float* src = qkbuf + (2 * s + rw) * HPW * Cfg::kQKRow;
       // bf16: lane group 0's copy of the whole sum per head; fp32: four
       // lane-group partials per head.  The sum starts from the first term.
       constexpr int kParts = kHalf ? 1 : 4;
       auto part = [&](int hh, int gg) {
-        return kHalf ? *(const f4*)(src + hh * 256 + 4 * r4)
+        return kHalf ? *(const f4*)(src + hh * 64 + 4 * r4)
                      : *(const f4*)(src + hh * 256 + gg * 64 + (((r4 + 4 * gg) & 15) << 2));
       };
       f4 acc = part(0, 0);
@@ -696,9 +720,10 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       if (GATE) dst = sgpr_ptr(dst);
       if (m == 0 && s < len && n0 + hh < a.N) dst[(unsigned)(s * a.N + hh)] = out;
     }
-    st.store(smem + ((it + 1) & 1) * Cfg::kBuf, rw, lane, n0, lenn, a.N, gpar, sig);
-    __syncthreads();
+    st.store(smem + ((it + Cfg::kNStage - 1) % Cfg::kNStage) * Cfg::kBuf, rw, lane, n0, lenn, a.N, gpar, sig);
+    if (Cfg::kNPart == 1) __syncthreads();
   }
+  if (Cfg::kNPart > 1) __syncthreads();   // every pass has ended
 
   if (live) {
     float* dst = a.ws_dW + (head * 4 + j) * 256;
@@ -709,13 +734,14 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   }
   // dw_r: the dv waves hold one partial per (step slot, head, v'); sum the
   // step slots in a fixed order
-  if (dv_wave) dfbuf[(rw - Cfg::kDvWave) * 64 + lane] = dwr;
+  float* dwr_s = parts + Cfg::kQK;   // the first set's df partials, free now
+  if (dv_wave) dwr_s[(rw - Cfg::kDvWave) * 64 + lane] = dwr;
   __syncthreads();
   if (w == 0 && lane < HPW * 16) {
     const int hh = lane / 16, e = lane % 16;
     float acc = 0.f;
 #pragma unroll
-    for (int s = 0; s < kSub; ++s) acc += dfbuf[hh * 64 + s * 16 + e];
+    for (int s = 0; s < kSub; ++s) acc += dwr_s[hh * 64 + s * 16 + e];
     if (n0 + hh < a.N) a.ws_dwr[((size_t)b * a.N + n0 + hh) * 16 + e] = acc * isig;
   }
   if (gate && w == 1 && lane < HPW && n0 + lane < a.N) {
@@ -884,7 +910,7 @@ static hipError_t set_lds_attribute(hipStream_t stream) {
   if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
   if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
   e = hipFuncSetAttribute((const void*)m2rnn_bwd_kernel<TIn, HPW, GATE>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          BwdCfg<HPW, GATE>::kBytes);
+                          BwdCfg<HPW, GATE, sizeof(TIn) == 2>::kBytes);
   const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
   if (e != hipSuccess) return e;
   if (e2 != hipSuccess) return e2;
@@ -894,7 +920,7 @@ static hipError_t set_lds_attribute(hipStream_t stream) {
 
 template <typename TIn, int HPW, bool GATE>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
-  typedef BwdCfg<HPW, GATE> Cfg;
+  typedef BwdCfg<HPW, GATE, sizeof(TIn) == 2> Cfg;
   static_assert(Cfg::kBytes <= 160 * 1024, "backward LDS budget");
   const hipError_t attr = set_lds_attribute<TIn, HPW, GATE>(stream);
   if (attr != hipSuccess) return attr;
