@@ -93,10 +93,10 @@ struct BwdCfg {
   // per staged step: K_s[64] (c k), Q_s[64] (q), V_s[HPW][16], F_s[HPW][4],
   // U_s[HPW][16], Kp_s[64] (c k permuted: [tile][g][r] = row 16 tile + 4 r + g),
   // with the gate G_s[HPW][2] (df -> da and df -> dalpha factors, in the df
-  // waves' row order, slot gate_slot(s, h)), and for bf16 inputs the fp16
-  // rows Hu_s[HPW][16] (u) and Hv_s[HPW][16] (v) that the dq and dk
-  // contractions take as their A operand
-  static constexpr int kStep = 192 + HPW * (GATE ? 54 : 52);
+  // waves' row order, slot gate_slot(s, h)), and for bf16 inputs UV_s
+  // [HPW][2][4][8] fp16, the A operand of the joint dq, dk contraction (u in
+  // the first, v in the second half of the 16 rows)
+  static constexpr int kStep = 192 + HPW * (36 + (GATE ? 2 : 0) + (HALF ? 32 : 0));
   static constexpr int kBuf = kSub * kStep;
   // Buffering.  bf16 inputs (HALF): three staging buffers and two sets of
   // partials, so that one barrier per sub-chunk suffices: the sweep of
@@ -207,8 +207,7 @@ struct BwdStage {
     float* U_s = F_s + kSub * HPW * 4;
     float* Kp_s = U_s + kSub * HPW * 16;
     float* G_s = Kp_s + kSub * 64;
-    _Float16* Hu_s = (_Float16*)(G_s + (GATE ? kSub * HPW * 2 : 0));   // [s][h][16] fp16
-    _Float16* Hv_s = Hu_s + kSub * HPW * 16;
+    _Float16* UV_s = (_Float16*)(G_s + (GATE ? kSub * HPW * 2 : 0));   // [s][h][u | v][4][8] fp16
     const int u = (rw - (NWAVES - NL)) * 64 + lane;
     int kind, t, e0;
     decode(u, kind, t, e0);
@@ -254,13 +253,22 @@ struct BwdStage {
     } else if (kind == 2) {
 #pragma unroll
       for (int i = 0; i < EPC; i += 4) *(f4*)(V_s + t * HPW * 16 + e0 + i) = f4{x[i], x[i + 1], x[i + 2], x[i + 3]};
-      if constexpr (sizeof(TIn) == 2)   // v exact in fp16 (normal range)
-        *(u32x4*)(Hv_s + t * HPW * 16 + e0) = __builtin_bit_cast(u32x4, (h8{(_Float16)x[0], (_Float16)x[1],
-            (_Float16)x[2], (_Float16)x[3], (_Float16)x[4], (_Float16)x[5], (_Float16)x[6], (_Float16)x[7]}));
+      if constexpr (sizeof(TIn) == 2) {
+        // v (exact in fp16 in the normal range) in k-slots 4..7 of the v
+        // half; a chunk is two lane groups' quads
+        _Float16* d = UV_s + t * HPW * 64 + (e0 / 16) * 64 + 32 + ((e0 % 16) / 4) * 8;
+        const _Float16 z = (_Float16)0.0f;
+        *(h8*)d = h8{z, z, z, z, (_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+        *(h8*)(d + 8) = h8{z, z, z, z, (_Float16)x[4], (_Float16)x[5], (_Float16)x[6], (_Float16)x[7]};
+      }
     } else if (kind == 3) {
       const f4 us = f4{x[0], x[1], x[2], x[3]} * sig;
       *(f4*)(U_s + t * HPW * 16 + e0) = us;
-      if constexpr (sizeof(TIn) == 2) *(h4*)(Hu_s + t * HPW * 16 + e0) = to_half4(us);
+      if constexpr (sizeof(TIn) == 2) {   // u in k-slots 0..3 of the u half
+        const h4 uh = to_half4(us), z = {(_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f, (_Float16)0.0f};
+        *(h8*)(UV_s + t * HPW * 64 + (e0 / 16) * 64 + ((e0 % 16) / 4) * 8) =
+            __builtin_shufflevector(uh, z, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
     }
     (void)n;
     if (u < kSub * HPW) {
@@ -407,6 +415,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   // so the two groups that share a write cycle hit different banks.
   const int qk_slot = kHalf ? hw * 64 + kk : hw * 256 + g * 64 + (((4 * j + m / 4 + 4 * g) & 15) << 2) + (m & 3);
   const int df_slot = kHalf ? hw * 256 + g * 64 + ((kk + 16 * (g & 1)) & 63) : qk_slot;
+  const int qk2_slot = (g >> 1) * HPW * 64 + qk_slot;   // bf16: dq (groups 0, 1) or dk (2, 3)
   const int dv_slot = hw * 320 + m * 20 + ((j + 4 * g + m) & 15);
 
   typename ReplayOperand<TIn>::type Af;
@@ -508,23 +517,16 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     const float* U_s = F_s + kSub * HPW * 4;
     const float* Kp_s = U_s + kSub * HPW * 16;     // k permuted, [s][tile][g][r] (c k in fp32, k in fp16)
     const float* G_s = Kp_s + kSub * 64;            // gate factors, [df wave][row][2]
-    const _Float16* Hu_s = (const _Float16*)(G_s + (GATE ? kSub * HPW * 2 : 0));   // fp16 rows of u, v
-    const _Float16* Hv_s = Hu_s + kSub * HPW * 16;
+    const _Float16* UV_s = (const _Float16*)(G_s + (GATE ? kSub * HPW * 2 : 0));   // dq, dk A operand
 
     if (live) {
       // replay the sub-chunk keeping H_{t-1} and Z_t on chip (and, for bf16
       // inputs, the fp16 rounding of H_{t-1} its contraction used)
       f4 Pp[kSub], Z[kSub];
-      h4 Ph[kSub];
+      h4 Ph[kSub + 1];   // bf16 inputs: the fp16 states, H_t of the last step included
       // dq_t[kk] (this head) = sum_v H_t[kk][v] u_t[v] = (1/c) sum_v P u:
-      // fp32 inputs, per-lane partials over the lane's four v; bf16 inputs,
-      // one MFMA with u in every row of A and the fp16 state tile (the next
-      // step's operand) in B, the whole sum in every lane group
-      auto dq_half = [&](int s, h4 ph) {
-        const h4 hu = *(const h4*)(Hu_s + (s * HPW + hw) * 16 + 4 * g);
-        const float dq = mfma_f16(hu, ph, f4{0.f, 0.f, 0.f, 0.f})[0];
-        if (g == 0) qkbuf[(2 * s) * HPW * Cfg::kQKRow + qk_slot] = dq;
-      };
+      // fp32 inputs, per-lane partials over the lane's four v in the replay;
+      // bf16 inputs, in the reverse sweep together with dk (below)
       // Steps s >= len of a short last sub-chunk are staged as f = 1 with
       // q = k = v = u = 0: an exact identity for C and a zero contribution to
       // dq, dk, dv, dW and dw_r (df of such steps is not stored), so all kSub
@@ -541,7 +543,6 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
           if constexpr (kHalf) {
             Ph[s] = to_half4(P);
             x = Af.times_half(Ph[s]);
-            if (s > 0) dq_half(s - 1, Ph[s]);
           } else {
             x = Af.times_state(P);
           }
@@ -558,7 +559,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
         }
         __builtin_amdgcn_sched_barrier(0);   // keep each step's loads in its step
       }
-      if constexpr (kHalf) dq_half(kSub - 1, to_half4(P));
+      if constexpr (kHalf) Ph[kSub] = to_half4(P);
       // reverse sweep over the sub-chunk.  The dW / dv contractions over the
       // tile's rows read H_{t-1} and D back from LDS in MFMA operand layout;
       // they run one step behind the sweep so that the LDS round trip
@@ -626,18 +627,23 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
             dfp = fmaf(R[i], fmaf(Pp[s][i], kInvScale, -Z[s][i]), dfp);   // <R, H_{t-1} - Z>
             fR[i] = fc[0] * R[i];
           }
-          // dk_t[kk] (this head) = sum_v' D[kk][v'] v_t[v'] (as dq above) and
-          // the per-lane partial of df_t
-          float* pk = qkbuf + (2 * s + 1) * HPW * Cfg::kQKRow + qk_slot;
+          // dk_t[kk] (this head) = sum_v' D[kk][v'] v_t[v'] and the per-lane
+          // partial of df_t
           float* pf = dfbuf + s * HPW * 256 + df_slot;
           // C_{t-1} = f R + D W^T; stage H_{t-1} and D of this step, finish
           // the previous step
           if constexpr (kHalf) {
             const h4 Dh = to_half4(D);
-            const h4 hv = *(const h4*)(Hv_s + (s * HPW + hw) * 16 + 4 * g);
             C = Ab.apply_half(Dh, fR);
-            const float dk = mfma_f16(hv, Dh, f4{0.f, 0.f, 0.f, 0.f})[0];
-            if (g == 0) *pk = dk;
+            // dq_t and dk_t in one MFMA (a 16-deep product costs a 32-deep
+            // one's cycles): A rows 0..7 hold u in k-slots 0..3 of each lane
+            // group, rows 8..15 v in k-slots 4..7; B holds H_t (the next
+            // step's fp16 state) in slots 0..3 and D in 4..7.  Result rows
+            // 0..7 are dq[kk], rows 8..15 dk[kk]; lane groups 0 and 2 write.
+            const h8 uv = *(const h8*)(UV_s + (s * HPW + hw) * 64 + (m >> 3) * 32 + 8 * g);
+            const f4 qk = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                uv, __builtin_shufflevector(Ph[s + 1], Dh, 0, 1, 2, 3, 4, 5, 6, 7), f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            if ((g & 1) == 0) qkbuf[2 * s * HPW * 64 + qk2_slot] = qk[0];
             *pf = dfp;
             xh[(s & 1) * 128 + xw] = Ph[s];
             xh[(s & 1) * 128 + 64 + xw] = Dh;
@@ -646,7 +652,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
             float dk = 0.f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) dk = fmaf(D[i], vv[i], dk);
-            *pk = dk;
+            qkbuf[(2 * s + 1) * HPW * Cfg::kQKRow + qk_slot] = dk;
             *pf = dfp;
             C = Ab.apply(D, fR);
             *(f4*)(xp + (s & 1) * 2 * Cfg::kTile + g * Cfg::kXs + m * 4) = Pp[s];
