@@ -523,6 +523,10 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
       // replay the sub-chunk keeping H_{t-1} and Z_t on chip (and, for bf16
       // inputs, the fp16 rounding of H_{t-1} its contraction used)
       f4 Pp[kSub], Z[kSub];
+      // 1 / c in an SGPR: a VOP3 instruction (which has the negation
+      // modifier) takes no literal constant on this target
+      float kis = kInvScale;
+      asm volatile("" : "+s"(kis));
       h4 Ph[kSub + 1];   // bf16 inputs: the fp16 states, H_t of the last step included
       // dq_t[kk] (this head) = sum_v H_t[kk][v] u_t[v] = (1/c) sum_v P u:
       // fp32 inputs, per-lane partials over the lane's four v in the replay;
@@ -549,6 +553,12 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
           const f4 r = fwd_tile_finish(x, P, K_s[s * 64 + kk], vv, fc);
 #pragma unroll
           for (int i = 0; i < 4; ++i) Z[s][i] = fmaf(-2.0f, r[i], 1.0f);
+          if constexpr (kHalf) {
+            // bf16 inputs keep H_{t-1} - Z for df in place of H_{t-1} (the
+            // transposes take the fp16 state)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Pp[s][i] = fmaf(Pp[s][i], kis, -Z[s][i]);
+          }
           if constexpr (!kHalf) {
             const f4 uu = *(const f4*)(U_s + (s * HPW + hw) * 16 + 4 * g);
             float dq = 0.f;
@@ -624,7 +634,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
             R[i] = fmaf(qv, uu[i], C[i]);                            // R = C + q u^T
             const float gz = fc[3] * Z[s][i];
             D[i] = R[i] * fmaf(-gz, Z[s][i], fc[3]);                 // (1-f) R (1 - Z^2)
-            dfp = fmaf(R[i], fmaf(Pp[s][i], kInvScale, -Z[s][i]), dfp);   // <R, H_{t-1} - Z>
+            dfp = fmaf(R[i], kHalf ? Pp[s][i] : fmaf(Pp[s][i], kInvScale, -Z[s][i]), dfp);   // <R, H_{t-1} - Z>
             fR[i] = fc[0] * R[i];
           }
           // dk_t[kk] (this head) = sum_v' D[kk][v'] v_t[v'] and the per-lane
