@@ -69,12 +69,19 @@ KERNEL_SOURCES = {
 
 
 def kernel_source_sha256(kind):
-    """sha256 over the kernel sources of `kind` and the shared device headers."""
+    """sha256 over the kernel sources of `kind` and the shared device headers,
+    with comments and blank space taken out: an edit to comments alone leaves
+    the kernels, and the counters taken of them, as they were."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for name in (*KERNEL_SOURCES[kind], "m2rnn_device.h", "m2rnn_internal.h"):
-        with open(os.path.join(ROOT, "non_linear_matrix_amd", "csrc", name), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "non_linear_matrix_amd", "csrc", name), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        text = "\n".join(" ".join(line.split()) for line in text.splitlines() if line.strip())
+        h.update(text.encode("utf-8"))
     return h.hexdigest()
 
 

@@ -91,7 +91,8 @@ struct BwdCfg {
   static constexpr int NWAVES = HPW * 4;
   static constexpr int NT = 64 * NWAVES;
   // per staged step: K_s[64] (c k), Q_s[64] (q), V_s[HPW][16], F_s[HPW][4],
-  // U_s[HPW][16], Kp_s[64] (c k permuted: [tile][g][r] = row 16 tile + 4 r + g),
+  // U_s[HPW][16], Kp_s[64] (k permuted, [tile][g][r] = row 16 tile + 4 r + g:
+  // c k in fp32 for fp32 inputs, k in fp16 for bf16 inputs),
   // with the gate G_s[HPW][2] (df -> da and df -> dalpha factors, in the df
   // waves' row order, slot gate_slot(s, h)), and for bf16 inputs UV_s
   // [HPW][2][4][8] fp16, the A operand of the joint dq, dk contraction (u in
@@ -122,7 +123,8 @@ struct BwdCfg {
   //       rows], partials over the four values of lane group g, the 4-row
   //       quads of group g rotated by 4 g quads (conflict-free writes,
   //       16-byte reads); bf16 inputs: 64 per block, the whole sum of each
-  //       row (an MFMA leaves it in every lane group; group 0 writes it);
+  //       row (the joint MFMA leaves dq in lane groups 0 and 1 and dk in 2
+  //       and 3; groups 0 and 2 write);
   //   df: [s][h] x 256 lane partials (the pass sums the whole block, in any
   //       order); fp32 inputs put them at the same offsets within the block
   //       as the qk partials, so that a step's dk and df partials leave in
