@@ -37,20 +37,23 @@ struct FwdCfg {
   static constexpr int WPH = 4 / TPW;
   static constexpr int NWAVES = HPW * WPH;
   static constexpr int NT = 64 * NWAVES;
-  // one staging buffer: K_s[TC][64], Q_s[TC][64], V_s[TC][HPW][16], F_s[TC][HPW][4]
-  static constexpr int kBuf = TC * (128 + HPW * 20);
-  // per-wave readout partials and w_r (the replay has no readout: its
-  // 53 KB let three workgroups share a CU)
+  // one staging buffer: K_s[TC][64], Q_s[TC][64] (not in the replay, which
+  // has no readout), V_s[TC][HPW][16], F_s[TC][HPW][4]
+  static constexpr int kQ = DENSE ? 0 : TC * 64;
+  static constexpr int kBuf = TC * (64 + HPW * 20) + kQ;
+  // per-wave readout partials and w_r (the replay has neither: its 37 KB let
+  // four workgroups share a CU)
   static constexpr int kY = DENSE ? 0 : TC * HPW * WPH * 16;
   static constexpr int kWr = DENSE ? 0 : HPW * 16;
   static constexpr int kFloats = 2 * kBuf + kY + kWr;
   static constexpr int kBytes = kFloats * 4;
 };
 
-template <typename TIn, int HPW, int NT, int TC, bool GATE>
+template <typename TIn, int HPW, int NT, int TC, bool GATE, bool WITH_Q = true>
 struct FwdStager {
   typedef typename Vec4<TIn>::raw raw;
-  static constexpr int kQK = (2 * TC * 16 + NT - 1) / NT;   // 4-vectors of q and k
+  static constexpr int NQK = (WITH_Q ? 2 : 1) * TC * 16;      // 4-vectors of k (and q)
+  static constexpr int kQK = (NQK + NT - 1) / NT;
   static constexpr int kV = (TC * HPW * 4 + NT - 1) / NT;   // 4-vectors of v
   raw qk[kQK];
   raw vv[kV];
@@ -64,10 +67,10 @@ struct FwdStager {
   __device__ void load(const FwdArgs& a, int b, int n0, int t0, int t_end, int tid) {
 #pragma unroll
     for (int r = 0; r < kQK; ++r) {
-      const int u = tid + r * NT;           // [0, 2*TC*16)
-      const int which = u / (TC * 16);      // 0: q, 1: k
+      const int u = tid + r * NT;           // [0, NQK)
+      const int which = WITH_Q ? u / (TC * 16) : 1;   // 0: q, 1: k
       const int t = (u / 16) % TC, e0 = (u % 16) * 4;
-      const bool ok = u < 2 * TC * 16 && t0 + t < t_end;
+      const bool ok = u < NQK && t0 + t < t_end;
       const TIn* src = (const TIn*)(which == 1 ? a.k : a.q);
       qk[r] = Vec4<TIn>::load(src + ((size_t)b * a.T + t0 + (ok ? t : 0)) * 64 + (ok ? e0 : 0));
     }
@@ -91,14 +94,14 @@ struct FwdStager {
   __device__ void store(float* buf, const FwdArgs& a, int n0, int t0, int t_end, int tid, float galpha,
                         float gbeta) const {
     float* K_s = buf;
-    float* Q_s = buf + TC * 64;
-    float* V_s = buf + 2 * TC * 64;
+    float* Q_s = buf + TC * 64;   // with q only
+    float* V_s = buf + (WITH_Q ? 2 : 1) * TC * 64;
     float* F_s = V_s + TC * HPW * 16;
 #pragma unroll
     for (int r = 0; r < kQK; ++r) {
       int u = tid + r * NT;
-      if (u < 2 * TC * 16) {
-        int which = u / (TC * 16);
+      if (u < NQK) {
+        int which = WITH_Q ? u / (TC * 16) : 1;
         int t = (u / 16) % TC, e0 = (u % 16) * 4;
         f4 x = Vec4<TIn>::to_f4(qk[r]);
         if (t0 + t >= t_end) x = f4{0.f, 0.f, 0.f, 0.f};
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
 
   const int nchunks = (te - tb + TC - 1) / TC;
   {
-    FwdStager<TIn, HPW, Cfg::NT, TC, GATE> st;
+    FwdStager<TIn, HPW, Cfg::NT, TC, GATE, !DENSE> st;
     st.load(a, b, n0, tb, te, tid);
     st.store(smem, a, n0, tb, te, tid, galpha, gbeta);
   }
@@ -234,13 +237,13 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
     // priority down (3, 2, 1, 0) over the four quarters of the chunk, which
     // gives the issue slots to the waves that are behind.
     __builtin_amdgcn_s_setprio(3);
-    FwdStager<TIn, HPW, Cfg::NT, TC, GATE> st;
+    FwdStager<TIn, HPW, Cfg::NT, TC, GATE, !DENSE> st;
     if (DENSE || !live) st.load(a, b, n0, tn, te, tid);
 
     const float* buf = smem + (c & 1) * Cfg::kBuf;
     const float* K_s = buf;
-    const float* Q_s = buf + TC * 64;
-    const float* V_s = buf + 2 * TC * 64;
+    const float* Q_s = buf + TC * 64;   // not in the replay
+    const float* V_s = buf + Cfg::kQ + TC * 64;
     const float* F_s = V_s + TC * HPW * 16;
     const int steps = min(TC, te - t0);
     if (live) {
@@ -261,7 +264,8 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
       };
       auto step = [&](int tt) {
         const TileVals<TPW> kq = load_tiles<TPW>(K_s + tt * 64 + m * 4 + j0);   // c k[16j+m]
-        const TileVals<TPW> qq = load_tiles<TPW>(Q_s + tt * 64 + m * 4 + j0);   // q[16j+m] / c
+        TileVals<TPW> qq = {};                                                  // q[16j+m] / c
+        if constexpr (!DENSE) qq = load_tiles<TPW>(Q_s + tt * 64 + m * 4 + j0);
         const f4 vv = *(const f4*)(V_s + (tt * HPW + hw) * 16 + 4 * g);
         const f4 fc = *(const f4*)(F_s + (tt * HPW + hw) * 4);                 // f, c(1-f), -2c(1-f)
         // The tiles' elements are independent once the contractions are
