@@ -381,11 +381,15 @@ __device__ __forceinline__ float sum4_over_lanes(float x0, float x1, float x2, f
   return row_sum16(__builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]));
 }
 
-template <typename TIn, int HPW, bool GATE>
+// HS: the restart states are the replay's, c H in fp16 (bf16 inputs);
+// otherwise H in fp32 (the caller's checkpoints, or the replay's c H for fp32
+// inputs), scaled by a.ck_scale.
+template <typename TIn, int HPW, bool GATE, bool HS>
 __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) void m2rnn_bwd_kernel(BwdArgs a) {
   // bf16 inputs: fp16 LDS transposes, dv partials from k itself; fp32
   // inputs: fp32 transposes, dv partials from c k
   constexpr bool kHalf = sizeof(TIn) == 2;
+  static_assert(kHalf || !HS, "fp16 restart states are for bf16 inputs");
   typedef BwdCfg<HPW, GATE, kHalf> Cfg;
   constexpr float kDvScale = kHalf ? 1.0f : kInvScale;
   extern __shared__ float smem[];
@@ -411,6 +415,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   // stored states H at t = s * L (s = 0 .. ns-1), L = a.ckpt_every <= kSub
   const int L = a.ckpt_every, ns = a.nck;
   const float* Hs = a.H_ckpt + head * (size_t)ns * 1024 + kk * 16 + 4 * g;
+  const _Float16* Hh = (const _Float16*)a.H_ckpt + head * (size_t)ns * 1024 + kk * 16 + 4 * g;   // HS
   // this lane's slots in the partials blocks (see BwdCfg).  bf16 inputs:
   // lane group 0 writes row kk of the dq, dk blocks, and the df partial of
   // lane group g sits in its quarter of the block rotated by 16 (g & 1) rows,
@@ -483,7 +488,12 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   // the next restart state, prefetched one sub-chunk ahead and scaled by c
   // only when it is used (so nothing waits on the load early)
   f4 Hnext = {0.f, 0.f, 0.f, 0.f};
-  if (live) Hnext = *(const f4*)(Hs + (size_t)(ns - 1) * 1024);
+  h4 Hnext_h = {};
+  if constexpr (HS) {
+    if (live) Hnext_h = *(const h4*)(Hh + (size_t)(ns - 1) * 1024);
+  } else {
+    if (live) Hnext = *(const f4*)(Hs + (size_t)(ns - 1) * 1024);
+  }
   __syncthreads();
 
   // Wave priorities.  The four waves of a SIMD run the same dependent chains
@@ -498,7 +508,10 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   for (int sb = ns - 1, it = 0; sb >= 0; --sb, ++it) {
     __builtin_amdgcn_s_setprio(3);
     const int t0 = sb * L, len = min(L, a.T - t0);
-    f4 P = Hnext * a.ck_scale;
+    f4 P;
+    const h4 P0h = Hnext_h;   // HS: the restart state as stored, c H in fp16
+    if constexpr (HS) P = __builtin_convertvector(P0h, f4);
+    else P = Hnext * a.ck_scale;
     // prefetch the sub-chunk this pass stages, kNStage - 1 ahead (registers
     // live for this iteration only), and the next restart state.  Near the
     // end sub-chunk 0 is fetched again and staged into a buffer no one reads:
@@ -507,7 +520,11 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
     Stage st;
     const int lenn = min(L, a.T - sn * L);
     st.load(a, rw, lane, b, n0, sn * L, lenn);
-    if (live) Hnext = *(const f4*)(Hs + (size_t)sr * 1024);
+    if constexpr (HS) {
+      if (live) Hnext_h = *(const h4*)(Hh + (size_t)sr * 1024);
+    } else {
+      if (live) Hnext = *(const f4*)(Hs + (size_t)sr * 1024);
+    }
     const float* buf = smem + (it % Cfg::kNStage) * Cfg::kBuf;
     float* qkbuf = parts + (it % Cfg::kNPart) * Cfg::kPart;
     float* dfbuf = qkbuf + Cfg::kQK;
@@ -547,7 +564,7 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
           Pp[s] = P;
           f4 x;
           if constexpr (kHalf) {
-            Ph[s] = to_half4(P);
+            Ph[s] = HS && s == 0 ? P0h : to_half4(P);   // (P0h is exactly P in fp16)
             x = Af.times_half(Ph[s]);
           } else {
             x = Af.times_state(P);
@@ -914,7 +931,7 @@ size_t backward_workspace_floats(int B, int T, int N, int ckpt_every, size_t* of
 // kernel instance; later launches on that device find it set.
 constexpr int kMaxDevices = 64;
 
-template <typename TIn, int HPW, bool GATE>
+template <typename TIn, int HPW, bool GATE, bool HS>
 static hipError_t set_lds_attribute(hipStream_t stream) {
   static std::mutex mu;
   static bool done[kMaxDevices] = {};
@@ -927,7 +944,7 @@ static hipError_t set_lds_attribute(hipStream_t stream) {
   int cur = -1;
   if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
   if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
-  e = hipFuncSetAttribute((const void*)m2rnn_bwd_kernel<TIn, HPW, GATE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+  e = hipFuncSetAttribute((const void*)m2rnn_bwd_kernel<TIn, HPW, GATE, HS>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           BwdCfg<HPW, GATE, sizeof(TIn) == 2>::kBytes);
   const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
   if (e != hipSuccess) return e;
@@ -936,14 +953,14 @@ static hipError_t set_lds_attribute(hipStream_t stream) {
   return hipSuccess;
 }
 
-template <typename TIn, int HPW, bool GATE>
+template <typename TIn, int HPW, bool GATE, bool HS>
 static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   typedef BwdCfg<HPW, GATE, sizeof(TIn) == 2> Cfg;
   static_assert(Cfg::kBytes <= 160 * 1024, "backward LDS budget");
-  const hipError_t attr = set_lds_attribute<TIn, HPW, GATE>(stream);
+  const hipError_t attr = set_lds_attribute<TIn, HPW, GATE, HS>(stream);
   if (attr != hipSuccess) return attr;
   dim3 grid((unsigned)(a.B * a.ngroups)), block(Cfg::NT);
-  hipLaunchKernelGGL((m2rnn_bwd_kernel<TIn, HPW, GATE>), grid, block, Cfg::kBytes, stream, a);
+  hipLaunchKernelGGL((m2rnn_bwd_kernel<TIn, HPW, GATE, HS>), grid, block, Cfg::kBytes, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   size_t blocks = ((size_t)a.B * a.T * 32 + 255) / 256;
@@ -955,12 +972,12 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename TIn, bool GATE>
+template <typename TIn, bool GATE, bool HS>
 static hipError_t launch_bwd_shape(const BwdArgs& a, hipStream_t stream) {
   switch (bwd_heads_per_group(a.B, a.N)) {
-    case 4: return launch_bwd_t<TIn, 4, GATE>(a, stream);
-    case 2: return launch_bwd_t<TIn, 2, GATE>(a, stream);
-    default: return launch_bwd_t<TIn, 1, GATE>(a, stream);
+    case 4: return launch_bwd_t<TIn, 4, GATE, HS>(a, stream);
+    case 2: return launch_bwd_t<TIn, 2, GATE, HS>(a, stream);
+    default: return launch_bwd_t<TIn, 1, GATE, HS>(a, stream);
   }
 }
 
@@ -976,8 +993,10 @@ hipError_t launch_backward(const BwdArgs& a0, const FwdArgs& replay, int dtype, 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (a.ckpt_every > kSub) {
-    // states every kSub steps, replayed from the caller's checkpoints
+  const bool replayed = a.ckpt_every > kSub;
+  if (replayed) {
+    // states every kSub steps, replayed from the caller's checkpoints (c H,
+    // in fp16 for bf16 inputs)
     hipError_t e = launch_densify(replay, dtype, stream);
     if (e != hipSuccess) return e;
     a.H_ckpt = replay.H_ckpt;
@@ -985,8 +1004,10 @@ hipError_t launch_backward(const BwdArgs& a0, const FwdArgs& replay, int dtype, 
     a.ckpt_every = kSub;
     a.nck = (a.T + kSub - 1) / kSub;
   }
-  if (a.ga) return dtype == 0 ? launch_bwd_shape<float, true>(a, stream) : launch_bwd_shape<bf16_t, true>(a, stream);
-  return dtype == 0 ? launch_bwd_shape<float, false>(a, stream) : launch_bwd_shape<bf16_t, false>(a, stream);
+  if (dtype == 0) return a.ga ? launch_bwd_shape<float, true, false>(a, stream) : launch_bwd_shape<float, false, false>(a, stream);
+  if (replayed)
+    return a.ga ? launch_bwd_shape<bf16_t, true, true>(a, stream) : launch_bwd_shape<bf16_t, false, true>(a, stream);
+  return a.ga ? launch_bwd_shape<bf16_t, true, false>(a, stream) : launch_bwd_shape<bf16_t, false, false>(a, stream);
 }
 
 int backward_sub_steps() { return kSub; }

@@ -249,12 +249,20 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
     if (live) {
       auto ckpt = [&](int t) {
         if (t == next_ck) {
-          float* dst = a.H_ckpt + (((size_t)b * a.N + n) * a.nck + ck_idx) * 1024;
+          const size_t at = (((size_t)b * a.N + n) * a.nck + ck_idx) * 1024;
           next_ck += a.ckpt_every;
           ++ck_idx;
+          if constexpr (DENSE && sizeof(TIn) == 2) {
+            // the replay's states for the bf16-input sweep: c H in fp16 (the
+            // sweep's contractions round the state to fp16 anyway)
 #pragma unroll
-          for (int j = 0; j < TPW; ++j)   // the replay's states stay scaled by c (only the sweep reads them)
-            *(f4*)(dst + (16 * (j0 + j) + m) * 16 + 4 * g) = DENSE ? P[j] : P[j] * kInvScale;
+            for (int j = 0; j < TPW; ++j)
+              *(h4*)((_Float16*)a.H_ckpt + at + (16 * (j0 + j) + m) * 16 + 4 * g) = to_half4(P[j]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < TPW; ++j)   // the replay's states stay scaled by c (only the sweep reads them)
+              *(f4*)(a.H_ckpt + at + (16 * (j0 + j) + m) * 16 + 4 * g) = DENSE ? P[j] : P[j] * kInvScale;
+          }
         }
       };
       auto step_priority = [](int tt) {
