@@ -18,7 +18,9 @@
 //  * the states the sweep restarts from: when the caller's checkpoints are
 //    sparser than kSub steps, a replay launch (the forward kernel in DENSE
 //    mode, m2rnn_fwd.hip) restarts every checkpoint chunk in parallel and
-//    writes H every kSub steps into the workspace;
+//    writes c H every kSub steps into the workspace (for bf16 inputs rounded
+//    once to fp16, the precision the sweep's contractions take the state in:
+//    half the bytes of the largest write and read of the backward);
 //  * one wave64 owns one 16-row tile of one (b, n) head (rows of H never mix
 //    in the recurrence; only the reductions couple them), so a head is four
 //    waves of one workgroup and a workgroup holds HPW heads of a batch row;
@@ -33,7 +35,8 @@
 //    are scaled back exactly), so D sits well inside fp16's range whatever
 //    the scale of the caller's gradients;
 //  * the sweep's few-step replays run one fp16 pass per step
-//    (m2rnn_device.h) from states that hold the forward's precision;
+//    (m2rnn_device.h) from states that the chunk replay computed at the
+//    forward's precision;
 //  * dW needs a contraction over the rows, which live on lanes: each step the
 //    wave writes its H_{t-1} and D tiles to LDS and reads them back in MFMA
 //    operand layout one step later (one bf16 MFMA on rounded factors for

@@ -158,9 +158,10 @@ template <> struct WOperand<float> {
 };
 
 // ------------------------- one fp16 pass, for the sweep's short replays only
-// The backward's reverse sweep replays a few steps at a time from states of
-// full precision, so the rounding of a single fp16 pass acts over those few
-// steps only and stays well inside the backward's bf16-input bar.  (Over a
+// The backward's reverse sweep replays a few steps at a time from states the
+// chunk replay computed at full precision (stored once rounded to fp16), so
+// the rounding of a single fp16 pass acts over those few steps only and
+// stays well inside the backward's bf16-input bar.  (Over a
 // whole 64-step checkpoint chunk it does not: with a gate close to 1 the
 // rounding errors of the state accumulate across the chunk, so the chunk
 // replay keeps the split.)  Both factors are rounded once to fp16
