@@ -161,7 +161,9 @@ size_t m2rnn_backward_workspace_bytes(int B, int T, int N, int K, int V, int ckp
  *   workspace            device buffer of at least
  *                        m2rnn_backward_workspace_bytes(...) bytes,
  *                        256-byte aligned; contents on entry are ignored
- * With bf16 inputs the reverse sweep rounds its factors once to fp16 and
+ * With bf16 inputs the reverse sweep rounds its factors once to fp16 (and,
+ * when ckpt_every > 4, restarts every 4 steps from states the replay of the
+ * checkpoint chunks computed at full precision and stored in fp16) and
  * first scales dy and dH_T by the power of two that puts their largest
  * magnitude in [1/4, 1/2), scaling every output back exactly: the results
  * do not depend on the scale of the caller's gradients (dy, dH_T times 2^k
