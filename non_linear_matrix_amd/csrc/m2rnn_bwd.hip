@@ -53,13 +53,6 @@
 namespace m2rnn {
 
 constexpr int kSub = 4;  // steps between restart states; their H_{t-1}, Z_t stay in registers
-constexpr int kAmaxParts = 1024;   // partial maxima of |dy|, |dH_T| (one per workgroup of the max pass)
-
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
 
 // The power of two sig = 2^-e that puts mx sig in [1/4, 1/2), and 1 / sig;
 // 1 when mx is zero or not finite.
@@ -791,48 +784,12 @@ __global__ __launch_bounds__(256 * HPW) __attribute__((amdgpu_waves_per_eu(4))) 
   }
 }
 
-// Largest finite magnitude of dy and dH_T, the gradients that enter the
-// sweep, as kAmaxParts per-workgroup partial maxima (grid = kAmaxParts
-// workgroups); every sweep workgroup reduces them to the same scale.  NaN and
-// infinite values are skipped, so a non-finite gradient of one chain leaves
-// the scale, and with it every other chain's results, as they would be
-// without it.
-__device__ __forceinline__ float finite_abs(float x) {
-  const float a = fabsf(x);
-  return a <= 3.4028235e38f ? a : 0.0f;
-}
-__device__ __forceinline__ float absmax4(f4 v) {
-  return fmaxf(fmaxf(finite_abs(v[0]), finite_abs(v[1])), fmaxf(finite_abs(v[2]), finite_abs(v[3])));
-}
-
+// The gradient scale's partial maxima (grad_absmax_part, m2rnn_device.h) as
+// a launch of its own, when no chunk replay runs that could carry them.
 __global__ __launch_bounds__(256) void m2rnn_bwd_absmax_kernel(const float* dy, size_t ndy4, const float* dH,
                                                               size_t ndh4, float* part) {
   __shared__ float wm[4];
-  // workgroup w streams its own contiguous slice of dy, 8 x 4 KB at a time
-  const size_t per = (ndy4 + gridDim.x - 1) / gridDim.x;
-  const size_t lo = min(ndy4, (size_t)blockIdx.x * per), hi = min(ndy4, lo + per);
-  const f4* p = (const f4*)dy;
-  float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
-  size_t i = lo + threadIdx.x;
-  for (; i + 7 * 256 < hi; i += 8 * 256) {   // eight loads in flight
-    f4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[i + u * 256];
-    m0 = fmaxf(m0, fmaxf(absmax4(v[0]), absmax4(v[1])));
-    m1 = fmaxf(m1, fmaxf(absmax4(v[2]), absmax4(v[3])));
-    m2 = fmaxf(m2, fmaxf(absmax4(v[4]), absmax4(v[5])));
-    m3 = fmaxf(m3, fmaxf(absmax4(v[6]), absmax4(v[7])));
-  }
-  for (; i < hi; i += 256) m0 = fmaxf(m0, absmax4(p[i]));
-  if (dH) {
-    const f4* h = (const f4*)dH;
-    for (size_t k = (size_t)blockIdx.x * 256 + threadIdx.x; k < ndh4; k += (size_t)gridDim.x * 256)
-      m1 = fmaxf(m1, absmax4(h[k]));
-  }
-  const float mx = wave_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
-  if (threadIdx.x % 64 == 0) wm[threadIdx.x / 64] = mx;
-  __syncthreads();
-  if (threadIdx.x == 0) part[blockIdx.x] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+  grad_absmax_part(dy, ndy4, dH, ndh4, part, (int)blockIdx.x, (int)gridDim.x, wm);
 }
 
 // Fixed-order sums over workgroups of the dq, dk partials.
@@ -984,19 +941,32 @@ static hipError_t launch_bwd_shape(const BwdArgs& a, hipStream_t stream) {
   }
 }
 
-hipError_t launch_backward(const BwdArgs& a0, const FwdArgs& replay, int dtype, hipStream_t stream) {
+hipError_t launch_backward(const BwdArgs& a0, const FwdArgs& replay0, int dtype, hipStream_t stream) {
   BwdArgs a = a0;
-  // the gradients' scale first: the read-only pass over dy then does not
-  // meet the replay's freshly written states in the caches
-  if (dtype == 0) {
-    a.ws_amax = nullptr;   // exact fp32 contractions: no scale needed
-  } else {
-    hipLaunchKernelGGL(m2rnn_bwd_absmax_kernel, dim3(kAmaxParts), dim3(256), 0, stream, a.dy,
-                       (size_t)a.B * a.T * a.N * 4, a.dH_T, a.dH_T ? (size_t)a.B * a.N * 256 : (size_t)0, a.ws_amax);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
+  FwdArgs replay = replay0;
   const bool replayed = a.ckpt_every > kSub;
+  // The gradients' scale (bf16 inputs; exact fp32 contractions need none):
+  // the first kAmaxParts workgroups of the chunk replay when there is one,
+  // so that the pass over dy runs beside the replay's arithmetic, else a
+  // launch of its own.
+  if (dtype == 0) {
+    a.ws_amax = nullptr;
+  } else {
+    const size_t ndy4 = (size_t)a.B * a.T * a.N * 4, ndh4 = a.dH_T ? (size_t)a.B * a.N * 256 : (size_t)0;
+    if (replayed) {
+      replay.amax_dy = a.dy;
+      replay.amax_ndy4 = ndy4;
+      replay.amax_dH = a.dH_T;
+      replay.amax_ndh4 = ndh4;
+      replay.amax_part = a.ws_amax;
+      replay.amax_wgs = kAmaxParts;
+    } else {
+      hipLaunchKernelGGL(m2rnn_bwd_absmax_kernel, dim3(kAmaxParts), dim3(256), 0, stream, a.dy, ndy4, a.dH_T, ndh4,
+                         a.ws_amax);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+  }
   if (replayed) {
     // states every kSub steps, replayed from the caller's checkpoints (c H,
     // in fp16 for bf16 inputs)

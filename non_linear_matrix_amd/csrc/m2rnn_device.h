@@ -197,6 +197,58 @@ struct WOperandF16 {
 template <typename TIn> struct ReplayOperand { typedef WOperand<TIn> type; };
 template <> struct ReplayOperand<bf16_t> { typedef WOperandF16 type; };
 
+// ------------------------------------------------- the gradients' scale
+// Largest finite magnitude of dy and dH_T, the gradients that enter the
+// backward's sweep, as kAmaxParts per-workgroup partial maxima; every sweep
+// workgroup reduces them to the same scale.  NaN and infinite values are
+// skipped, so a non-finite gradient of one chain leaves the scale, and with
+// it every other chain's results, as they would be without it.  Run by
+// workgroups of 256 threads: those of their own launch, or extra workgroups
+// of the chunk replay, which then overlap the replay's arithmetic.
+constexpr int kAmaxParts = 128;
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float finite_abs(float x) {
+  const float a = fabsf(x);
+  return a <= 3.4028235e38f ? a : 0.0f;
+}
+__device__ __forceinline__ float absmax4(f4 v) {
+  return fmaxf(fmaxf(finite_abs(v[0]), finite_abs(v[1])), fmaxf(finite_abs(v[2]), finite_abs(v[3])));
+}
+// Workgroup wg of nwg: the maximum over its contiguous slice of dy (eight
+// 4 KB loads in flight at a time) and its share of dH_T, into part[wg].
+// wm: four floats of LDS.
+__device__ __forceinline__ void grad_absmax_part(const float* dy, size_t ndy4, const float* dH, size_t ndh4,
+                                                 float* part, int wg, int nwg, float* wm) {
+  const size_t per = (ndy4 + nwg - 1) / nwg;
+  const size_t lo = min(ndy4, (size_t)wg * per), hi = min(ndy4, lo + per);
+  const f4* p = (const f4*)dy;
+  float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+  size_t i = lo + threadIdx.x;
+  for (; i + 7 * 256 < hi; i += 8 * 256) {
+    f4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[i + u * 256];
+    m0 = fmaxf(m0, fmaxf(absmax4(v[0]), absmax4(v[1])));
+    m1 = fmaxf(m1, fmaxf(absmax4(v[2]), absmax4(v[3])));
+    m2 = fmaxf(m2, fmaxf(absmax4(v[4]), absmax4(v[5])));
+    m3 = fmaxf(m3, fmaxf(absmax4(v[6]), absmax4(v[7])));
+  }
+  for (; i < hi; i += 256) m0 = fmaxf(m0, absmax4(p[i]));
+  if (dH) {
+    const f4* h = (const f4*)dH;
+    for (size_t k = (size_t)wg * 256 + threadIdx.x; k < ndh4; k += (size_t)nwg * 256) m1 = fmaxf(m1, absmax4(h[k]));
+  }
+  const float mx = wave_max(fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
+  if (threadIdx.x % 64 == 0) wm[threadIdx.x / 64] = mx;
+  __syncthreads();
+  if (threadIdx.x == 0) part[wg] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+}
+
 // ------------------------------------------------------ cross-lane reductions
 // (every control used here reads a lane of the same row, so bound_ctrl never
 // applies; setting it lets the compiler fold the move into the add)

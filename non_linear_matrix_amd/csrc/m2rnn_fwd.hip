@@ -171,6 +171,14 @@ __global__ __launch_bounds__(256 * HPW / TPW) void m2rnn_fwd_kernel(FwdArgs a) {
   const int hw = w / WPH, ts = w % WPH, j0 = ts * TPW;   // head in group, tile set, first tile
   const int ngroups = (a.N + HPW - 1) / HPW;
   int blk = blockIdx.x;
+  if constexpr (DENSE) {
+    static_assert(Cfg::NT == 256, "the gradient-scale role runs on 256 threads");
+    if (blk < a.amax_wgs) {   // uniform over the workgroup
+      grad_absmax_part(a.amax_dy, a.amax_ndy4, a.amax_dH, a.amax_ndh4, a.amax_part, blk, a.amax_wgs, smem);
+      return;
+    }
+    blk -= a.amax_wgs;
+  }
   const int n0 = (blk % ngroups) * HPW;
   blk /= ngroups;
   int tb = 0, te = a.T;
@@ -367,7 +375,7 @@ static hipError_t launch_fwd(const FwdArgs& a, hipStream_t stream) {
   typedef FwdCfg<HPW, TPW, TC, DENSE> Cfg;
   static_assert(Cfg::kBytes <= 64 * 1024, "forward LDS budget");
   const int ngroups = (a.N + HPW - 1) / HPW;
-  dim3 grid((unsigned)(a.B * ngroups * (DENSE ? a.src_nck : 1))), block(Cfg::NT);
+  dim3 grid((unsigned)(a.B * ngroups * (DENSE ? a.src_nck : 1) + (DENSE ? a.amax_wgs : 0))), block(Cfg::NT);
   hipLaunchKernelGGL((m2rnn_fwd_kernel<TIn, HPW, TPW, TC, DENSE, GATE>), grid, block, Cfg::kBytes, stream, a);
   return hipGetLastError();
 }

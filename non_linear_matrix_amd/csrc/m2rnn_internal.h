@@ -21,6 +21,13 @@ struct FwdArgs {
   int src_every = 0, src_nck = 0;
   // row-split forward: per-row-group readout partials [B][N][4][T][16]
   float* ypart = nullptr;
+  // replay: amax_wgs extra workgroups (the first ones) that compute the
+  // backward's gradient scale (grad_absmax_part) while the replay runs
+  const float* amax_dy = nullptr;
+  const float* amax_dH = nullptr;
+  size_t amax_ndy4 = 0, amax_ndh4 = 0;
+  float* amax_part = nullptr;
+  int amax_wgs = 0;
 };
 
 hipError_t launch_forward(const FwdArgs& a, int dtype, hipStream_t stream);
